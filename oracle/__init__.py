@@ -1,0 +1,245 @@
+"""ctypes wrapper around the CPU oracle (oracle/dflash2_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by
+the benchmark's CPU-baseline leg, never by the product path.  Inputs are
+host numpy arrays (or CPU torch tensors); bf16 tensors are passed as their
+raw 16-bit patterns.  Every function returns fresh numpy outputs.
+
+Parity status per function (details in the C source):
+  topk, project, pair_scores, path, verify_greedy, verify_reject, dynconv2,
+  philox -- all pinned by the CPU tests in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("DFLASH2_ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
+
+FP32, BF16, FP16 = 0, 1, 2
+PATH_VITERBI, PATH_GREEDY, PATH_SAMPLE = 0, 1, 2
+GATE_IDENTITY, GATE_SIGMOID = 0, 1
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from . import build as _b
+            _b.build()
+        _lib = C.CDLL(LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+P = C.c_void_p
+I32, I64, U64, F64 = C.c_int32, C.c_int64, C.c_uint64, C.c_double
+
+
+def _declare(L):
+    L.oracle_set_num_threads.argtypes = [C.c_int]
+    L.oracle_get_num_threads.restype = C.c_int
+    L.oracle_philox4x64_10.argtypes = [U64, U64, P, P]
+    L.oracle_uniform_from_word.argtypes = [U64]
+    L.oracle_uniform_from_word.restype = F64
+    L.oracle_topk.argtypes = [P, C.c_int, I64, I64, C.c_int, P, P]
+    L.oracle_project.argtypes = [P, C.c_int, I64, C.c_int, P, C.c_int, C.c_int, P]
+    L.oracle_pair_scores.argtypes = [P, P, P, P, C.c_int, I64, P, P, P, P, C.c_int, C.c_int,
+                                     C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P]
+    L.oracle_path.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, F64, U64, P, P, P, P, P]
+    L.oracle_verify_greedy.argtypes = [P, C.c_int, I64, P, C.c_int, C.c_int, P, P, P]
+    L.oracle_verify_reject.argtypes = [P, C.c_int, I64, P, P, P, P, C.c_int, C.c_int, C.c_int,
+                                       F64, U64, P, P, P, P, P]
+    L.oracle_dynconv2.argtypes = [P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P]
+    for f in ("oracle_topk", "oracle_project", "oracle_pair_scores", "oracle_path",
+              "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2"):
+        getattr(L, f).restype = C.c_int
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise OracleError(f"{name} returned {rc}")
+
+
+def host(x, dtype=None):
+    """Contiguous host numpy array from a numpy array or a torch tensor.
+    bf16 / fp16 torch tensors become uint16 bit patterns plus a dtype code."""
+    try:
+        import torch
+    except ImportError:  # pragma: no cover
+        torch = None
+    if torch is not None and isinstance(x, torch.Tensor):
+        x = x.detach().cpu().contiguous()
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).numpy().view(np.uint16), BF16
+        if x.dtype == torch.float16:
+            return x.view(torch.int16).numpy().view(np.uint16), FP16
+        x = x.numpy()
+    x = np.ascontiguousarray(x if dtype is None else x.astype(dtype))
+    code = {np.dtype(np.float32): FP32}.get(x.dtype, None)
+    return x, code
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def set_num_threads(n: int):
+    lib().oracle_set_num_threads(int(n))
+
+
+def num_threads() -> int:
+    return int(lib().oracle_get_num_threads())
+
+
+def philox(seed: int, counter, key1: int = 0) -> np.ndarray:
+    ctr = np.ascontiguousarray(np.array(counter, dtype=np.uint64).reshape(4))
+    out = np.zeros(4, dtype=np.uint64)
+    lib().oracle_philox4x64_10(int(seed) & (2**64 - 1), int(key1), _ptr(ctr), _ptr(out))
+    return out
+
+
+def uniform_from_word(w: int) -> float:
+    return float(lib().oracle_uniform_from_word(int(w)))
+
+
+def topk(logits, k: int):
+    """logits [..., V] (fp32/bf16/fp16) -> (idx int32 [..., k], val fp32 [..., k])."""
+    a, dt = host(logits)
+    if dt is None:
+        a, dt = host(a, np.float32)
+    V = a.shape[-1]
+    rows = int(np.prod(a.shape[:-1]))
+    idx = np.zeros(a.shape[:-1] + (k,), dtype=np.int32)
+    val = np.zeros(a.shape[:-1] + (k,), dtype=np.float32)
+    _check(lib().oracle_topk(_ptr(a), dt, rows, V, k, _ptr(idx), _ptr(val)), "oracle_topk")
+    return idx, val
+
+
+def project(x, w, gate: int = GATE_IDENTITY) -> np.ndarray:
+    """x [n, d] (bf16 or fp32), w [r, d] bf16 -> gate(x @ w.T) in float64."""
+    xa, xdt = host(x)
+    if xdt is None:
+        xa, xdt = host(xa, np.float32)
+    wa, wdt = host(w)
+    assert wdt == BF16
+    n, d = xa.shape
+    r = wa.shape[0]
+    out = np.zeros((n, r), dtype=np.float64)
+    _check(lib().oracle_project(_ptr(xa), xdt, n, d, _ptr(wa), r, gate, _ptr(out)), "oracle_project")
+    return out
+
+
+def pair_scores(cand_idx, cand_val, last_tok, emb, h, w_a, w_b, w_h, gate: int = GATE_IDENTITY,
+                intermediates: bool = False):
+    ci = np.ascontiguousarray(np.asarray(host(cand_idx)[0], dtype=np.int32))
+    cv = np.ascontiguousarray(np.asarray(host(cand_val)[0], dtype=np.float32))
+    lt = np.ascontiguousarray(np.asarray(host(last_tok)[0], dtype=np.int32))
+    ea, edt = host(emb)
+    if edt is None:
+        ea, edt = host(ea, np.float32)
+    ha, hdt = host(h)
+    wa, _ = host(w_a)
+    wb, _ = host(w_b)
+    wh, _ = host(w_h)
+    assert hdt == BF16
+    B, T, K = ci.shape
+    V, d = ea.shape
+    r = wa.shape[0]
+    S = np.zeros((B, T, K, K), dtype=np.float32)
+    outs = [None] * 4
+    if intermediates:
+        outs = [np.zeros((B, r), np.float32), np.zeros((B, T, K, r), np.float32),
+                np.zeros((B, T, K, r), np.float32), np.zeros((B, T, r), np.float32)]
+    _check(lib().oracle_pair_scores(_ptr(ci), _ptr(cv), _ptr(lt), _ptr(ea), edt, V, _ptr(ha),
+                                    _ptr(wa), _ptr(wb), _ptr(wh), B, T, K, d, r, gate, _ptr(S),
+                                    *[_ptr(o) for o in outs]), "oracle_pair_scores")
+    if intermediates:
+        return S, dict(a_last=outs[0], a_cand=outs[1], b_cand=outs[2], h=outs[3])
+    return S
+
+
+def path(scores, cand_idx, mode: int, temperature: float = 0.0, seed: int = 0):
+    """-> dict(rank, tok, q, score, margin)."""
+    S = np.ascontiguousarray(np.asarray(host(scores)[0], dtype=np.float32))
+    ci = np.ascontiguousarray(np.asarray(host(cand_idx)[0], dtype=np.int32))
+    B, T, K, _ = S.shape
+    rank = np.zeros((B, T), np.int32)
+    tok = np.zeros((B, T), np.int32)
+    q = np.zeros((B, T, K), np.float32)
+    score = np.zeros((B,), np.float32)
+    margin = np.zeros((B, T), np.float64)
+    _check(lib().oracle_path(_ptr(S), _ptr(ci), B, T, K, mode, float(temperature),
+                             int(seed) & (2**64 - 1), _ptr(rank), _ptr(tok), _ptr(q), _ptr(score),
+                             _ptr(margin)), "oracle_path")
+    return dict(rank=rank, tok=tok, q=q, score=score, margin=margin)
+
+
+def verify_greedy(target, path_tok):
+    za, zdt = host(target)
+    if zdt is None:
+        za, zdt = host(za, np.float32)
+    pt = np.ascontiguousarray(np.asarray(host(path_tok)[0], dtype=np.int32))
+    B, T = pt.shape
+    V = za.shape[-1]
+    assert za.shape[:2] == (B, T + 1)
+    acc = np.zeros((B,), np.int32)
+    out = np.zeros((B, T + 1), np.int32)
+    am = np.zeros((B, T + 1), np.int32)
+    _check(lib().oracle_verify_greedy(_ptr(za), zdt, V, _ptr(pt), B, T, _ptr(acc), _ptr(out),
+                                      _ptr(am)), "oracle_verify_greedy")
+    return dict(accept_len=acc, out_tok=out, argmax=am)
+
+
+def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, seed: int):
+    za, zdt = host(target)
+    if zdt is None:
+        za, zdt = host(za, np.float32)
+    pt = np.ascontiguousarray(np.asarray(host(path_tok)[0], dtype=np.int32))
+    pr = np.ascontiguousarray(np.asarray(host(path_rank)[0], dtype=np.int32))
+    ci = np.ascontiguousarray(np.asarray(host(cand_idx)[0], dtype=np.int32))
+    qa = np.ascontiguousarray(np.asarray(host(q)[0], dtype=np.float32))
+    B, T = pt.shape
+    K = ci.shape[-1]
+    V = za.shape[-1]
+    assert za.shape[:2] == (B, T + 1)
+    acc = np.zeros((B,), np.int32)
+    out = np.zeros((B, T + 1), np.int32)
+    ma = np.zeros((B, T), np.float64)
+    ms = np.zeros((B,), np.float64)
+    fb = np.zeros((1,), np.int32)
+    _check(lib().oracle_verify_reject(_ptr(za), zdt, V, _ptr(pt), _ptr(pr), _ptr(ci), _ptr(qa), B, T,
+                                      K, float(temperature), int(seed) & (2**64 - 1), _ptr(acc),
+                                      _ptr(out), _ptr(ma), _ptr(ms), _ptr(fb)),
+           "oracle_verify_reject")
+    return dict(accept_len=acc, out_tok=out, margin_accept=ma, margin_sample=ms,
+                fallbacks=int(fb[0]))
+
+
+def dynconv2(x, x_prev, w, base=None, group: int = 16) -> np.ndarray:
+    """x [B, L, d] bf16, x_prev [B, d] bf16 or None, w [2G, d] bf16,
+    base [2, d] fp32 or None -> y [B, L, d] fp32."""
+    xa, xdt = host(x)
+    wa, wdt = host(w)
+    assert xdt == BF16 and wdt == BF16
+    xp = None
+    if x_prev is not None:
+        xp, pdt = host(x_prev)
+        assert pdt == BF16
+    bs = None
+    if base is not None:
+        bs = np.ascontiguousarray(np.asarray(host(base)[0], dtype=np.float32))
+    B, L, d = xa.shape
+    y = np.zeros((B, L, d), np.float32)
+    _check(lib().oracle_dynconv2(_ptr(xa), _ptr(xp), _ptr(wa), _ptr(bs), B, L, d, group, _ptr(y)),
+           "oracle_dynconv2")
+    return y
