@@ -1,0 +1,301 @@
+// api.hip -- the C ABI (include/dflash2.h): argument validation on the host,
+// workspace carving, launches on the caller's stream, status codes.
+// No entry point allocates, synchronises or reads device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/dflash2.h"
+#include "df2_internal.h"
+
+using namespace df2;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) {
+    g_err[0] = 0;
+    return DF2_OK;
+  }
+  return fail(DF2_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_dt(int dt, const char* name) {
+  if (dt != DF2_FP32 && dt != DF2_BF16 && dt != DF2_FP16)
+    return fail(DF2_ERR_DTYPE, "%s: dtype %d is not a dense FP32/BF16/FP16 code", name, dt);
+  return DF2_OK;
+}
+
+int elem_size(int dt) { return dt == DF2_FP32 ? 4 : 2; }
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+constexpr int kMaxT = 63;
+constexpr int64_t kMaxVocab = (int64_t)1 << 31;
+constexpr int kMaxB = 1 << 20;
+
+}  // namespace
+
+extern "C" {
+
+int dflash2_abi_version(void) { return DFLASH2_ABI_VERSION; }
+
+const char* dflash2_status_string(int status) {
+  switch (status) {
+    case DF2_OK: return "ok";
+    case DF2_ERR_NULL: return "null pointer";
+    case DF2_ERR_DTYPE: return "unsupported dtype";
+    case DF2_ERR_SHAPE: return "size out of range";
+    case DF2_ERR_WORKSPACE: return "workspace too small";
+    case DF2_ERR_UNSUPPORTED: return "unsupported mode or temperature";
+    case DF2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dflash2_last_error(void) { return g_err; }
+
+int dflash2_init(void) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "dflash2_init");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_status(e, "dflash2_init");
+  g_err[0] = 0;
+  return DF2_OK;
+}
+
+// ------------------------------------------------------------------ top-K
+size_t dflash2_topk_workspace_bytes(int64_t rows, int64_t vocab, int k) {
+  if (rows <= 0 || vocab <= 0) return 0;
+  return topk_plan(rows, vocab, k).ws_bytes;
+}
+
+int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k, int32_t* out_idx,
+                 float* out_val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dt(dt, "dflash2_topk");
+  if (st) return st;
+  REQUIRE(rows >= 0, DF2_ERR_SHAPE, "dflash2_topk: rows %lld < 0", (long long)rows);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_topk: vocab %lld", (long long)vocab);
+  REQUIRE(k >= 1 && k <= 16 && k <= vocab, DF2_ERR_SHAPE, "dflash2_topk: k %d not in [1, min(16, vocab)]", k);
+  if (rows == 0) return DF2_OK;
+  REQUIRE(logits && out_idx && out_val, DF2_ERR_NULL, "dflash2_topk: null logits/out_idx/out_val");
+  REQUIRE(((uintptr_t)logits % elem_size(dt)) == 0, DF2_ERR_SHAPE, "dflash2_topk: misaligned logits");
+  TopkPlan plan = topk_plan(rows, vocab, k);
+  REQUIRE(plan.ws_bytes == 0 || (ws && ws_bytes >= plan.ws_bytes), DF2_ERR_WORKSPACE,
+          "dflash2_topk: workspace %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  return hip_status(launch_topk(logits, dt, rows, vocab, k, out_idx, out_val, ws, plan, stream),
+                    "dflash2_topk");
+}
+
+// ------------------------------------------------------------------ pair scores
+namespace {
+struct PairWs {
+  size_t ab, alast, h, total;
+};
+PairWs pair_ws(int B, int T, int K, int r) {
+  PairWs w;
+  size_t off = 0;
+  w.ab = off;
+  off += align256((size_t)B * T * K * 2 * r * sizeof(float));
+  w.alast = off;
+  off += align256((size_t)B * r * sizeof(float));
+  w.h = off;
+  off += align256((size_t)B * T * r * sizeof(float));
+  w.total = off;
+  return w;
+}
+}  // namespace
+
+size_t dflash2_pair_scores_workspace_bytes(int B, int T, int K, int d, int r) {
+  (void)d;
+  if (B <= 0 || T <= 0 || K <= 0 || r <= 0) return 0;
+  return pair_ws(B, T, K, r).total;
+}
+
+int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                        const void* emb, int emb_dt, int64_t vocab, const void* h, const void* w_a,
+                        const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
+                        int gate, float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_pair_scores: embedding table must be BF16");
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_pair_scores: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_pair_scores: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_pair_scores: K %d not in [1, 16]", K);
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: d %d is not a positive multiple of 64", d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: r %d not a multiple of 16 in [16, 256]", r);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores: vocab %lld", (long long)vocab);
+  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores: gate %d", gate);
+  if (B == 0) return DF2_OK;
+  REQUIRE(cand_idx && cand_val && last_tok && emb && h && w_a && w_b && w_h && scores, DF2_ERR_NULL,
+          "dflash2_pair_scores: null pointer argument");
+  REQUIRE(aligned16(emb) && aligned16(h) && aligned16(w_a) && aligned16(w_b) && aligned16(w_h),
+          DF2_ERR_SHAPE, "dflash2_pair_scores: emb/h/w_* must be 16-byte aligned");
+  PairWs pw = pair_ws(B, T, K, r);
+  REQUIRE(ws && ws_bytes >= pw.total, DF2_ERR_WORKSPACE, "dflash2_pair_scores: workspace %zu < %zu bytes",
+          ws_bytes, pw.total);
+  float* ab = (float*)((char*)ws + pw.ab);
+  float* alast = (float*)((char*)ws + pw.alast);
+  float* hg = (float*)((char*)ws + pw.h);
+  GemmSeg s[3] = {};
+  // candidates: [A | B] = E[cand] [W_A; W_B]^T
+  s[0].x = (const uint16_t*)emb;
+  s[0].gather = cand_idx;
+  s[0].x_rows = vocab;
+  s[0].ldx = d;
+  s[0].M = B * T * K;
+  s[0].w0 = (const uint16_t*)w_a;
+  s[0].w1 = (const uint16_t*)w_b;
+  s[0].n0 = r;
+  s[0].N = 2 * r;
+  s[0].out = ab;
+  s[0].ldo = 2 * r;
+  s[0].gate = DF2_GATE_IDENTITY;
+  // last verified tokens: A only
+  s[1] = s[0];
+  s[1].gather = last_tok;
+  s[1].M = B;
+  s[1].w1 = (const uint16_t*)w_a;
+  s[1].N = r;
+  s[1].out = alast;
+  s[1].ldo = r;
+  // gate: H = gate(h W_H^T)
+  s[2].x = (const uint16_t*)h;
+  s[2].gather = nullptr;
+  s[2].x_rows = (int64_t)B * T;
+  s[2].ldx = d;
+  s[2].M = B * T;
+  s[2].w0 = (const uint16_t*)w_h;
+  s[2].w1 = (const uint16_t*)w_h;
+  s[2].n0 = r;
+  s[2].N = r;
+  s[2].out = hg;
+  s[2].ldo = r;
+  s[2].gate = gate;
+  hipError_t e = launch_gemm(s, 3, d, 1, 128, stream);
+  if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
+  return hip_status(launch_pair_epilogue(ab, alast, hg, cand_val, B, T, K, r, scores, stream),
+                    "dflash2_pair_scores (epilogue)");
+}
+
+// ------------------------------------------------------------------ path
+int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
+                         float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                         int32_t* path_tok, float* q, float* path_score, hipStream_t stream) {
+  REQUIRE(mode == DF2_PATH_VITERBI || mode == DF2_PATH_GREEDY || mode == DF2_PATH_SAMPLE,
+          DF2_ERR_UNSUPPORTED, "dflash2_path_viterbi: mode %d", mode);
+  REQUIRE(mode != DF2_PATH_SAMPLE || (temperature > 0.f && isfinite(temperature)), DF2_ERR_UNSUPPORTED,
+          "dflash2_path_viterbi: sampling needs a finite temperature > 0 (got %g)", (double)temperature);
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_path_viterbi: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_path_viterbi: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_path_viterbi: K %d not in [1, 16]", K);
+  if (B == 0) return DF2_OK;
+  REQUIRE(scores && cand_idx && path_rank && path_tok && q, DF2_ERR_NULL,
+          "dflash2_path_viterbi: null pointer argument");
+  REQUIRE(mode != DF2_PATH_SAMPLE || seed_dev, DF2_ERR_NULL, "dflash2_path_viterbi: sampling needs seed_dev");
+  return hip_status(launch_path(scores, cand_idx, B, T, K, mode, temperature, seed_dev, path_rank,
+                                path_tok, q, path_score, stream),
+                    "dflash2_path_viterbi");
+}
+
+// ------------------------------------------------------------------ dynconv2
+size_t dflash2_dynconv2_workspace_bytes(int B, int L, int d, int group) {
+  if (B <= 0 || L <= 0 || d <= 0 || group != 16 || d % 64) return 0;
+  return conv_plan(B, L, d, group).ws_bytes;
+}
+
+int dflash2_dynconv2(const void* x, const void* x_prev, const void* w, const float* base, int B,
+                     int L, int d, int group, void* y, int y_dt, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  REQUIRE(y_dt == DF2_BF16 || y_dt == DF2_FP32, DF2_ERR_DTYPE, "dflash2_dynconv2: y dtype %d", y_dt);
+  REQUIRE(group == 16, DF2_ERR_SHAPE, "dflash2_dynconv2: group %d (only 16 is supported)", group);
+  REQUIRE(d >= 64 && d % 64 == 0 && d <= 16384, DF2_ERR_SHAPE, "dflash2_dynconv2: d %d", d);
+  REQUIRE(B >= 0 && L >= 1 && (int64_t)B * L < (1 << 30), DF2_ERR_SHAPE, "dflash2_dynconv2: B %d L %d", B, L);
+  if (B == 0) return DF2_OK;
+  REQUIRE(x && w && y, DF2_ERR_NULL, "dflash2_dynconv2: null x/w/y");
+  REQUIRE(aligned16(x) && aligned16(w) && aligned16(y) && (!x_prev || aligned16(x_prev)), DF2_ERR_SHAPE,
+          "dflash2_dynconv2: x/x_prev/w/y must be 16-byte aligned");
+  ConvPlan plan = conv_plan(B, L, d, group);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_dynconv2: workspace %zu < %zu bytes",
+          ws_bytes, plan.ws_bytes);
+  return hip_status(launch_dynconv2(x, x_prev, w, base, B, L, d, group, y, y_dt == DF2_BF16 ? 1 : 0, ws,
+                                    plan, stream),
+                    "dflash2_dynconv2");
+}
+
+// ------------------------------------------------------------------ verify
+size_t dflash2_verify_workspace_bytes(int B, int T, int64_t vocab) {
+  if (B <= 0 || T <= 0 || vocab <= 0) return 0;
+  return verify_plan(B, T, vocab).ws_bytes;
+}
+
+int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                          int B, int T, int32_t* accept_len, int32_t* out_tok, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  int st = check_dt(dt, "dflash2_verify_greedy");
+  if (st) return st;
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_verify_greedy: vocab %lld", (long long)vocab);
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_verify_greedy: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_greedy: T %d not in [1, %d]", T, kMaxT);
+  if (B == 0) return DF2_OK;
+  REQUIRE(target_logits && path_tok && accept_len && out_tok, DF2_ERR_NULL,
+          "dflash2_verify_greedy: null pointer argument");
+  REQUIRE(((uintptr_t)target_logits % elem_size(dt)) == 0, DF2_ERR_SHAPE, "dflash2_verify_greedy: misaligned logits");
+  VerifyPlan plan = verify_plan(B, T, vocab);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_verify_greedy: workspace %zu < %zu bytes",
+          ws_bytes, plan.ws_bytes);
+  return hip_status(launch_verify_greedy(target_logits, dt, vocab, path_tok, B, T, accept_len, out_tok,
+                                         ws, plan, stream),
+                    "dflash2_verify_greedy");
+}
+
+int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                          const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
+                          int T, int K, float temperature, const uint64_t* seed_dev,
+                          int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  int st = check_dt(dt, "dflash2_verify_reject");
+  if (st) return st;
+  REQUIRE(temperature > 0.f && isfinite(temperature), DF2_ERR_UNSUPPORTED,
+          "dflash2_verify_reject: needs a finite temperature > 0 (got %g)", (double)temperature);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_verify_reject: vocab %lld", (long long)vocab);
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_verify_reject: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_reject: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_verify_reject: K %d not in [1, 16]", K);
+  if (B == 0) return DF2_OK;
+  REQUIRE(target_logits && path_tok && path_rank && cand_idx && q && seed_dev && accept_len && out_tok,
+          DF2_ERR_NULL, "dflash2_verify_reject: null pointer argument");
+  REQUIRE(((uintptr_t)target_logits % elem_size(dt)) == 0, DF2_ERR_SHAPE, "dflash2_verify_reject: misaligned logits");
+  VerifyPlan plan = verify_plan(B, T, vocab);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_verify_reject: workspace %zu < %zu bytes",
+          ws_bytes, plan.ws_bytes);
+  return hip_status(launch_verify_reject(target_logits, dt, vocab, path_tok, path_rank, cand_idx, q, B, T,
+                                         K, temperature, seed_dev, accept_len, out_tok, ws, plan, stream),
+                    "dflash2_verify_reject");
+}
+
+// ------------------------------------------------------------------ Philox
+int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
+                       uint64_t* out, hipStream_t stream) {
+  REQUIRE(n >= 0, DF2_ERR_SHAPE, "dflash2_philox4x64: n %d", n);
+  if (n == 0) return DF2_OK;
+  REQUIRE(seed_dev && b && t && out, DF2_ERR_NULL, "dflash2_philox4x64: null pointer argument");
+  return hip_status(launch_philox(seed_dev, b, t, n, out, stream), "dflash2_philox4x64");
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// df2_device.h -- device-side helpers shared by the HIP kernels of the
+// draft-block library (gfx950, wave64).  Internal; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace df2 {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- elements
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ float half_to_f32(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, sizeof v);
+  return (float)v;
+}
+
+// float -> bf16 bits, round to nearest even (inputs here are finite)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- ordering
+// Order-preserving unsigned code of a float.  -0 is folded onto +0 so that
+// equal values compare equal.
+__device__ __forceinline__ uint32_t ord_of(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float value_of_ord(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+// A (value, index) pair as one integer: larger value first, and among equal
+// values the lower index first.  Distinct indices give distinct keys, so a
+// top-K by key is unique and independent of the order of any merge.  Key 0
+// is never produced for a finite value and serves as "empty".
+__device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
+  return ((uint64_t)ord_of(f) << 32) | (uint64_t)(~idx);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
+__device__ __forceinline__ float key_value(uint64_t k) { return value_of_ord((uint32_t)(k >> 32)); }
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl_xor(lo, m);
+  hi = __shfl_xor(hi, m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// number of set bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return __popcll(m & ((1ull << lane_id()) - 1ull));
+}
+
+// Select the 16 largest keys among n keys held 'per' to a lane (keys[i] of
+// lane l is element l + 64 i); returns the j-th largest in lane j (j < 16),
+// 0 elsewhere or when fewer than j+1 non-empty keys exist.  The selected
+// keys are cleared in 'keys'.
+template <int PER>
+__device__ __forceinline__ uint64_t wave_take16(uint64_t (&keys)[PER]) {
+  uint64_t mine = 0;
+  const int lane = lane_id();
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) best = keys[i] > best ? keys[i] : best;
+    uint64_t top = wave_max_u64(best);
+    if (top == 0) break;
+    if (lane == j) mine = top;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (keys[i] == top) keys[i] = 0;
+  }
+  return mine;
+}
+
+// ---------------------------------------------------------------- Philox
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds; each
+// multiplies counter words 0 and 2 by the round multipliers, and xors the
+// high product halves with words 1/3 and the round key; the key advances by
+// the Weyl increments between rounds.
+struct u64x4 {
+  uint64_t w[4];
+};
+__device__ __forceinline__ u64x4 philox4x64_10(uint64_t key0, uint64_t key1, uint64_t c0,
+                                               uint64_t c1, uint64_t c2, uint64_t c3) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    uint64_t lo0 = M0 * c0, hi0 = __umul64hi(M0, c0);
+    uint64_t lo1 = M1 * c2, hi1 = __umul64hi(M1, c2);
+    uint64_t n0 = hi1 ^ c1 ^ key0, n2 = hi0 ^ c3 ^ key1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+    key0 += W0;
+    key1 += W1;
+  }
+  u64x4 o;
+  o.w[0] = c0;
+  o.w[1] = c1;
+  o.w[2] = c2;
+  o.w[3] = c3;
+  return o;
+}
+// (2 * (w >> 41) + 1) * 2^-24: exact in fp32, inside (0, 1)
+__device__ __forceinline__ float uniform_of_word(uint64_t w) {
+  return (float)(2u * (uint32_t)(w >> 41) + 1u) * (1.0f / 16777216.0f);
+}
+__device__ __forceinline__ float cycle_uniform(uint64_t seed, int b, int t, int word) {
+  u64x4 o = philox4x64_10(seed, 0, (uint64_t)t, (uint64_t)b, 0, 0);
+  return uniform_of_word(o.w[word]);
+}
+
+}  // namespace df2

@@ -1,0 +1,92 @@
+// df2_internal.h -- host-side launchers of the draft-block kernels.
+// Internal; the C ABI (api.hip) validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace df2 {
+
+// Aligned sub-buffer carving of a caller workspace.
+inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// ---- top-K -----------------------------------------------------------------
+struct TopkPlan {
+  int splits;       // work-groups per row
+  int64_t chunk;    // elements per split (multiple of 64)
+  size_t ws_bytes;  // partial-key buffer
+};
+TopkPlan topk_plan(int64_t rows, int64_t vocab, int k);
+hipError_t launch_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
+                       int32_t* out_idx, float* out_val, void* ws, const TopkPlan& plan,
+                       hipStream_t stream);
+
+// ---- projection GEMM (bf16 MFMA, fp32 out) --------------------------------
+struct GemmSeg {
+  const uint16_t* x;      // bf16 rows
+  const int32_t* gather;  // nullable: row ids into x (-> zero row if outside [0, x_rows))
+  int64_t x_rows;         // number of rows x holds (bound for gather)
+  int64_t ldx;            // elements between rows of x
+  int M;                  // rows of the product
+  const uint16_t* w0;     // W rows 0..n0-1
+  const uint16_t* w1;     // W rows n0..N-1 (row n -> w1[n - n0])
+  int n0;
+  int N;                  // output columns (multiple of 16)
+  float* out;             // out[m * ldo + n] (+ kslice * out_kstride)
+  int64_t ldo;
+  int64_t out_kstride;    // elements between K-slice partial outputs
+  int gate;               // 0 identity, 1 sigmoid (only when ksplit == 1)
+  int tiles_m, tiles_n;   // filled by the launcher
+};
+// out = gate(X W^T) for up to 3 segments in one launch; K = d (multiple of 64)
+hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
+                       hipStream_t stream);
+
+// ---- pair scores epilogue ---------------------------------------------------
+hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
+                                const float* cand_val, int B, int T, int K, int r,
+                                float* scores, hipStream_t stream);
+
+// ---- path ------------------------------------------------------------------
+hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
+                       float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                       int32_t* path_tok, float* q, float* path_score, hipStream_t stream);
+
+// ---- verification ------------------------------------------------------------
+struct VerifyPlan {
+  int splits;        // work-groups per target row in the streaming pass
+  int64_t chunk;     // elements per split
+  int rchunks;       // chunks of the residual scan per request
+  int64_t rchunk;    // elements per residual chunk
+  size_t off_part;   // partial results [rows, splits] (8 bytes each)
+  size_t off_dec;    // per-request decision record
+  size_t off_rsum;   // residual chunk sums [B, rchunks]
+  size_t ws_bytes;
+};
+VerifyPlan verify_plan(int B, int T, int64_t vocab);
+hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
+                                int B, int T, int32_t* accept_len, int32_t* out_tok, void* ws,
+                                const VerifyPlan& plan, hipStream_t stream);
+hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
+                                const int32_t* path_rank, const int32_t* cand_idx, const float* q,
+                                int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                                int32_t* accept_len, int32_t* out_tok, void* ws,
+                                const VerifyPlan& plan, hipStream_t stream);
+
+// ---- two-tap dynamic conv ---------------------------------------------------
+struct ConvPlan {
+  int ksplit;
+  int bm;
+  size_t ws_bytes;
+};
+ConvPlan conv_plan(int B, int L, int d, int group);
+hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, const float* base,
+                           int B, int L, int d, int group, void* y, int y_dt, void* ws,
+                           const ConvPlan& plan, hipStream_t stream);
+
+// ---- Philox words -----------------------------------------------------------
+hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
+                         uint64_t* out, hipStream_t stream);
+
+}  // namespace df2

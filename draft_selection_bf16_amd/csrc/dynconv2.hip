@@ -1,0 +1,148 @@
+// dynconv2.hip -- two-tap dynamic depthwise convolution.
+//
+// "DFlash 2: Keep Drafting Parallel", section "A lightweight local
+// convolution", equation Conv_k(x)_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1}:
+// each tap is a learned base kernel plus a correction computed from the
+// current hidden state, one correction per 16 channels; the first position
+// reads the last verified token (Fig. 4).  With c_t = W x_t in R^{2G}:
+//   y_t[ch] = (base0[ch] + c_t[ch/16]) x_t[ch] + (base1[ch] + c_t[G + ch/16]) x_{t-1}[ch].
+//
+// Two launches per application:
+//  1. the tap corrections c = X W^T on the matrix cores (gemm.hip), with the
+//     reduction over d split into slices so that a few hundred work-groups
+//     share a skinny problem (M = B*L rows, N = 2G, K = d); each slice
+//     writes its own partial product;
+//  2. a streaming epilogue, one work-group per (b, t) row: sums the slice
+//     partials of its 2G taps in a fixed order into LDS, then reads x_t and
+//     x_{t-1} with 16-byte loads and writes y (bf16 round-to-nearest-even, or
+//     fp32).
+#include "df2_device.h"
+#include "df2_internal.h"
+
+namespace df2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxTaps = 2048;   // 2G <= 2048  <=>  d <= 16384
+
+template <bool Y_BF16>
+__global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ x_prev,
+    const float* __restrict__ base, const float* __restrict__ part, int ksplit, int64_t kstride,
+    int L, int d, void* __restrict__ y) {
+  __shared__ float sc[kMaxTaps];
+  const int row = blockIdx.x;          // b * L + t
+  const int b = row / L, t = row % L;
+  const int G = d / 16, NT = 2 * G;
+  for (int n = threadIdx.x; n < NT; n += kThreads) {
+    const float* p = part + (int64_t)row * NT + n;
+    float acc = 0.f;
+    for (int s = 0; s < ksplit; ++s) acc += p[(int64_t)s * kstride];
+    sc[n] = acc;
+  }
+  __syncthreads();
+  const uint16_t* xt = x + (int64_t)row * d;
+  const uint16_t* xp = t > 0 ? x + (int64_t)(row - 1) * d : (x_prev ? x_prev + (int64_t)b * d : nullptr);
+  // 8 channels per 16-byte load; channel groups of 16 never straddle a load
+  for (int c8 = threadIdx.x; c8 < d / 8; c8 += kThreads) {
+    const int ch0 = c8 * 8, g = ch0 / 16;
+    const u32x4 vx = *(const u32x4*)(xt + ch0);
+    const u32x4 vp = xp ? *(const u32x4*)(xp + ch0) : u32x4{0u, 0u, 0u, 0u};
+    const float c0 = sc[g], c1 = sc[G + g];
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wx = vx[e >> 1], wp = vp[e >> 1];
+      const float fx = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
+      const float fp = (e & 1) ? bf16_hi(wp) : bf16_lo(wp);
+      const float k0 = base ? base[ch0 + e] + c0 : c0;
+      const float k1 = base ? base[d + ch0 + e] + c1 : c1;
+      out[e] = fmaf(k0, fx, k1 * fp);
+    }
+    if (Y_BF16) {
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        o[h] = (uint32_t)f32_to_bf16_rne(out[2 * h]) | ((uint32_t)f32_to_bf16_rne(out[2 * h + 1]) << 16);
+      *(u32x4*)((uint16_t*)y + (int64_t)row * d + ch0) = o;
+    } else {
+      float* yo = (float*)y + (int64_t)row * d + ch0;
+      *(f32x4*)yo = f32x4{out[0], out[1], out[2], out[3]};
+      *(f32x4*)(yo + 4) = f32x4{out[4], out[5], out[6], out[7]};
+    }
+  }
+}
+
+}  // namespace
+
+ConvPlan conv_plan(int B, int L, int d, int group) {
+  (void)group;
+  ConvPlan p;
+  p.bm = 64;
+  const int M = B * L, N = 2 * (d / 16);
+  const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
+  const int nk = d / 64;
+  // smallest divisor of d/64 that gives >= 256 work-groups (at most 16 slices)
+  int ks = 1;
+  for (int s = 1; s <= nk && s <= 16; ++s) {
+    if (nk % s) continue;
+    ks = s;
+    if (tiles * s >= 256) break;
+  }
+  p.ksplit = ks;
+  p.ws_bytes = align256((size_t)ks * (size_t)M * (size_t)N * sizeof(float));
+  return p;
+}
+
+hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, const float* base,
+                           int B, int L, int d, int group, void* y, int y_dt, void* ws,
+                           const ConvPlan& plan, hipStream_t stream) {
+  (void)group;
+  const int M = B * L, G = d / 16, N = 2 * G;
+  if (M == 0) return hipSuccess;
+  float* part = (float*)ws;
+  GemmSeg s{};
+  s.x = (const uint16_t*)x;
+  s.gather = nullptr;
+  s.x_rows = M;
+  s.ldx = d;
+  s.M = M;
+  s.w0 = (const uint16_t*)w;
+  s.w1 = (const uint16_t*)w;
+  s.n0 = N;
+  s.N = N;
+  s.out = part;
+  s.ldo = N;
+  s.out_kstride = (int64_t)M * N;
+  s.gate = 0;
+  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, stream);
+  if (e != hipSuccess) return e;
+  if (y_dt == 1)
+    conv_epilogue_kernel<true><<<dim3(M), dim3(kThreads), 0, stream>>>(
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
+  else
+    conv_epilogue_kernel<false><<<dim3(M), dim3(kThreads), 0, stream>>>(
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Philox words
+namespace {
+__global__ void philox_kernel(const uint64_t* __restrict__ seed_dev, const int32_t* __restrict__ b,
+                              const int32_t* __restrict__ t, int n, uint64_t* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  u64x4 o = philox4x64_10(seed_dev[0], 0, (uint64_t)(uint32_t)t[i], (uint64_t)(uint32_t)b[i], 0, 0);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[(int64_t)i * 4 + k] = o.w[k];
+}
+}  // namespace
+
+hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
+                         uint64_t* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  philox_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(seed_dev, b, t, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace df2

@@ -1,0 +1,212 @@
+// select.hip -- the path selector after the projections: bilinear pair
+// scores and the path through the K x K lattices.
+//
+// Pair score ("DFlash 2: Keep Drafting Parallel", section "A lightweight
+// path selector", equation S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>):
+// one work-group per (request, position); the predecessor rows A(a) (the
+// candidates of position t-1, or the last verified token at t = 0) are
+// scaled by the gate H_t once in LDS, then each of the K x K threads takes
+// one r-long dot product with B(b).  fp32 throughout.
+//
+// Path (same section; and "DFlash 2 讓 Qwen3.8-27B 快了兩倍", item 2 --
+// Viterbi): one wave per request.  VITERBI keeps delta_t[j] = max_i
+// delta_{t-1}[i] + S_t[i][j] with back-pointers in LDS: lane l owns target
+// rank j = l & 15 and four predecessors i = 4 (l >> 4) + e, and the four
+// lane groups are combined with cross-lane max (value, lowest rank).
+// GREEDY follows the best successor; SAMPLE draws c_t from
+// softmax_j(S_t(c_{t-1}, j) / tau) by inverse CDF in rank order with a
+// Philox uniform.  Path sums are float additions.
+#include "df2_device.h"
+#include "df2_internal.h"
+
+namespace df2 {
+namespace {
+
+constexpr int kMaxR = 256;
+
+__global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
+                                                            const float* __restrict__ a_last,
+                                                            const float* __restrict__ hgate,
+                                                            const float* __restrict__ cand_val,
+                                                            int T, int K, int r,
+                                                            float* __restrict__ scores) {
+  __shared__ float sG[16][kMaxR + 1];   // A(pred) * H_t
+  __shared__ float sB[16][kMaxR + 1];   // B(cand)
+  const int bt = blockIdx.x, b = bt / T, t = bt % T;
+  const int tid = threadIdx.x;
+  const int npred = t == 0 ? 1 : K;
+  const float* H = hgate + (int64_t)bt * r;
+  // stage: predecessor rows scaled by the gate, candidate B rows
+  for (int e = tid; e < npred * r; e += blockDim.x) {
+    int i = e / r, q = e % r;
+    float a = t == 0 ? a_last[(int64_t)b * r + q]
+                     : ab[((int64_t)(bt - 1) * K + i) * (2 * r) + q];
+    sG[i][q] = a * H[q];
+  }
+  for (int e = tid; e < K * r; e += blockDim.x) {
+    int j = e / r, q = e % r;
+    sB[j][q] = ab[((int64_t)bt * K + j) * (2 * r) + r + q];
+  }
+  __syncthreads();
+  const int i = tid / 16, j = tid % 16;
+  if (i >= K || j >= K) return;
+  float* out = scores + ((int64_t)bt * K + i) * K + j;
+  if (i >= npred) {
+    *out = -INFINITY;
+    return;
+  }
+  float acc = 0.f;
+  for (int q = 0; q < r; ++q) acc = fmaf(sG[i][q], sB[j][q], acc);
+  *out = cand_val[(int64_t)bt * K + j] + acc;
+}
+
+// (value, rank) comparison: larger value, then lower rank
+__device__ __forceinline__ bool better(float v1, int i1, float v0, int i0) {
+  return v1 > v0 || (v1 == v0 && i1 < i0);
+}
+
+__global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ cand_idx, int T,
+                                                  int K, int mode, float inv_tau,
+                                                  const uint64_t* __restrict__ seed_dev,
+                                                  int32_t* __restrict__ path_rank,
+                                                  int32_t* __restrict__ path_tok,
+                                                  float* __restrict__ q, float* __restrict__ path_score) {
+  __shared__ uint8_t psi[64][16];
+  __shared__ int32_t chosen[64];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const float* S = scores + (int64_t)b * T * K * K;
+  const int j = lane & 15;
+  float total = 0.f;
+
+  if (mode == 0) {  // VITERBI
+    const int ig = lane >> 4;
+    float delta = (j < K) ? S[j] : -INFINITY;   // held by lanes with ig == 0 (all groups copy)
+    for (int t = 1; t < T; ++t) {
+      float best = -INFINITY;
+      int arg = ig * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int i = ig * 4 + e;
+        float di = __shfl(delta, i);   // delta_{t-1}[i] from lane i
+        if (i < K && j < K) {
+          float v = di + S[((int64_t)t * K + i) * K + j];
+          if (v > best) {
+            best = v;
+            arg = i;
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        float ob = __shfl_xor(best, m);
+        int oa = __shfl_xor(arg, m);
+        if (better(ob, oa, best, arg)) {
+          best = ob;
+          arg = oa;
+        }
+      }
+      if (lane < 16) psi[t][lane] = (uint8_t)arg;
+      delta = (j < K) ? best : -INFINITY;
+    }
+    // end argmax over j (lowest rank on ties)
+    float bv = (lane < K) ? delta : -INFINITY;
+    int bi = lane < K ? lane : 64;
+    for (int m = 1; m < 16; m <<= 1) {
+      float ov = __shfl_xor(bv, m);
+      int oi = __shfl_xor(bi, m);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      int c = bi;
+      chosen[T - 1] = c;
+      for (int t = T - 1; t >= 1; --t) {
+        c = psi[t][c];
+        chosen[t - 1] = c;
+      }
+      total = bv;
+    }
+    __syncthreads();
+  } else {
+    const uint64_t seed = (mode == 2) ? seed_dev[0] : 0ull;
+    int prev = 0;
+    for (int t = 0; t < T; ++t) {
+      float v = (lane < K) ? S[((int64_t)t * K + prev) * K + lane] : -INFINITY;
+      int pick;
+      if (mode == 1) {  // GREEDY
+        float bv = v;
+        int bi = lane < K ? lane : 64;
+        for (int m = 1; m < 64; m <<= 1) {
+          float ov = __shfl_xor(bv, m);
+          int oi = __shfl_xor(bi, m);
+          if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        pick = bi;
+        if (lane < K) q[((int64_t)b * T + t) * K + lane] = lane == pick ? 1.f : 0.f;
+      } else {  // SAMPLE
+        float mx = wave_max_f32(v);
+        float e = (lane < K) ? expf((v - mx) * inv_tau) : 0.f;
+        float z = wave_sum_f32(e);
+        float p = e / z;
+        // inclusive prefix sum in rank order
+        float c = p;
+        for (int m = 1; m < 16; m <<= 1) {
+          float o = __shfl_up(c, m);
+          if (lane >= m) c += o;
+        }
+        float u = cycle_uniform(seed, b, t, 0);
+        uint64_t over = ballot(lane < K && c > u);
+        if (over) {
+          pick = __ffsll((unsigned long long)over) - 1;
+        } else {  // rounding: take the last rank with mass
+          uint64_t nz = ballot(lane < K && p > 0.f);
+          pick = nz ? 63 - __clzll((unsigned long long)nz) : 0;
+        }
+        if (lane < K) q[((int64_t)b * T + t) * K + lane] = p;
+      }
+      float sv = __shfl(v, pick);
+      total = (t == 0) ? sv : total + sv;
+      if (lane == 0) chosen[t] = pick;
+      prev = pick;
+    }
+    __syncthreads();
+  }
+  for (int t = lane; t < T; t += 64) {
+    int c = chosen[t];
+    path_rank[(int64_t)b * T + t] = c;
+    path_tok[(int64_t)b * T + t] = cand_idx[((int64_t)b * T + t) * K + c];
+    if (mode == 0)
+      for (int k = 0; k < K; ++k) q[((int64_t)b * T + t) * K + k] = k == c ? 1.f : 0.f;
+  }
+  if (lane == 0 && path_score) path_score[b] = total;
+}
+
+}  // namespace
+
+hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
+                                const float* cand_val, int B, int T, int K, int r, float* scores,
+                                hipStream_t stream) {
+  if (B * T == 0) return hipSuccess;
+  pair_epilogue_kernel<<<dim3(B * T), dim3(256), 0, stream>>>(ab, a_last, hgate, cand_val, T, K, r,
+                                                                scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
+                       float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                       int32_t* path_tok, float* q, float* path_score, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  float inv_tau = mode == 2 ? 1.0f / temperature : 0.f;
+  path_kernel<<<dim3(B), dim3(64), 0, stream>>>(scores, cand_idx, T, K, mode, inv_tau, seed_dev,
+                                                path_rank, path_tok, q, path_score);
+  return hipGetLastError();
+}
+
+}  // namespace df2

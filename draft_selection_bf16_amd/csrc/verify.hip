@@ -1,0 +1,583 @@
+// verify.hip -- lossless verification of the drafted path against the
+// target's logits.
+//
+// Greedy ("DFlash 2 讓 Qwen3.8-27B 快了兩倍", section "輸出完全一致"; the
+// teaikeji explainer, section 五): the emitted tokens are the target's own
+// argmax chain -- the accepted drafts, then the target's token at the first
+// disagreement (or the bonus token of row T).
+// Rejection sampling ("DFlash 2: Keep Drafting Parallel", section "A
+// lightweight path selector": rejection sampling restores the exact target
+// distribution): accept draft t with probability min(1, p/q); at the first
+// rejection draw from max(0, p - q) by index-order inverse CDF.
+//
+// Both are one streaming pass over the [B, T+1, V] target logits (16-byte
+// loads, several work-groups per row, per-row partials merged by a small
+// kernel) plus O(B) follow-up work:
+//   greedy : row argmax partials -> per-request prefix check;
+//   reject : row (argmax, sum of exp) partials -> per-request accept chain
+//            -> residual mass per vocabulary chunk of the one row that is
+//            resampled -> chunk search and in-chunk scan.
+// Probabilities are fp32, p(v) = 2^((z_v - m) * log2(e) / tau) / s.
+#include "df2_device.h"
+#include "df2_internal.h"
+
+namespace df2 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kUnroll = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct DecRec {  // per-request decision of the rejection pass
+  int n;         // accepted drafts; the row that is (re)sampled
+  int argmax;    // lowest argmax of that row (fallback when no mass)
+  float m, s;    // row max and sum of exp2((z - m) c)
+  float u2;      // the uniform of the draw
+  float pad;
+};
+
+struct RowPart {  // streaming partial of one chunk of one row
+  uint64_t key;   // (max value, lowest index) of the chunk
+  float s;        // sum of exp2((z - value(key)) c) over the chunk
+  float pad;
+};
+
+template <int DT>
+struct Elt;
+template <>
+struct Elt<0> {
+  static constexpr int VN = 4, ESZ = 4;
+  __device__ static float vget(const u32x4& v, int e) { return __uint_as_float(v[e]); }
+  __device__ static float one(const void* p, int64_t i) { return ((const float*)p)[i]; }
+};
+template <>
+struct Elt<1> {
+  static constexpr int VN = 8, ESZ = 2;
+  __device__ static float vget(const u32x4& v, int e) {
+    uint32_t w = v[e >> 1];
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  }
+  __device__ static float one(const void* p, int64_t i) { return bf16_to_f32(((const uint16_t*)p)[i]); }
+};
+template <>
+struct Elt<2> {
+  static constexpr int VN = 8, ESZ = 2;
+  __device__ static float vget(const u32x4& v, int e) {
+    uint32_t w = v[e >> 1];
+    return half_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+  }
+  __device__ static float one(const void* p, int64_t i) { return half_to_f32(((const uint16_t*)p)[i]); }
+};
+
+// Visit elements [lo, hi) of a row: scalar head/tail up to 16-byte
+// alignment, vector body with kUnroll loads in flight per thread.  Within a
+// thread the visiting order is increasing in index.
+template <int DT, typename F>
+__device__ __forceinline__ void stream_row(const void* rowp, int64_t lo, int64_t hi, F& f) {
+  using E = Elt<DT>;
+  const int tid = threadIdx.x;
+  const uintptr_t base = (uintptr_t)rowp;
+  uintptr_t p0 = base + (uintptr_t)lo * E::ESZ;
+  int64_t head = (int64_t)(((16 - (p0 & 15)) & 15) / E::ESZ);
+  int64_t a0 = lo + head < hi ? lo + head : hi;
+  int64_t a1 = a0 + (hi - a0) / E::VN * E::VN;
+  for (int64_t i = lo + tid; i < a0; i += kThreads) f.one(E::one(rowp, i), i);
+  const u32x4* vp = (const u32x4*)(base + (uintptr_t)a0 * E::ESZ);
+  const int64_t ng = (a1 - a0) / E::VN;
+  for (int64_t g0 = tid; g0 < ng; g0 += (int64_t)kThreads * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t g = g0 + (int64_t)u * kThreads;
+      v[u] = g < ng ? __builtin_nontemporal_load(vp + g) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t g = g0 + (int64_t)u * kThreads;
+      if (g < ng) {
+        float x[E::VN];
+#pragma unroll
+        for (int e = 0; e < E::VN; ++e) x[e] = E::vget(v[u], e);
+        f.template group<E::VN>(x, a0 + g * E::VN);
+      }
+    }
+  }
+  for (int64_t i = a1 + tid; i < hi; i += kThreads) f.one(E::one(rowp, i), i);
+}
+
+// ---------------------------------------------------------------- argmax
+struct ArgMax {
+  float best = -INFINITY;
+  int64_t idx = -1;
+  __device__ void one(float x, int64_t i) {
+    if (x > best || (idx < 0 && x == x)) {  // NaN is never taken
+      best = x;
+      idx = i;
+    }
+  }
+  template <int N>
+  __device__ void group(const float (&x)[N], int64_t i0) {
+    float gm = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) gm = fmaxf(gm, x[e]);
+    if (gm > best || idx < 0) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) one(x[e], i0 + e);
+    }
+  }
+};
+
+__device__ __forceinline__ uint64_t block_max_key(uint64_t k, uint64_t* sred) {
+  k = wave_max_u64(k);
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) sred[wave] = k;
+  __syncthreads();
+  uint64_t r = sred[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = sred[w] > r ? sred[w] : r;
+  __syncthreads();
+  return r;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void argmax_part_kernel(const void* __restrict__ z,
+                                                               int64_t vocab, int splits,
+                                                               int64_t chunk,
+                                                               uint64_t* __restrict__ part) {
+  __shared__ uint64_t sred[kWaves];
+  const int64_t row = blockIdx.x / splits;
+  const int sp = blockIdx.x % splits;
+  const int64_t lo = (int64_t)sp * chunk, hi = lo + chunk < vocab ? lo + chunk : vocab;
+  const void* rowp = (const char*)z + row * vocab * Elt<DT>::ESZ;
+  ArgMax f;
+  stream_row<DT>(rowp, lo, hi, f);
+  uint64_t k = f.idx >= 0 ? make_key(f.best, (uint32_t)f.idx) : 0ull;
+  k = block_max_key(k, sred);
+  if (threadIdx.x == 0) part[row * splits + sp] = k;
+}
+
+// one wave per request: merge the argmax partials of rows t = 0..T, then the
+// longest agreeing prefix
+__global__ __launch_bounds__(64) void greedy_final_kernel(const uint64_t* __restrict__ part,
+                                                          int splits, int T,
+                                                          const int32_t* __restrict__ path_tok,
+                                                          int32_t* __restrict__ accept_len,
+                                                          int32_t* __restrict__ out_tok) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  int y = -1;
+  if (lane <= T) {
+    const uint64_t* p = part + ((int64_t)b * (T + 1) + lane) * splits;
+    uint64_t k = 0;
+    for (int s = 0; s < splits; ++s) k = p[s] > k ? p[s] : k;
+    y = k ? (int)key_index(k) : -1;
+  }
+  bool miss = lane < T && path_tok[(int64_t)b * T + lane] != y;
+  uint64_t mm = ballot(miss);
+  int n = mm ? __ffsll((unsigned long long)mm) - 1 : T;
+  int yn = __shfl(y, n);
+  if (lane == 0) accept_len[b] = n;
+  if (lane <= T) {
+    int v = lane < n ? path_tok[(int64_t)b * T + lane] : lane == n ? yn : -1;
+    out_tok[(int64_t)b * (T + 1) + lane] = v;
+  }
+}
+
+// ---------------------------------------------------------------- softmax stats
+struct SumExp {
+  float c;            // log2(e) / tau
+  float m = -INFINITY;
+  float s = 0.f;
+  int64_t idx = -1;   // lowest index of the running max
+  __device__ void one(float x, int64_t i) {
+    if (x > m) {
+      s = (m == -INFINITY) ? 0.f : s * exp2f((m - x) * c);
+      m = x;
+      idx = i;
+    }
+    s += exp2f((x - m) * c);
+  }
+  template <int N>
+  __device__ void group(const float (&x)[N], int64_t i0) {
+    float gm = x[0];
+#pragma unroll
+    for (int e = 1; e < N; ++e) gm = fmaxf(gm, x[e]);
+    if (gm > m) {
+      s = (m == -INFINITY) ? 0.f : s * exp2f((m - gm) * c);
+      m = gm;
+#pragma unroll
+      for (int e = N - 1; e >= 0; --e)
+        if (x[e] == gm) idx = i0 + e;
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) s += exp2f((x[e] - m) * c);
+  }
+};
+
+// combine two (key, s) partials, both sums relative to their own max
+__device__ __forceinline__ void combine_part(uint64_t& k, float& s, uint64_t k2, float s2, float c) {
+  if (k2 == 0ull) return;
+  if (k == 0ull) {
+    k = k2;
+    s = s2;
+    return;
+  }
+  float m1 = key_value(k), m2 = key_value(k2);
+  if (k2 > k) {
+    s = s * exp2f((m1 - m2) * c) + s2;
+    k = k2;
+  } else {
+    s = s + s2 * exp2f((m2 - m1) * c);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sumexp_part_kernel(const void* __restrict__ z,
+                                                               int64_t vocab, int splits,
+                                                               int64_t chunk, float c,
+                                                               RowPart* __restrict__ part) {
+  __shared__ uint64_t sk[kWaves];
+  __shared__ float ss[kWaves];
+  const int64_t row = blockIdx.x / splits;
+  const int sp = blockIdx.x % splits;
+  const int64_t lo = (int64_t)sp * chunk, hi = lo + chunk < vocab ? lo + chunk : vocab;
+  const void* rowp = (const char*)z + row * vocab * Elt<DT>::ESZ;
+  SumExp f;
+  f.c = c;
+  stream_row<DT>(rowp, lo, hi, f);
+  uint64_t k = f.idx >= 0 ? make_key(f.m, (uint32_t)f.idx) : 0ull;
+  float s = f.idx >= 0 ? f.s : 0.f;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t k2 = shfl_xor_u64(k, m);
+    float s2 = __shfl_xor(s, m);
+    // symmetric combine so that both lanes hold the same result
+    uint64_t ka = k < k2 ? k : k2, kb = k < k2 ? k2 : k;
+    float sa = k < k2 ? s : s2, sb = k < k2 ? s2 : s;
+    combine_part(kb, sb, ka, sa, c);
+    k = kb;
+    s = sb;
+  }
+  const int wave = threadIdx.x / kWave;
+  if (lane_id() == 0) {
+    sk[wave] = k;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t K0 = sk[0];
+    float S0 = ss[0];
+    for (int w = 1; w < kWaves; ++w) combine_part(K0, S0, sk[w], ss[w], c);
+    RowPart r;
+    r.key = K0;
+    r.s = S0;
+    r.pad = 0.f;
+    part[row * splits + sp] = r;
+  }
+}
+
+// one wave per request: row statistics, accept chain, decision record
+template <int DT>
+__global__ __launch_bounds__(64) void reject_decide_kernel(
+    const void* __restrict__ z, int64_t vocab, const RowPart* __restrict__ part, int splits, int T,
+    int K, float c, const int32_t* __restrict__ path_tok, const int32_t* __restrict__ path_rank,
+    const float* __restrict__ q, const uint64_t* __restrict__ seed_dev,
+    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok, DecRec* __restrict__ dec) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const uint64_t seed = seed_dev[0];
+  uint64_t k = 0ull;
+  float s = 0.f;
+  if (lane <= T) {
+    const RowPart* p = part + ((int64_t)b * (T + 1) + lane) * splits;
+    for (int i = 0; i < splits; ++i) combine_part(k, s, p[i].key, p[i].s, c);
+  }
+  bool reject = false;
+  if (lane < T) {
+    const int32_t x = path_tok[(int64_t)b * T + lane];
+    const int rk = path_rank[(int64_t)b * T + lane];
+    const float qx = (rk >= 0 && rk < K) ? q[((int64_t)b * T + lane) * K + rk] : 0.f;
+    float px = 0.f;
+    if (x >= 0 && x < vocab) {
+      const void* rowp = (const char*)z + ((int64_t)b * (T + 1) + lane) * vocab * Elt<DT>::ESZ;
+      float zx = Elt<DT>::one(rowp, x);
+      px = exp2f((zx - key_value(k)) * c) / s;
+    }
+    const float u1 = cycle_uniform(seed, b, lane, 1);
+    const bool accept = qx <= 0.f || u1 < px / qx;
+    reject = !accept;
+  }
+  uint64_t rm = ballot(reject);
+  const int n = rm ? __ffsll((unsigned long long)rm) - 1 : T;
+  uint32_t klo = __shfl((uint32_t)k, n), khi = __shfl((uint32_t)(k >> 32), n);
+  float sn = __shfl(s, n);
+  uint64_t knn = ((uint64_t)khi << 32) | klo;
+  if (lane == 0) {
+    accept_len[b] = n;
+    DecRec d;
+    d.n = n;
+    d.argmax = knn ? (int)key_index(knn) : 0;
+    d.m = key_value(knn);
+    d.s = sn;
+    d.u2 = cycle_uniform(seed, b, n, 2);
+    d.pad = 0.f;
+    dec[b] = d;
+  }
+  if (lane <= T && lane != n)
+    out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? path_tok[(int64_t)b * T + lane] : -1;
+}
+
+// residual weight of entry v of the resampled row
+struct Residual {
+  float m, s, c;
+  int ncand;            // candidates falling in the current range
+  int32_t cid[16];
+  float cq[16];
+  __device__ __forceinline__ float w(float x, int64_t v) const {
+    float p = exp2f((x - m) * c) / s;
+    for (int i = 0; i < ncand; ++i)
+      if (cid[i] == v) {
+        float r = p - cq[i];
+        return r > 0.f ? r : 0.f;
+      }
+    return p;
+  }
+};
+
+struct ResidualSum {
+  const Residual* R;
+  float acc = 0.f;
+  __device__ void one(float x, int64_t i) { acc += R->w(x, i); }
+  template <int N>
+  __device__ void group(const float (&x)[N], int64_t i0) {
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc += R->w(x[e], i0 + e);
+  }
+};
+
+// load the decision and the candidates of the resampled row that lie in
+// [lo, hi) into LDS (thread 0), return the row pointer
+template <int DT>
+__device__ __forceinline__ const void* residual_setup(
+    Residual& R, const void* z, int64_t vocab, int T, int K, float c, int b,
+    const DecRec* dec, const int32_t* cand_idx, const float* q, int64_t lo, int64_t hi) {
+  const DecRec d = dec[b];
+  R.m = d.m;
+  R.s = d.s;
+  R.c = c;
+  R.ncand = 0;
+  if (d.n < T) {
+    for (int kk = 0; kk < K; ++kk) {
+      int32_t v = cand_idx[((int64_t)b * T + d.n) * K + kk];
+      if (v >= lo && v < hi) {
+        R.cid[R.ncand] = v;
+        R.cq[R.ncand] = q[((int64_t)b * T + d.n) * K + kk];
+        R.ncand++;
+      }
+    }
+  }
+  return (const char*)z + ((int64_t)b * (T + 1) + d.n) * vocab * Elt<DT>::ESZ;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void residual_chunk_kernel(
+    const void* __restrict__ z, int64_t vocab, int T, int K, float c, int rchunks, int64_t rchunk,
+    const DecRec* __restrict__ dec, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ q, float* __restrict__ rsum) {
+  __shared__ Residual R;
+  __shared__ float sred[kWaves];
+  const int b = blockIdx.x / rchunks, ch = blockIdx.x % rchunks;
+  const int64_t lo = (int64_t)ch * rchunk, hi = lo + rchunk < vocab ? lo + rchunk : vocab;
+  __shared__ const void* srow;
+  if (threadIdx.x == 0) srow = residual_setup<DT>(R, z, vocab, T, K, c, b, dec, cand_idx, q, lo, hi);
+  __syncthreads();
+  ResidualSum f;
+  f.R = &R;
+  if (lo < hi) stream_row<DT>(srow, lo, hi, f);
+  float v = wave_sum_f32(f.acc);
+  if (lane_id() == 0) sred[threadIdx.x / kWave] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kWaves; ++w) t += sred[w];
+    rsum[(int64_t)b * rchunks + ch] = t;
+  }
+}
+
+// one work-group per request: find the chunk where the running mass passes
+// u2 * total, then the entry inside it
+template <int DT>
+__global__ __launch_bounds__(kThreads) void residual_find_kernel(
+    const void* __restrict__ z, int64_t vocab, int T, int K, float c, int rchunks, int64_t rchunk,
+    const DecRec* __restrict__ dec, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ q, const float* __restrict__ rsum, int32_t* __restrict__ out_tok) {
+  __shared__ Residual R;
+  __shared__ const void* srow;
+  __shared__ float s_target;
+  __shared__ int s_chunk;
+  __shared__ float sscan[kThreads];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const DecRec d = dec[b];
+  if (tid < kWave) {  // wave 0: prefix over chunk sums (rchunks <= 64)
+    float v = tid < rchunks ? rsum[(int64_t)b * rchunks + tid] : 0.f;
+    float incl = v;
+    for (int m = 1; m < 64; m <<= 1) {
+      float o = __shfl_up(incl, m);
+      if (tid >= m) incl += o;
+    }
+    float total = __shfl(incl, 63);
+    float target = d.u2 * total;
+    uint64_t over = ballot(tid < rchunks && incl > target);
+    uint64_t nz = ballot(tid < rchunks && v > 0.f);
+    int ch;
+    float before;
+    if (!(total > 0.f)) {
+      ch = -1;  // no residual mass
+      before = 0.f;
+    } else if (over) {
+      ch = __ffsll((unsigned long long)over) - 1;
+      before = __shfl(incl - v, ch);
+    } else {
+      ch = 63 - __clzll((unsigned long long)nz);
+      before = __shfl(incl - v, ch);
+    }
+    if (tid == 0) {
+      s_chunk = ch;
+      s_target = target - before;
+    }
+  }
+  __syncthreads();
+  const int ch = s_chunk;
+  if (ch < 0) {
+    if (tid == 0) out_tok[(int64_t)b * (T + 1) + d.n] = d.argmax;
+    return;
+  }
+  const int64_t lo = (int64_t)ch * rchunk, hi = lo + rchunk < vocab ? lo + rchunk : vocab;
+  if (tid == 0) srow = residual_setup<DT>(R, z, vocab, T, K, c, b, dec, cand_idx, q, lo, hi);
+  __syncthreads();
+  // contiguous sub-range per thread, in index order
+  const int64_t per = (rchunk + kThreads - 1) / kThreads;
+  const int64_t t0 = lo + tid * per, t1 = t0 + per < hi ? t0 + per : hi;
+  float mine = 0.f;
+  for (int64_t v = t0; v < t1; ++v) mine += R.w(Elt<DT>::one(srow, v), v);
+  sscan[tid] = mine;
+  __syncthreads();
+  if (tid == 0) {  // sequential prefix over the 256 thread sums
+    float run = 0.f;
+    int hit = -1, last_nz = -1;
+    for (int i = 0; i < kThreads; ++i) {
+      float nx = run + sscan[i];
+      if (sscan[i] > 0.f) last_nz = i;
+      if (hit < 0 && nx > s_target) hit = i;
+      if (hit < 0) run = nx;
+    }
+    int tsel = hit >= 0 ? hit : last_nz;
+    int y = -1;
+    if (tsel >= 0) {
+      const int64_t s0 = lo + tsel * per, s1 = s0 + per < hi ? s0 + per : hi;
+      float acc = hit >= 0 ? run : 0.f;
+      int64_t lastv = -1;
+      for (int64_t v = s0; v < s1; ++v) {
+        float wv = R.w(Elt<DT>::one(srow, v), v);
+        if (wv > 0.f) lastv = v;
+        acc += wv;
+        if (hit >= 0 && acc > s_target) {
+          y = (int)v;
+          break;
+        }
+      }
+      if (y < 0) y = (int)lastv;
+    }
+    if (y < 0) y = d.argmax;
+    out_tok[(int64_t)b * (T + 1) + d.n] = y;
+  }
+}
+
+}  // namespace
+
+VerifyPlan verify_plan(int B, int T, int64_t vocab) {
+  VerifyPlan p;
+  const int64_t rows = (int64_t)B * (T + 1);
+  int64_t want = (2048 + rows - 1) / (rows > 0 ? rows : 1);
+  int64_t max_by_size = vocab / 16384;
+  int64_t s = want < max_by_size ? want : max_by_size;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  int64_t chunk = (vocab + s - 1) / s;
+  chunk = (chunk + 63) / 64 * 64;
+  s = (vocab + chunk - 1) / chunk;
+  p.splits = (int)s;
+  p.chunk = chunk;
+  int64_t rc = (vocab + 63) / 64;
+  rc = (rc + 2047) / 2048 * 2048;
+  if (rc < 4096) rc = 4096;
+  p.rchunk = rc;
+  p.rchunks = (int)((vocab + rc - 1) / rc);
+  size_t off = 0;
+  p.off_part = off;
+  off += align256((size_t)rows * s * sizeof(RowPart));
+  p.off_dec = off;
+  off += align256((size_t)B * sizeof(DecRec));
+  p.off_rsum = off;
+  off += align256((size_t)B * p.rchunks * sizeof(float));
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
+                                int B, int T, int32_t* accept_len, int32_t* out_tok, void* ws,
+                                const VerifyPlan& plan, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const int64_t rows = (int64_t)B * (T + 1);
+  uint64_t* part = (uint64_t*)((char*)ws + plan.off_part);
+  dim3 grid((unsigned)(rows * plan.splits)), block(kThreads);
+  if (dt == 0)
+    argmax_part_kernel<0><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+  else if (dt == 1)
+    argmax_part_kernel<1><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+  else
+    argmax_part_kernel<2><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+  greedy_final_kernel<<<dim3(B), dim3(64), 0, stream>>>(part, plan.splits, T, path_tok, accept_len,
+                                                         out_tok);
+  return hipGetLastError();
+}
+
+template <int DT>
+static void reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
+                          const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
+                          int T, int K, float c, const uint64_t* seed_dev, int32_t* accept_len,
+                          int32_t* out_tok, void* ws, const VerifyPlan& plan, hipStream_t stream) {
+  const int64_t rows = (int64_t)B * (T + 1);
+  RowPart* part = (RowPart*)((char*)ws + plan.off_part);
+  DecRec* dec = (DecRec*)((char*)ws + plan.off_dec);
+  float* rsum = (float*)((char*)ws + plan.off_rsum);
+  sumexp_part_kernel<DT><<<dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream>>>(
+      z, vocab, plan.splits, plan.chunk, c, part);
+  reject_decide_kernel<DT><<<dim3(B), dim3(64), 0, stream>>>(z, vocab, part, plan.splits, T, K, c,
+                                                            path_tok, path_rank, q, seed_dev,
+                                                            accept_len, out_tok, dec);
+  residual_chunk_kernel<DT><<<dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream>>>(
+      z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum);
+  residual_find_kernel<DT><<<dim3(B), dim3(kThreads), 0, stream>>>(
+      z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum, out_tok);
+}
+
+hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
+                                const int32_t* path_rank, const int32_t* cand_idx, const float* q,
+                                int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                                int32_t* accept_len, int32_t* out_tok, void* ws,
+                                const VerifyPlan& plan, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const float c = kLog2e / temperature;
+  if (dt == 0)
+    reject_launch<0>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                     out_tok, ws, plan, stream);
+  else if (dt == 1)
+    reject_launch<1>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                     out_tok, ws, plan, stream);
+  else
+    reject_launch<2>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                     out_tok, ws, plan, stream);
+  return hipGetLastError();
+}
+
+}  // namespace df2

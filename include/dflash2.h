@@ -1,0 +1,224 @@
+/*
+ * dflash2.h -- C ABI of the DFlash 2 per-cycle draft-block library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One decode cycle of DFlash 2 speculative decoding, after the drafter has
+ * produced a block of logits:
+ *
+ *   dflash2_dynconv2       two-tap dynamic depthwise convolution (inside the
+ *                          drafter, before/after every attention and MLP
+ *                          sublayer)
+ *   dflash2_topk           keep the K best candidates of every draft position
+ *   dflash2_pair_scores    score every adjacent candidate pair
+ *   dflash2_path_viterbi   pick one path through the K x K lattices
+ *   dflash2_verify_greedy  accept the longest prefix the target agrees with
+ *   dflash2_verify_reject  speculative rejection sampling with a residual draw
+ *
+ * Sources (the pages that define the operations; cited by title/section):
+ *   [KDP]  "DFlash 2: Keep Drafting Parallel" (Inco AI blog; zh-CN mirror
+ *          "DFlash 2：保持并行起草").
+ *   [WC]   "DFlash 2 讓 Qwen3.8-27B 快了兩倍" (wiselychen), section
+ *          "DFlash 2 的三個改進" and section "輸出完全一致".
+ *   [TEAI] "DFlash2 并行投机解码解读" (teaikeji), sections 二 and 五.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked "host".  All tensors are
+ *     dense, row-major, contiguous.  The caller owns every buffer; the
+ *     library never allocates device memory.  Stages that need scratch take
+ *     (ws, ws_bytes), sized by the matching *_workspace_bytes() query; the
+ *     workspace may be reused between calls that are ordered on one stream.
+ *   - Every call is asynchronous on `stream`: it validates its arguments on
+ *     the host, enqueues kernels and returns.  It never synchronises, never
+ *     allocates and never reads device memory on the host, so it may be
+ *     recorded into a HIP graph by stream capture.
+ *   - Return value: DF2_OK (0) or a positive df2_status.  Argument errors
+ *     are detected before anything is launched; nothing is written then.
+ *     A launch failure returns DF2_ERR_HIP.  dflash2_last_error() gives a
+ *     thread-local description of the last failure.
+ *   - Floating-point inputs named "logits" accept DF2_FP32, DF2_BF16 or
+ *     DF2_FP16 (dense heads only, as the selector requires; [WC] deployment
+ *     section); any other code returns DF2_ERR_DTYPE.
+ *   - Limits: 1 <= K <= 16, K <= vocab, 1 <= T <= 63, vocab < 2^31.
+ *   - Results are deterministic: the same inputs (and seed) give the same
+ *     bits on every run and every launch geometry.
+ */
+#ifndef DFLASH2_H
+#define DFLASH2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DF2_OK = 0,
+  DF2_ERR_NULL = 1,        /* a required pointer is NULL */
+  DF2_ERR_DTYPE = 2,       /* unsupported dtype code */
+  DF2_ERR_SHAPE = 3,       /* a size is out of the supported range */
+  DF2_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the query returned */
+  DF2_ERR_UNSUPPORTED = 5, /* mode / temperature combination not supported */
+  DF2_ERR_HIP = 6          /* the HIP runtime reported an error */
+} df2_status;
+
+typedef enum { DF2_FP32 = 0, DF2_BF16 = 1, DF2_FP16 = 2 } df2_dtype;
+
+typedef enum { DF2_PATH_VITERBI = 0, DF2_PATH_GREEDY = 1, DF2_PATH_SAMPLE = 2 } df2_path_mode;
+
+typedef enum { DF2_GATE_IDENTITY = 0, DF2_GATE_SIGMOID = 1 } df2_gate;
+
+#define DFLASH2_ABI_VERSION 1
+
+int dflash2_abi_version(void);
+/* Static text for a status code (host). */
+const char* dflash2_status_string(int status);
+/* Thread-local text of the last failure on this thread (host). */
+const char* dflash2_last_error(void);
+/* Query the current device once and cache its properties; optional (every
+ * entry point calls it), but call it before capturing a graph. */
+int dflash2_init(void);
+
+/* ------------------------------------------------------------------------
+ * Top-K per row.  [KDP] "The right tokens are already there" and "A
+ * lightweight path selector": DFlash 2 keeps the K (= 16) best candidates of
+ * each draft position instead of only the first.
+ *
+ *   logits   [rows, vocab] of dtype `dt` (rows = B * T)
+ *   out_idx  [rows, k] int32   token ids, best first
+ *   out_val  [rows, k] float   their logits (exact: bf16/fp16 -> fp32)
+ * Order: value descending; equal values (with -0 == +0) by lower token id.
+ * NaN entries are never selected.  ws: see dflash2_topk_workspace_bytes.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_topk_workspace_bytes(int64_t rows, int64_t vocab, int k);
+int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k, int32_t* out_idx,
+                 float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Pair scores.  [KDP] "A lightweight path selector", equation
+ *   S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >
+ * U_t(b) is the drafter's logit of candidate b (cand_val), A and B give each
+ * token a rank-r embedding, H gates the match from the position's hidden
+ * state; [WC] eq. 1.  Read as A(tok) = W_A E[tok], B(tok) = W_B E[tok],
+ * H_t = gate(W_H h_t) with W in R^{r x d}.  At t = 0 the only predecessor
+ * is the last verified token (the traversal starts there).
+ *
+ *   cand_idx [B, T, K] int32, cand_val [B, T, K] float (from dflash2_topk)
+ *   last_tok [B] int32           last verified token of each request
+ *   emb      [vocab, d]          token embedding table, dtype emb_dt (BF16)
+ *   h        [B, T, d] bf16      drafter hidden state per draft position
+ *   w_a, w_b, w_h [r, d] bf16
+ *   scores   [B, T, K, K] float  S[b,t,a,b']: a = predecessor rank (t >= 1)
+ *            or 0 = last verified token (t = 0; rows a >= 1 of t = 0 are
+ *            -inf), b' = candidate rank at t.
+ * Limits: d % 64 == 0, 16 <= r <= 256, r % 16 == 0.  Token ids outside
+ * [0, vocab) read a zero embedding.  Accumulation: fp32 (MFMA bf16 inputs).
+ * ws layout (float, each part 256-byte aligned): AB [B*T*K, 2r] (A in
+ * columns 0..r-1, B in r..2r-1), A_last [B, r], H [B*T, r].
+ * ------------------------------------------------------------------------ */
+size_t dflash2_pair_scores_workspace_bytes(int B, int T, int K, int d, int r);
+int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                        const void* emb, int emb_dt, int64_t vocab, const void* h, const void* w_a,
+                        const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
+                        int gate, float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Path through the lattice.
+ *   DF2_PATH_GREEDY  [KDP] "A lightweight path selector": from the last
+ *                    verified token follow the best successor at each step.
+ *   DF2_PATH_VITERBI [WC] "DFlash 2 的三個改進" item 2: max-sum dynamic
+ *                    programme over the lattice.
+ *   DF2_PATH_SAMPLE  [KDP] same section: the sampled path draws from the
+ *                    same scores; c_t ~ softmax_j(S_t(c_{t-1}, j) / tau),
+ *                    inverse CDF in candidate-rank order with Philox4x64-10
+ *                    key (seed, 0), counter (t, b, 0, 0), word 0.
+ * Path sums are float additions; argmax ties go to the lowest rank.
+ *
+ *   scores     [B, T, K, K] float     cand_idx [B, T, K] int32
+ *   seed_dev   [1] uint64 (device; read by SAMPLE only, may be NULL else)
+ *   path_rank  [B, T] int32  chosen candidate rank per position
+ *   path_tok   [B, T] int32  chosen token id
+ *   q          [B, T, K] float  the proposal the step drew from (one-hot for
+ *              VITERBI / GREEDY), for dflash2_verify_reject
+ *   path_score [B] float (nullable)  float sum of S along the path
+ * SAMPLE needs temperature > 0 (else DF2_ERR_UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
+                         float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                         int32_t* path_tok, float* q, float* path_score, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Two-tap dynamic depthwise convolution.  [KDP] "A lightweight local
+ * convolution", equation Conv_k(x)_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1};
+ * each tap is a learned base kernel plus a correction computed from the
+ * current hidden state, one correction per `group` (= 16) channels; the first
+ * position reads the last verified token (Fig. 4).
+ * Reading: c_t = W x_t in R^{2G}, G = d / group; channel ch uses
+ *   k0 = base[0][ch] + c_t[ch / group],  k1 = base[1][ch] + c_t[G + ch / group].
+ *
+ *   x      [B, L, d] bf16         x_prev [B, d] bf16 (nullable -> zeros)
+ *   w      [2G, d] bf16           base   [2, d] float (nullable -> zeros)
+ *   y      [B, L, d] of y_dt (DF2_BF16, round to nearest even, or DF2_FP32)
+ * Limits: group == 16, d % 64 == 0, 1 <= L.  Accumulation fp32.  y must not
+ * overlap x or x_prev.  ws: see dflash2_dynconv2_workspace_bytes.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_dynconv2_workspace_bytes(int B, int L, int d, int group);
+int dflash2_dynconv2(const void* x, const void* x_prev, const void* w, const float* base, int B,
+                     int L, int d, int group, void* y, int y_dt, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy verification.  [WC] "輸出完全一致", [TEAI] 五: under greedy
+ * decoding the output is the target's own token-by-token output.
+ * y_t = argmax_v Z[b,t,v] (lowest id on ties) for t = 0..T; n = longest
+ * prefix with path_tok[b,t] == y_t; emitted: path_tok[b,0..n-1] then y_n.
+ *
+ *   target_logits [B, T+1, vocab] of dtype dt (row T gives the bonus token)
+ *   path_tok      [B, T] int32
+ *   accept_len    [B] int32     n (0..T); acceptance length = n + 1
+ *   out_tok       [B, T+1] int32 the n+1 emitted tokens, then -1
+ * ------------------------------------------------------------------------ */
+size_t dflash2_verify_workspace_bytes(int B, int T, int64_t vocab);
+int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                          int B, int T, int32_t* accept_len, int32_t* out_tok, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Speculative rejection sampling.  [KDP] "A lightweight path selector":
+ * rejection sampling restores the exact target distribution; [WC]
+ * "輸出完全一致".  With p_t = softmax(Z_t / tau):
+ *   accept draft t iff u1 < p_t(x_t) / q_t(x_t)        (word 1 at (t, b))
+ *   at the first rejection draw from max(0, p_t - q~_t) (q~ = q on the
+ *   candidates of position t, 0 elsewhere) by index-order inverse CDF with
+ *   u2 (word 2 at (t, b)); if every draft is accepted, draw the bonus token
+ *   from p_T with word 2 at (T, b).
+ * Uniforms: Philox4x64-10, key (seed, 0), counter (t, b, 0, 0); a word w
+ * maps to (2 * (w >> 41) + 1) * 2^-24.  q_t(x_t) <= 0 accepts.
+ *
+ *   target_logits [B, T+1, vocab]; path_tok, path_rank [B, T] int32;
+ *   cand_idx [B, T, K] int32; q [B, T, K] float (from dflash2_path_viterbi)
+ *   seed_dev [1] uint64 (device)
+ *   accept_len [B], out_tok [B, T+1] as in dflash2_verify_greedy
+ * Needs temperature > 0 (else DF2_ERR_UNSUPPORTED).  Probabilities fp32.
+ * ------------------------------------------------------------------------ */
+int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                          const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
+                          int T, int K, float temperature, const uint64_t* seed_dev,
+                          int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Philox4x64-10 words as the sampling steps above draw them (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11): for each i,
+ * out[4i..4i+3] = Philox4x64-10(key = (seed, 0), counter = (t[i], b[i], 0, 0)).
+ *   seed_dev [1] uint64; b, t [n] int32; out [4n] uint64 (all device).
+ * ------------------------------------------------------------------------ */
+int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
+                       uint64_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH2_H */

@@ -51,10 +51,10 @@ def _declare(L):
     L.oracle_project.argtypes = [P, C.c_int, I64, C.c_int, P, C.c_int, C.c_int, P]
     L.oracle_pair_scores.argtypes = [P, P, P, P, C.c_int, I64, P, P, P, P, C.c_int, C.c_int,
                                      C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P, P]
-    L.oracle_path.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, F64, U64, P, P, P, P, P]
+    L.oracle_path.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, F64, U64, P, P, P, P, P, P]
     L.oracle_verify_greedy.argtypes = [P, C.c_int, I64, P, C.c_int, C.c_int, P, P, P]
     L.oracle_verify_reject.argtypes = [P, C.c_int, I64, P, P, P, P, C.c_int, C.c_int, C.c_int,
-                                       F64, U64, P, P, P, P, P]
+                                       F64, U64, P, P, P, P, P, P]
     L.oracle_dynconv2.argtypes = [P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P]
     for f in ("oracle_topk", "oracle_project", "oracle_pair_scores", "oracle_path",
               "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2"):
@@ -168,8 +168,16 @@ def pair_scores(cand_idx, cand_val, last_tok, emb, h, w_a, w_b, w_h, gate: int =
     return S
 
 
-def path(scores, cand_idx, mode: int, temperature: float = 0.0, seed: int = 0):
-    """-> dict(rank, tok, q, score, margin)."""
+def _bids(b_ids, B):
+    if b_ids is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(b_ids, dtype=np.int32).reshape(B))
+    return a
+
+
+def path(scores, cand_idx, mode: int, temperature: float = 0.0, seed: int = 0, b_ids=None):
+    """-> dict(rank, tok, q, score, margin).  b_ids: request index per row
+    for the Philox counter (default: the row number)."""
     S = np.ascontiguousarray(np.asarray(host(scores)[0], dtype=np.float32))
     ci = np.ascontiguousarray(np.asarray(host(cand_idx)[0], dtype=np.int32))
     B, T, K, _ = S.shape
@@ -178,9 +186,10 @@ def path(scores, cand_idx, mode: int, temperature: float = 0.0, seed: int = 0):
     q = np.zeros((B, T, K), np.float32)
     score = np.zeros((B,), np.float32)
     margin = np.zeros((B, T), np.float64)
+    bi = _bids(b_ids, B)
     _check(lib().oracle_path(_ptr(S), _ptr(ci), B, T, K, mode, float(temperature),
-                             int(seed) & (2**64 - 1), _ptr(rank), _ptr(tok), _ptr(q), _ptr(score),
-                             _ptr(margin)), "oracle_path")
+                             int(seed) & (2**64 - 1), _ptr(bi), _ptr(rank), _ptr(tok), _ptr(q),
+                             _ptr(score), _ptr(margin)), "oracle_path")
     return dict(rank=rank, tok=tok, q=q, score=score, margin=margin)
 
 
@@ -200,7 +209,8 @@ def verify_greedy(target, path_tok):
     return dict(accept_len=acc, out_tok=out, argmax=am)
 
 
-def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, seed: int):
+def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, seed: int,
+                  b_ids=None):
     za, zdt = host(target)
     if zdt is None:
         za, zdt = host(za, np.float32)
@@ -217,8 +227,10 @@ def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, 
     ma = np.zeros((B, T), np.float64)
     ms = np.zeros((B,), np.float64)
     fb = np.zeros((1,), np.int32)
+    bi = _bids(b_ids, B)
     _check(lib().oracle_verify_reject(_ptr(za), zdt, V, _ptr(pt), _ptr(pr), _ptr(ci), _ptr(qa), B, T,
-                                      K, float(temperature), int(seed) & (2**64 - 1), _ptr(acc),
+                                      K, float(temperature), int(seed) & (2**64 - 1), _ptr(bi),
+                                      _ptr(acc),
                                       _ptr(out), _ptr(ma), _ptr(ms), _ptr(fb)),
            "oracle_verify_reject")
     return dict(accept_len=acc, out_tok=out, margin_accept=ma, margin_sample=ms,

@@ -310,7 +310,9 @@ int oracle_pair_scores(const int32_t* cand_idx, const float* cand_val, const int
 /* Scores and path sums are float with float additions; argmax ties go  */
 /* to the lowest candidate rank.  q[b,t,:] is the proposal actually used */
 /* (one-hot for the deterministic modes).  margin[b,t] is the relative  */
-/* margin of the decision that fixed c_t (see each mode).               */
+/* margin of the decision that fixed c_t (see each mode).  b_ids        */
+/* (nullable) gives the request index used in the Philox counter of row */
+/* b (default b), so that a subset of a batch can be recomputed.        */
 /* Pinned by: brute force over all K^T paths; Viterbi >= greedy; the    */
 /* rank-independent special case; Monte Carlo for SAMPLE.               */
 /* ------------------------------------------------------------------ */
@@ -357,8 +359,8 @@ static int inverse_cdf(const double* w, int n, double u, double total, double* m
 }
 
 int oracle_path(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
-                double temperature, uint64_t seed, int32_t* path_rank, int32_t* path_tok, float* q,
-                float* path_score, double* margin) {
+                double temperature, uint64_t seed, const int32_t* b_ids, int32_t* path_rank,
+                int32_t* path_tok, float* q, float* path_score, double* margin) {
   if (mode == OR_PATH_SAMPLE && !(temperature > 0)) return 5;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
@@ -430,7 +432,7 @@ int oracle_path(const float* scores, const int32_t* cand_idx, int B, int T, int 
             z += e[j];
           }
           for (int j = 0; j < K; ++j) e[j] /= z;
-          double u0 = cycle_uniform(seed, b, t, 0), mm = 0.0;
+          double u0 = cycle_uniform(seed, b_ids ? b_ids[b] : b, t, 0), mm = 0.0;
           pick = inverse_cdf(e, K, u0, 1.0, &mm);
           if (pick < 0) { /* rounding left the running sum below u0 */
             pick = K - 1;
@@ -508,6 +510,7 @@ int oracle_verify_greedy(const void* target, int dt, int64_t vocab, const int32_
 /* All probabilities in double.  A proposal q_t(x_t) <= 0 accepts.  If   */
 /* the residual has no mass (rounding only), the lowest argmax of p_t is */
 /* emitted and *fallbacks is incremented.                                */
+/* b_ids (nullable): request index of row b in the Philox counter.      */
 /* margin_accept[b,t]: |u1 - p/q| for each evaluated draft (NaN if not   */
 /* evaluated); margin_sample[b]: relative distance of u2 * mass from the */
 /* neighbouring CDF steps.                                               */
@@ -532,7 +535,8 @@ static void softmax_row(const void* target, int dt, int64_t base, int64_t vocab,
 
 int oracle_verify_reject(const void* target, int dt, int64_t vocab, const int32_t* path_tok,
                          const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
-                         int T, int K, double temperature, uint64_t seed, int32_t* accept_len,
+                         int T, int K, double temperature, uint64_t seed, const int32_t* b_ids,
+                         int32_t* accept_len,
                          int32_t* out_tok, double* margin_accept, double* margin_sample,
                          int32_t* fallbacks) {
   if (!(temperature > 0)) return 5;
@@ -541,6 +545,7 @@ int oracle_verify_reject(const void* target, int dt, int64_t vocab, const int32_
   for (int b = 0; b < B; ++b) {
     double* p = (double*)malloc(sizeof(double) * (size_t)vocab);
     double* w = (double*)malloc(sizeof(double) * (size_t)vocab);
+    const int bc = b_ids ? b_ids[b] : b; /* request index of the counter */
     int n = T, y = -1;
     if (margin_accept)
       for (int t = 0; t < T; ++t) margin_accept[(int64_t)b * T + t] = NAN;
@@ -548,7 +553,7 @@ int oracle_verify_reject(const void* target, int dt, int64_t vocab, const int32_
       softmax_row(target, dt, ((int64_t)b * (T + 1) + t) * vocab, vocab, temperature, p);
       int32_t x = path_tok[(int64_t)b * T + t];
       double qx = q[((int64_t)b * T + t) * K + path_rank[(int64_t)b * T + t]];
-      double u1 = cycle_uniform(seed, b, t, 1);
+      double u1 = cycle_uniform(seed, bc, t, 1);
       double ratio = qx > 0 ? p[x] / qx : INFINITY;
       if (margin_accept) margin_accept[(int64_t)b * T + t] = fabs(u1 - ratio);
       if (u1 < ratio) continue;
@@ -569,7 +574,7 @@ int oracle_verify_reject(const void* target, int dt, int64_t vocab, const int32_
     }
     double mass = 0.0;
     for (int64_t v = 0; v < vocab; ++v) mass += w[v];
-    double u2 = cycle_uniform(seed, b, n, 2), ms = 0.0;
+    double u2 = cycle_uniform(seed, bc, n, 2), ms = 0.0;
     if (mass > 0) {
       y = inverse_cdf(w, (int)vocab, u2, mass, &ms);
       if (y < 0) { /* rounding left the running sum below u2 * mass */

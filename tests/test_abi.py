@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads without a GPU, exports every
+function include/dflash2.h declares, and rejects bad arguments with the
+documented status before anything is launched.  Every call here has at
+least one invalid argument, so nothing reaches the GPU runtime."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import draft_selection_bf16_amd as df2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = C.c_void_p(0x100000)      # aligned non-null stand-in; never dereferenced here
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dflash2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash2_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = df2.lib()
+    declared = _declared()
+    assert len(declared) >= 15
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(df2.EXPORTS)
+
+
+def test_version_and_strings():
+    assert df2.dflash2_abi_version() == 1
+    assert df2.dflash2_status_string(0) == "ok"
+    assert df2.dflash2_status_string(4) == "workspace too small"
+
+
+def _last():
+    return df2.lib().dflash2_last_error().decode()
+
+
+def test_topk_validation():
+    L = df2.lib()
+    assert L.dflash2_topk(FAKE, 7, 4, 1000, 16, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_DTYPE
+    assert "dense" in _last()
+    assert L.dflash2_topk(FAKE, 1, 4, 1000, 17, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_topk(FAKE, 1, 4, 10, 16, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_topk(FAKE, 1, 4, 1000, 0, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_topk(None, 1, 4, 1000, 16, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_NULL
+    need = df2.dflash2_topk_workspace_bytes(480, 151936, 16)
+    assert need > 0
+    assert L.dflash2_topk(FAKE, 1, 480, 151936, 16, FAKE, FAKE, FAKE, need - 1, None) == \
+        df2.DF2_ERR_WORKSPACE
+    # zero rows is a no-op and succeeds without touching the runtime
+    assert L.dflash2_topk(None, 1, 0, 1000, 16, None, None, None, 0, None) == df2.DF2_OK
+
+
+def test_pair_scores_validation():
+    L = df2.lib()
+    args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, FAKE, kw.get("edt", 1), 151936, FAKE, FAKE,
+                         FAKE, FAKE, kw.get("B", 2), kw.get("T", 7), kw.get("K", 16),
+                         kw.get("d", 5120), kw.get("r", 256), kw.get("gate", 0), FAKE, FAKE,
+                         kw.get("ws", 1 << 30), None]
+    assert L.dflash2_pair_scores(*args(edt=0)) == df2.DF2_ERR_DTYPE
+    assert L.dflash2_pair_scores(*args(d=100)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(r=8)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(r=264)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(K=17)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(T=0)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(T=64)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores(*args(gate=5)) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_pair_scores(*args(ci=None)) == df2.DF2_ERR_NULL
+    need = df2.dflash2_pair_scores_workspace_bytes(2, 7, 16, 5120, 256)
+    assert L.dflash2_pair_scores(*args(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+
+
+def test_path_validation():
+    L = df2.lib()
+    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+        df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, float("inf"), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  None) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, 1.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
+        df2.DF2_ERR_NULL
+    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 0, 0, 1.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
+        df2.DF2_ERR_SHAPE
+    assert L.dflash2_path_viterbi(None, FAKE, 2, 7, 16, 0, 0.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
+        df2.DF2_ERR_NULL
+
+
+def test_conv_validation():
+    L = df2.lib()
+    need = df2.dflash2_dynconv2_workspace_bytes(32, 16, 5120)
+    assert need > 0
+    assert L.dflash2_dynconv2(FAKE, FAKE, FAKE, None, 32, 16, 5120, 16, FAKE, 2, FAKE, need, None) == \
+        df2.DF2_ERR_DTYPE
+    assert L.dflash2_dynconv2(FAKE, FAKE, FAKE, None, 32, 16, 5120, 8, FAKE, 1, FAKE, need, None) == \
+        df2.DF2_ERR_SHAPE
+    assert L.dflash2_dynconv2(FAKE, FAKE, FAKE, None, 32, 16, 5000, 16, FAKE, 1, FAKE, need, None) == \
+        df2.DF2_ERR_SHAPE
+    assert L.dflash2_dynconv2(FAKE, FAKE, FAKE, None, 32, 0, 5120, 16, FAKE, 1, FAKE, need, None) == \
+        df2.DF2_ERR_SHAPE
+    assert L.dflash2_dynconv2(None, FAKE, FAKE, None, 32, 16, 5120, 16, FAKE, 1, FAKE, need, None) == \
+        df2.DF2_ERR_NULL
+    assert L.dflash2_dynconv2(C.c_void_p(0x100002), FAKE, FAKE, None, 32, 16, 5120, 16, FAKE, 1, FAKE,
+                              need, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_dynconv2(FAKE, FAKE, FAKE, None, 32, 16, 5120, 16, FAKE, 1, FAKE, need - 1,
+                              None) == df2.DF2_ERR_WORKSPACE
+
+
+def test_verify_validation():
+    L = df2.lib()
+    need = df2.dflash2_verify_workspace_bytes(32, 15, 151936)
+    assert need > 0
+    assert L.dflash2_verify_greedy(FAKE, 5, 151936, FAKE, 32, 15, FAKE, FAKE, FAKE, need, None) == \
+        df2.DF2_ERR_DTYPE
+    assert L.dflash2_verify_greedy(FAKE, 1, 151936, FAKE, 32, 64, FAKE, FAKE, FAKE, need, None) == \
+        df2.DF2_ERR_SHAPE
+    assert L.dflash2_verify_greedy(FAKE, 1, 151936, None, 32, 15, FAKE, FAKE, FAKE, need, None) == \
+        df2.DF2_ERR_NULL
+    assert L.dflash2_verify_greedy(FAKE, 1, 151936, FAKE, 32, 15, FAKE, FAKE, FAKE, need - 1, None) == \
+        df2.DF2_ERR_WORKSPACE
+    args = [FAKE, 1, 151936, FAKE, FAKE, FAKE, FAKE, 32, 15, 16]
+    tail = [FAKE, FAKE, FAKE, FAKE, need, None]
+    assert L.dflash2_verify_reject(*args, 0.0, *tail) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_verify_reject(*args, -1.0, *tail) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_verify_reject(*args, 1.0, None, *tail[1:]) == df2.DF2_ERR_NULL
+    assert L.dflash2_verify_reject(*args[:-1], 0, 1.0, *tail) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_verify_reject(*args, 1.0, *tail[:-2], need - 1, None) == df2.DF2_ERR_WORKSPACE
+
+
+def test_philox_validation():
+    L = df2.lib()
+    assert L.dflash2_philox4x64(FAKE, FAKE, FAKE, -1, FAKE, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_philox4x64(None, FAKE, FAKE, 4, FAKE, None) == df2.DF2_ERR_NULL
+    assert L.dflash2_philox4x64(None, None, None, 0, None, None) == df2.DF2_OK
+
+
+def test_binding_raises_on_error():
+    import torch
+    x = torch.zeros(4, 10, dtype=torch.float64)     # unsupported dtype
+    with pytest.raises(df2.DFlash2Error) as e:
+        df2.dflash2_topk(x, 4, x, x, None, stream=type("S", (), {"cuda_stream": 0})())
+    assert e.value.status == df2.DF2_ERR_DTYPE

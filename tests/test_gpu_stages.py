@@ -1,0 +1,400 @@
+"""GPU parity, stage by stage: each C-ABI entry point against the CPU oracle
+on the same seeded inputs.  Index, path and decision outputs must be
+bit-exact (sampling decisions at an oracle margin below 1e-6 are reported,
+not failed); scores and conv outputs within 1e-3 relative (rms floor);
+bf16 conv outputs within one bf16 step."""
+import numpy as np
+import pytest
+import torch
+
+import draft_selection_bf16_amd as df2
+import oracle
+import synth
+from gpu_util import DEV, NEAR_TIE, bf16_ulp_close, close, dev, report, ws
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------- Philox
+def test_philox_words_match_oracle():
+    n = 300
+    rng = np.random.default_rng(0)
+    b = rng.integers(0, 1 << 20, n).astype(np.int32)
+    t = rng.integers(0, 64, n).astype(np.int32)
+    for seed in (0, 2, 4_000_123, 2**63 - 5):
+        sd = torch.tensor([seed], dtype=torch.int64, device=DEV)
+        out = torch.empty(4 * n, dtype=torch.int64, device=DEV)
+        df2.dflash2_philox4x64(sd, dev(torch.from_numpy(b)), dev(torch.from_numpy(t)), out)
+        _sync()
+        got = out.cpu().numpy().view(np.uint64).reshape(n, 4)
+        for i in range(0, n, 7):
+            ref = oracle.philox(seed, (int(t[i]), int(b[i]), 0, 0))
+            assert np.array_equal(got[i], ref), (seed, i)
+
+
+# ----------------------------------------------------------------- top-K
+def _topk_gpu(x, k):
+    V = x.shape[-1]
+    rows = x.numel() // V
+    idx = torch.empty(x.shape[:-1] + (k,), dtype=torch.int32, device=DEV)
+    val = torch.empty(x.shape[:-1] + (k,), dtype=torch.float32, device=DEV)
+    w = ws(df2.dflash2_topk_workspace_bytes(rows, V, k))
+    df2.dflash2_topk(x, k, idx, val, w)
+    _sync()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def _check_topk(x_cpu, k):
+    gi, gv = _topk_gpu(dev(x_cpu), k)
+    oi, ov = oracle.topk(x_cpu, k)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv, ov)
+
+
+@pytest.mark.parametrize("k", [1, 4, 16])
+def test_topk_tiny_fp32(k):
+    w = synth.WORKLOADS["tiny_b1_blk4_v1000"]
+    z, _, _ = synth.drafter_logits(w)
+    _check_topk(z, k)
+
+
+@pytest.mark.parametrize("V", [1001, 4099, 16384, 151936, 151939])
+def test_topk_bf16_ragged_vocab(V):
+    """Row lengths that are not multiples of 8 start rows off 16-byte
+    alignment: the head/tail path runs."""
+    g = torch.Generator().manual_seed(V)
+    z = (3 * torch.randn(5, V, generator=g)).to(torch.bfloat16)
+    _check_topk(z, 16)
+
+
+def test_topk_ties_and_signed_zero():
+    g = torch.Generator().manual_seed(1)
+    z = torch.round(torch.randn(9, 50000, generator=g) * 2) / 2     # heavy ties
+    z[0] = 0.0
+    z[0, ::2] = -0.0
+    z[1] = 1.0
+    z[2, :100] = 7.0
+    _check_topk(z.to(torch.bfloat16), 16)
+    _check_topk(z, 16)
+
+
+def test_topk_fp16():
+    g = torch.Generator().manual_seed(2)
+    z = (3 * torch.randn(4, 32771, generator=g)).to(torch.float16)
+    _check_topk(z, 16)
+
+
+def test_topk_adversarial_ascending_rows():
+    """Ascending rows make every entry a new maximum: the threshold filter
+    hits its slow path on every load."""
+    V = 70000
+    z = torch.arange(V, dtype=torch.float32).repeat(3, 1) * 1e-3
+    z[1] = z[1].flip(0)
+    _check_topk(z.to(torch.bfloat16), 16)
+
+
+def test_topk_launch_shape_of_the_b32_blk16_workload():
+    """480 rows of 151,936 bf16 logits, the launch configuration the
+    benchmark times; all rows compared."""
+    w = synth.WORKLOADS["b32_blk16_v151936_conv"]
+    z, tok, rank = synth.drafter_logits(w, device=DEV)
+    gi, gv = _topk_gpu(z, 16)
+    oi, ov = oracle.topk(z.cpu(), 16)
+    assert np.array_equal(gi, oi) and np.array_equal(gv, ov)
+    tok = tok.cpu().numpy()
+    r16 = (gi == tok[..., None]).any(-1).mean()
+    report("topk b32_blk16", recall16=round(float(r16), 4))
+
+
+def test_topk_gumbel_v262144_rows():
+    w = synth.scaled(synth.WORKLOADS["b64_blk16_v262144_stress"], B=2)
+    z, _, _ = synth.drafter_logits(w, device=DEV)
+    gi, gv = _topk_gpu(z, 16)
+    oi, ov = oracle.topk(z.cpu(), 16)
+    assert np.array_equal(gi, oi) and np.array_equal(gv, ov)
+
+
+# ----------------------------------------------------------------- pair scores
+def _pair_gpu(cand_idx, cand_val, last, E, h, wa, wb, wh, gate=0):
+    B, T, K = cand_idx.shape
+    d, r = E.shape[1], wa.shape[0]
+    S = torch.empty((B, T, K, K), dtype=torch.float32, device=DEV)
+    nb = df2.dflash2_pair_scores_workspace_bytes(B, T, K, d, r)
+    w = ws(nb)
+    df2.dflash2_pair_scores(dev(cand_idx), dev(cand_val), dev(last), dev(E), dev(h), dev(wa), dev(wb),
+                            dev(wh), S, w, gate=gate)
+    _sync()
+    return S.cpu().numpy(), w
+
+
+def _ws_views(w, B, T, K, r):
+    def a256(n):
+        return (n + 255) // 256 * 256
+    f = w.view(torch.float32)
+    n_ab = B * T * K * 2 * r
+    off_al = a256(n_ab * 4) // 4
+    off_h = off_al + a256(B * r * 4) // 4
+    ab = f[:n_ab].view(B, T, K, 2 * r).cpu().numpy()
+    al = f[off_al:off_al + B * r].view(B, r).cpu().numpy()
+    hg = f[off_h:off_h + B * T * r].view(B, T, r).cpu().numpy()
+    return ab, al, hg
+
+
+@pytest.mark.parametrize("gate", [0, 1])
+def test_pair_scores_tiny(gate):
+    w = synth.WORKLOADS["tiny_b1_blk4_v1000"]
+    z, _, _ = synth.drafter_logits(w)
+    idx, val = oracle.topk(z, w.K)
+    E = synth.embeddings(w)
+    wa, wb, wh = synth.selector_weights(w)
+    h, last = synth.context_hidden(w), synth.last_tokens(w)
+    Sg, _ = _pair_gpu(torch.from_numpy(idx), torch.from_numpy(val), last, E, h, wa, wb, wh, gate)
+    So = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, gate=gate)
+    close(Sg, So)
+
+
+def test_pair_scores_mid_with_intermediates():
+    """B=3, T=7, K=16, V=4096, d=512, r=256: several GEMM tiles, a ragged
+    M tail (3*7*16 = 336 rows), gathered rows."""
+    w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=3, V=4096, d=512)
+    z, _, _ = synth.drafter_logits(w)
+    idx, val = oracle.topk(z, 16)
+    E = synth.embeddings(w)
+    wa, wb, wh = synth.selector_weights(w)
+    h, last = synth.context_hidden(w), synth.last_tokens(w)
+    Sg, wsp = _pair_gpu(torch.from_numpy(idx), torch.from_numpy(val), last, E, h, wa, wb, wh)
+    So, inter = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, intermediates=True)
+    worst = close(Sg, So)
+    ab, al, hg = _ws_views(wsp, 3, 7, 16, 256)
+    close(ab[..., :256], inter["a_cand"])
+    close(ab[..., 256:], inter["b_cand"])
+    close(al, inter["a_last"])
+    close(hg, inter["h"])
+    report("pair_scores mid", worst_err_over_bound=round(worst, 4))
+
+
+def test_pair_scores_out_of_range_tokens_read_zero_rows():
+    w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=1, V=512, d=128, r=32)
+    E = synth.embeddings(w)
+    wa, wb, wh = synth.selector_weights(w)
+    h = synth.context_hidden(w)
+    cand = torch.randint(0, 512, (1, 7, 4), dtype=torch.int32)
+    cand[0, 3, 2] = 10_000_000      # out of range -> zero embedding -> bigram 0
+    val = torch.randn(1, 7, 4)
+    last = torch.tensor([-5], dtype=torch.int32)
+    Sg, _ = _pair_gpu(cand, val, last, E, h, wa, wb, wh)
+    assert np.all(Sg[0, 3, :, 2] == val[0, 3, 2].item())
+    assert np.all(Sg[0, 0, 0, :] == val[0, 0].numpy())   # last token -> zero A
+
+
+# ----------------------------------------------------------------- path
+def _path_gpu(S, cand, mode, tau=0.0, seed=0):
+    B, T, K, _ = S.shape
+    pr = torch.empty((B, T), dtype=torch.int32, device=DEV)
+    pt = torch.empty((B, T), dtype=torch.int32, device=DEV)
+    q = torch.empty((B, T, K), dtype=torch.float32, device=DEV)
+    ps = torch.empty((B,), dtype=torch.float32, device=DEV)
+    sd = torch.tensor([seed], dtype=torch.int64, device=DEV)
+    df2.dflash2_path_viterbi(dev(S), dev(cand), mode, pr, pt, q, ps, temperature=tau, seed_dev=sd)
+    _sync()
+    return dict(rank=pr.cpu().numpy(), tok=pt.cpu().numpy(), q=q.cpu().numpy(), score=ps.cpu().numpy())
+
+
+@pytest.mark.parametrize("B,T,K,ties", [(1, 3, 4, False), (32, 15, 16, False), (64, 15, 16, True),
+                                        (8, 7, 16, True), (5, 1, 16, False), (3, 63, 16, False),
+                                        (7, 9, 5, True)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_path_deterministic_modes_bit_exact(B, T, K, ties, mode):
+    S = synth.pair_score_lattice(B, T, K, seed=B * 100 + T, ties=ties)
+    cand = torch.randint(0, 151936, (B, T, K), dtype=torch.int32,
+                         generator=torch.Generator().manual_seed(T))
+    g = _path_gpu(S, cand, mode)
+    o = oracle.path(S.numpy(), cand.numpy(), mode)
+    for key in ("rank", "tok", "q", "score"):
+        assert np.array_equal(g[key], o[key]), key
+
+
+@pytest.mark.parametrize("B,T,K,tau", [(64, 15, 16, 1.0), (8, 7, 16, 0.5), (200, 3, 4, 2.0)])
+def test_path_sampled(B, T, K, tau):
+    S = synth.pair_score_lattice(B, T, K, seed=7 + T, spread=1.0)
+    cand = torch.randint(0, 151936, (B, T, K), dtype=torch.int32,
+                         generator=torch.Generator().manual_seed(5))
+    seed = 2
+    g = _path_gpu(S, cand, 2, tau, seed)
+    o = oracle.path(S.numpy(), cand.numpy(), 2, temperature=tau, seed=seed)
+    near, bad = 0, 0
+    for b in range(B):
+        if np.array_equal(g["rank"][b], o["rank"][b]):
+            close(g["q"][b], o["q"][b], rel=1e-5)
+            assert g["score"][b] == o["score"][b]
+            continue
+        t = int(np.flatnonzero(g["rank"][b] != o["rank"][b])[0])
+        if o["margin"][b, t] < NEAR_TIE:
+            near += 1
+        else:
+            bad += 1
+    report("path sample", B=B, T=T, near_tie_mismatches=near)
+    assert bad == 0
+    near_ties = int((o["margin"] < NEAR_TIE).sum())
+    report("path sample", decisions=B * T, near_ties=near_ties)
+
+
+# ----------------------------------------------------------------- verify
+def _verify_greedy_gpu(Z, path_tok):
+    B, T1, V = Z.shape
+    acc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, T1), dtype=torch.int32, device=DEV)
+    w = ws(df2.dflash2_verify_workspace_bytes(B, T1 - 1, V))
+    df2.dflash2_verify_greedy(dev(Z), dev(path_tok), acc, out, w)
+    _sync()
+    return acc.cpu().numpy(), out.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,B,T,V,dtype", [("tiny", 1, 3, 1000, torch.float32),
+                                               ("ragged", 5, 7, 10007, torch.bfloat16),
+                                               ("b32_blk16", 32, 15, 151936, torch.bfloat16),
+                                               ("fp16", 3, 5, 5003, torch.float16),
+                                               ("t63", 2, 63, 3001, torch.bfloat16)])
+def test_verify_greedy_exact(name, B, T, V, dtype):
+    w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=T + 1, V=V)
+    d_dev = DEV if V > 100000 else "cpu"
+    z, tok, _ = synth.drafter_logits(w, device=d_dev)
+    Z = synth.target_logits(w, z, tok, device=d_dev).to(dtype)
+    # drafts: mostly the true token, so prefixes of every length occur
+    path = tok.to(torch.int32).clone()
+    g = torch.Generator(device=d_dev).manual_seed(B)
+    flip = torch.rand(path.shape, generator=g, device=d_dev) < 0.15
+    path = torch.where(flip, (path + 1) % V, path).to(torch.int32)
+    ga, go = _verify_greedy_gpu(Z, path)
+    o = oracle.verify_greedy(Z.cpu(), path.cpu())
+    assert np.array_equal(ga, o["accept_len"])
+    assert np.array_equal(go, o["out_tok"])
+    report(f"verify greedy {name}", mean_accept=float(ga.mean()))
+
+
+def test_verify_greedy_ties_take_lowest_index():
+    Z = torch.zeros((2, 3, 40000), dtype=torch.bfloat16)
+    Z[:, :, 777] = 5.0
+    Z[:, :, 30001] = 5.0
+    Z[1, 1, 5] = 5.0
+    path = torch.tensor([[777, 777], [777, 5]], dtype=torch.int32)
+    ga, go = _verify_greedy_gpu(Z, path)
+    o = oracle.verify_greedy(Z, path)
+    assert np.array_equal(ga, o["accept_len"]) and np.array_equal(go, o["out_tok"])
+    assert list(go[0]) == [777, 777, 777] and list(go[1]) == [777, 5, 777]
+
+
+def _verify_reject_gpu(Z, path_tok, path_rank, cand, q, tau, seed):
+    B, T1, V = Z.shape
+    acc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, T1), dtype=torch.int32, device=DEV)
+    w = ws(df2.dflash2_verify_workspace_bytes(B, T1 - 1, V))
+    sd = torch.tensor([seed], dtype=torch.int64, device=DEV)
+    df2.dflash2_verify_reject(dev(Z), dev(path_tok), dev(path_rank), dev(cand), dev(q), tau, sd, acc,
+                              out, w)
+    _sync()
+    return acc.cpu().numpy(), out.cpu().numpy()
+
+
+def _reject_case(B, T, V, tau, seed, sampled=True, dtype=torch.bfloat16):
+    w = synth.scaled(synth.WORKLOADS["b8_blk8_v151936_sampled"], B=B, block=T + 1, V=V, tau=tau)
+    d_dev = DEV if V > 100000 else "cpu"
+    z, tok, _ = synth.drafter_logits(w, device=d_dev)
+    Z = synth.target_logits(w, z, tok, device=d_dev).to(dtype)
+    idx, val = oracle.topk(z.cpu(), 16)
+    S = synth.pair_score_lattice(B, T, 16, seed=seed, spread=1.0).numpy()
+    S = S + val[:, :, None, :]
+    mode = oracle.PATH_SAMPLE if sampled else oracle.PATH_VITERBI
+    pth = oracle.path(S, idx, mode, temperature=tau, seed=seed)
+    return Z, pth, idx
+
+
+@pytest.mark.parametrize("B,T,V,tau,sampled", [(8, 7, 151936, 1.0, True), (16, 15, 20000, 0.7, True),
+                                               (16, 15, 20000, 1.0, False), (4, 3, 1000, 1.5, True)])
+def test_verify_reject_matches_oracle(B, T, V, tau, sampled):
+    seed = 2
+    Z, pth, idx = _reject_case(B, T, V, tau, seed, sampled)
+    ga, go = _verify_reject_gpu(Z, torch.from_numpy(pth["tok"]), torch.from_numpy(pth["rank"]),
+                                torch.from_numpy(idx), torch.from_numpy(pth["q"]), tau, seed)
+    o = oracle.verify_reject(Z.cpu(), pth["tok"], pth["rank"], idx, pth["q"], tau, seed)
+    near, bad = 0, 0
+    for b in range(B):
+        if ga[b] == o["accept_len"][b] and np.array_equal(go[b], o["out_tok"][b]):
+            continue
+        ma = o["margin_accept"][b]
+        if np.nanmin(ma[: o["accept_len"][b] + 1]) < NEAR_TIE or o["margin_sample"][b] < NEAR_TIE:
+            near += 1
+        else:
+            bad += 1
+    report("verify reject", B=B, T=T, V=V, near_tie_mismatches=near,
+           mean_accept=float(np.mean(o["accept_len"])), fallbacks=o["fallbacks"])
+    assert bad == 0
+
+
+def test_verify_reject_distribution_on_gpu():
+    """Many copies of one request: the first emitted token must follow p_0
+    (the drafts are drawn from q, so acceptance + residual restore p)."""
+    V, K, T, tau, N = 64, 4, 2, 1.0, 100_000
+    rng = np.random.default_rng(3)
+    Zrow = (rng.normal(size=(T + 1, V)) * 1.5).astype(np.float32)
+    p0 = np.exp(Zrow[0] - Zrow[0].max())
+    p0 /= p0.sum()
+    cands = np.array([[3, 9, 27, 40], [1, 2, 5, 63]], np.int32)
+    qrow = np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.25, 0.25]], np.float32)
+    rank = np.stack([rng.choice(K, size=N, p=qrow[t] / qrow[t].sum()) for t in range(T)], 1)
+    rank = rank.astype(np.int32)
+    tok = np.take_along_axis(np.broadcast_to(cands, (N, T, K)), rank[..., None], -1)[..., 0]
+    Z = torch.from_numpy(np.broadcast_to(Zrow, (N, T + 1, V)).copy())
+    ga, go = _verify_reject_gpu(Z, torch.from_numpy(tok.astype(np.int32)), torch.from_numpy(rank),
+                                torch.from_numpy(np.broadcast_to(cands, (N, T, K)).copy()),
+                                torch.from_numpy(np.broadcast_to(qrow, (N, T, K)).copy()), tau, 11)
+    counts = np.bincount(go[:, 0], minlength=V).astype(float)
+    e = N * p0
+    keep = e > 5
+    chi2 = float((((counts - e) ** 2) / e)[keep].sum())
+    report("verify reject MC", chi2=round(chi2, 1), dof=int(keep.sum()) - 1)
+    assert chi2 < int(keep.sum()) + 8 * np.sqrt(2 * keep.sum())
+
+
+# ----------------------------------------------------------------- dynconv2
+def _conv_gpu(x, xp, wt, base, y_dtype):
+    B, L, d = x.shape
+    y = torch.empty((B, L, d), dtype=y_dtype, device=DEV)
+    w = ws(df2.dflash2_dynconv2_workspace_bytes(B, L, d))
+    df2.dflash2_dynconv2(dev(x), None if xp is None else dev(xp), dev(wt),
+                         None if base is None else dev(base), y, w)
+    _sync()
+    return y
+
+
+@pytest.mark.parametrize("B,L,d,base,prev", [(1, 4, 64, True, True), (2, 16, 256, False, True),
+                                             (3, 5, 320, True, False), (32, 16, 5120, False, True)])
+def test_dynconv2_matches_oracle(B, L, d, base, prev):
+    w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=L, d=d, conv_base=base)
+    x, xp, wt, bs = synth.conv_site(w, 0)
+    if not prev:
+        xp = None
+    yo = oracle.dynconv2(x, xp, wt, bs)
+    y32 = _conv_gpu(x, xp, wt, bs, torch.float32)
+    worst = close(y32.cpu().numpy(), yo)
+    y16 = _conv_gpu(x, xp, wt, bs, torch.bfloat16)
+    ulp = bf16_ulp_close(y16, yo)
+    report("dynconv2", B=B, L=L, d=d, worst_err_over_bound=round(worst, 4), bf16_ulps=ulp)
+
+
+def test_dynconv2_identity_and_shift_exact():
+    B, L, d = 2, 16, 5120
+    w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, d=d)
+    x, xp, _, _ = synth.conv_site(w, 1)
+    zero = torch.zeros((2 * d // 16, d), dtype=torch.bfloat16)
+    ident = torch.stack([torch.ones(d), torch.zeros(d)])
+    shift = torch.stack([torch.zeros(d), torch.ones(d)])
+    y = _conv_gpu(x, xp, zero, ident, torch.bfloat16).cpu()
+    assert torch.equal(y, x)
+    y = _conv_gpu(x, xp, zero, shift, torch.bfloat16).cpu()
+    assert torch.equal(y[:, 0], xp) and torch.equal(y[:, 1:], x[:, :-1])
