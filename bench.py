@@ -1,0 +1,334 @@
+"""Throughput of the DFlash 2 per-cycle draft-block path on one MI355X.
+
+One step = one whole cycle over one batch of synthetic inputs, replayed from a
+HIP graph: 20 two-tap conv sites (each its own x, x_{-1} and tap weights),
+top-16 over the drafter's block logits, pair scores (gathered bf16 MFMA
+projections + bilinear epilogue), the Viterbi path, and greedy verification
+against the target's logits.  Default workload: 32 requests, block 16
+(15 drafts), vocabulary 151,936, hidden 5120, rank 256.
+
+Prints one JSON line.  value = draft blocks per second (requests x cycles /
+s) for the whole step; per-kernel times come from HIP events recorded on the
+launch stream by the library's timing hook; the roofline object describes the
+kernel with the largest time per step; cpu_baseline times the CPU oracle on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft blocks/s (topk+select+verify) at B=1/8/32, block 8/16; % HBM peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm",
+               "pair_epilogue", "path", "argmax_part", "greedy_final"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b32_blk16_v151936_conv")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batch x block sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="requests the oracle recomputes")
+    ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device copy of this size (counter calibration)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def build_cycle(w, dev, E=None, conv=True):
+    import torch
+    import synth
+    from draft_selection_bf16_amd.cycle import ConvSite, Cycle
+    z, tok, _ = synth.drafter_logits(w, device=dev)
+    Z = synth.target_logits(w, z, tok, device=dev)
+    if E is None:
+        E = synth.embeddings(w, device=dev)
+    wa, wb, wh = synth.selector_weights(w, device=dev)
+    h = synth.context_hidden(w, device=dev)
+    last = synth.last_tokens(w, device=dev)
+    sites = []
+    if conv:
+        for s in range(w.conv_sites):
+            x, xp, wt, bs = synth.conv_site(w, s, device=dev)
+            sites.append(ConvSite(x, xp, wt, bs, torch.empty(x.shape, dtype=torch.bfloat16, device=dev)))
+    cyc = Cycle(logits=z, target=Z, emb=E, h=h, w_a=wa, w_b=wb, w_h=wh, last_tok=last, K=w.K,
+                path_mode=w.path_mode, verify=w.verify, tau=w.tau if w.tau > 0 else 1.0,
+                conv_sites=sites, seed=w.seed)
+    return cyc, E
+
+
+def time_graph(cyc, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        cyc.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        cyc.replay()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return a.elapsed_time(b) / steps, wall
+
+
+def profile_kernels(cyc, steps):
+    """Per-launch durations of each kernel tag over `steps` eager cycles."""
+    import torch
+    import draft_selection_bf16_amd as df2
+    out = {}
+    per_step_launch = {"conv_gemm": len(cyc.conv_sites), "conv_epilogue": len(cyc.conv_sites)}
+    for tag in KERNEL_TAGS:
+        n_per = per_step_launch.get(tag, 1)
+        if n_per == 0:
+            continue
+        torch.cuda.synchronize()
+        df2.dflash2_profile_start(tag, steps * n_per)
+        for _ in range(steps):
+            cyc.run()
+        ms = df2.dflash2_profile_stop(steps * n_per)
+        if ms:
+            out[tag] = dict(launches_per_step=len(ms) / steps, avg_us=1e3 * sum(ms) / len(ms),
+                            us_per_step=1e3 * sum(ms) / steps)
+    return out
+
+
+def algorithmic(w, tag, esz=2):
+    """(bytes, flops) one launch of `tag` must move / compute."""
+    B, T, K, V, d, r = w.B, w.T, w.K, w.V, w.d, w.r
+    G2 = 2 * (d // 16)
+    L = w.block
+    if tag == "topk_chunk":
+        return B * T * V * esz + B * T * K * 8, 0
+    if tag in ("argmax_part", "sumexp_part"):
+        return B * (T + 1) * V * esz, 0
+    if tag == "project_gemm":
+        mc = B * T * K
+        outs = mc * 2 * r + B * r + B * T * r
+        return (mc + B + B * T) * d * 2 + 3 * r * d * 2 + 4 * outs, 2 * d * outs
+    if tag == "conv_gemm":
+        return B * L * d * 2 + G2 * d * 2, 2 * B * L * d * G2
+    if tag == "conv_epilogue":
+        return 2 * B * L * d * 2 + B * d * 2, 4 * B * L * d
+    return None, None
+
+
+def roofline_of(w, tag, avg_us):
+    by, fl = algorithmic(w, tag)
+    if by is None:
+        return None
+    t = avg_us * 1e-6
+    if fl and fl / by > (BF16_PEAK_TFLOPS * 1e12) / (HBM_PEAK_GBS * 1e9):
+        ach = fl / t / 1e12
+        return dict(kernel=tag, bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
+                    algorithmic_flops=fl, algorithmic_bytes=by, avg_us=round(avg_us, 2))
+    ach = by / t / 1e9
+    return dict(kernel=tag, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, algorithmic_bytes=by,
+                avg_us=round(avg_us, 2))
+
+
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_b32_blk16_v151936_conv.txt")
+TAG_NAMES = {"conv_gemm": "gemm_kernel<64", "conv_epilogue": "conv_epilogue_kernel",
+             "topk_chunk": "topk_chunk_kernel", "project_gemm": "gemm_kernel<128",
+             "argmax_part": "argmax_part_kernel"}
+
+
+def source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "draft_selection_bf16_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(tag):
+    """HBM bytes per launch of `tag` from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy's readings), or None
+    when the summary is missing or the kernel sources changed since."""
+    if not os.path.exists(COUNTERS):
+        return None
+    kv, rows = {}, {}
+    for line in open(COUNTERS):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        if line.startswith("kernel "):
+            parts = line.split()
+            rows[parts[1]] = {k: float(v) for k, v in (p.split("=") for p in parts[2:])}
+        elif "=" in line:
+            k, v = (x.strip() for x in line.split("=", 1))
+            kv[k] = v
+    if kv.get("source_sha256") != source_hash() or tag not in rows:
+        return None
+    r = rows[tag]
+    return int(1024 * (r["fetch_kib"] * float(kv["fetch_factor"]) +
+                       r["write_kib"] * float(kv["write_factor"])))
+
+
+def cpu_baseline(cyc, w, nreq):
+    """The oracle's cycle for `nreq` of the requests (all 20 conv sites on
+    those requests, top-16, pair scores, Viterbi, greedy verification)."""
+    import numpy as np
+    import torch
+    import oracle
+    rows = list(range(nreq))
+    # host copies (not timed)
+    z = cyc.logits[rows].cpu()
+    Z = cyc.target[rows].cpu()
+    h = cyc.h[rows].cpu()
+    last = cyc.last_tok[rows].cpu().numpy()
+    wa, wb, wh = cyc.w_a.cpu(), cyc.w_b.cpu(), cyc.w_h.cpu()
+    sites = [(s.x[rows].cpu(), s.x_prev[rows].cpu(), s.w.cpu(),
+              None if s.base is None else s.base.cpu()) for s in cyc.conv_sites]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for x, xp, wt, bs in sites:
+        oracle.dynconv2(x, xp, wt, bs)
+    idx, val = oracle.topk(z, w.K)
+    t1 = time.perf_counter()
+    # embedding rows of the oracle's own candidates (a gather; not timed)
+    uniq, inv = np.unique(np.concatenate([idx.ravel(), last]), return_inverse=True)
+    sub = cyc.emb[torch.from_numpy(uniq).to(cyc.emb.device).long()].cpu()
+    ridx = inv[: idx.size].reshape(idx.shape).astype(np.int32)
+    rlast = inv[idx.size:].astype(np.int32)
+    t2 = time.perf_counter()
+    S = oracle.pair_scores(ridx, val, rlast, sub, h, wa, wb, wh)
+    p = oracle.path(S, idx, oracle.PATH_VITERBI)
+    oracle.verify_greedy(Z, p["tok"])
+    t3 = time.perf_counter()
+    secs = (t1 - t0) + (t3 - t2)
+    return dict(value=round(nreq / secs, 4), unit="blocks/s", cores=oracle.num_threads(),
+                kind="oracle", seconds=round(secs, 2),
+                sample=f"{nreq} of {w.B} requests of {w.name}: 20 conv sites, top-16, pair scores, "
+                       f"Viterbi path, greedy verify (embedding-row gather excluded)")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
+              f"multi-GPU form in this build", file=sys.stderr)
+        sys.exit(2)
+    log("importing torch")
+    import torch
+    import synth
+    import draft_selection_bf16_amd as df2
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    df2.lib()
+    dev = torch.device("cuda:0")
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    w = synth.WORKLOADS[args.workload]
+    log(f"building inputs for {w.name}")
+    cyc, E = build_cycle(w, dev)
+    cyc.run()
+    torch.cuda.synchronize()
+    cyc.capture()
+    log("timing the full cycle")
+    ms, wall = time_graph(cyc, args.steps, args.warmup)
+    value = w.B / (ms / 1e3)
+
+    # the same cycle without the conv sites (top-K + select + verify only)
+    cyc_nc, _ = build_cycle(w, dev, E=E, conv=False)
+    cyc_nc.capture(conv=False)
+    ms_nc, _ = time_graph(cyc_nc, args.steps, args.warmup)
+
+    kernels = {}
+    roof = None
+    if not args.no_kernel_profile:
+        log("per-kernel event timing")
+        kernels = profile_kernels(cyc, min(args.steps, 50))
+        dom = max(kernels, key=lambda k: kernels[k]["us_per_step"])
+        roof = roofline_of(w, dom, kernels[dom]["avg_us"])
+        if roof is not None and w.name == "b32_blk16_v151936_conv":
+            roof["traffic"] = measured_traffic(dom)
+        for k, v in kernels.items():
+            rl = roofline_of(w, k, v["avg_us"])
+            if rl:
+                v["roofline"] = {kk: rl[kk] for kk in ("bound", "achieved", "unit", "frac")}
+
+    sweep = {}
+    if not args.no_sweep:
+        log("sweep")
+        del cyc_nc
+        for name in ("b1_blk8_v151936", "b8_blk8_v151936_sampled", "b32_blk8_v151936",
+                     "b1_blk16_v151936", "b8_blk16_v151936"):
+            ws_ = synth.WORKLOADS[name]
+            c2, _ = build_cycle(ws_, dev, E=E, conv=False)
+            c2.capture(conv=False)
+            m2, _ = time_graph(c2, args.steps, args.warmup)
+            sweep[name] = dict(B=ws_.B, block=ws_.block, path=ws_.path_mode, verify=ws_.verify,
+                               us_per_cycle=round(m2 * 1e3, 2), blocks_per_s=round(ws_.B / (m2 / 1e3), 1))
+            del c2
+        sweep[w.name + " (no conv)"] = dict(B=w.B, block=w.block, us_per_cycle=round(ms_nc * 1e3, 2),
+                                            blocks_per_s=round(w.B / (ms_nc / 1e3), 1))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(cyc, w, args.cpu_sample)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "block": w.block, "draft_tokens": w.T,
+                   "candidates": w.K, "vocab": w.V, "hidden": w.d, "rank": w.r,
+                   "conv_sites": w.conv_sites, "path": w.path_mode, "verify": w.verify,
+                   "step": "20 x dynconv2 + topk + pair_scores + path + verify, one HIP graph"},
+        "tokens_scored_per_s": round(w.B * w.T * w.K / (ms / 1e3), 1),
+        "value_without_conv": round(w.B / (ms_nc / 1e3), 1),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "sweep": sweep,
+        "wall_s_timed": round(wall, 3),
+    }
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(s + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -31,7 +31,7 @@ EXPORTS = [
     "dflash2_path_viterbi",
     "dflash2_dynconv2_workspace_bytes", "dflash2_dynconv2",
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
-    "dflash2_philox4x64",
+    "dflash2_philox4x64", "dflash2_profile_start", "dflash2_profile_stop",
 ]
 
 
@@ -72,6 +72,10 @@ def lib():
         L.dflash2_verify_greedy.argtypes = [P, I, I64, P, I, I, P, P, P, SZ, P]
         L.dflash2_verify_reject.argtypes = [P, I, I64, P, P, P, P, I, I, I, F, P, P, P, P, SZ, P]
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
+        L.dflash2_profile_start.argtypes = [C.c_char_p, I]
+        L.dflash2_profile_start.restype = I
+        L.dflash2_profile_stop.argtypes = [P, I, P]
+        L.dflash2_profile_stop.restype = I
         for name in ("dflash2_topk", "dflash2_pair_scores", "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
                      "dflash2_philox4x64"):
@@ -189,3 +193,18 @@ def dflash2_verify_reject(target, path_tok, path_rank, cand_idx, q, temperature,
 def dflash2_philox4x64(seed_dev, b, t, out, stream=None):
     _check(lib().dflash2_philox4x64(_ptr(seed_dev), _ptr(b), _ptr(t), int(b.numel()), _ptr(out),
                                     _stream(stream)), "dflash2_philox4x64")
+
+
+def dflash2_profile_start(kernel: str, max_launches: int):
+    """Arm the kernel timing hook for one kernel tag (see include/dflash2.h)."""
+    _check(lib().dflash2_profile_start(kernel.encode(), int(max_launches)), "dflash2_profile_start")
+
+
+def dflash2_profile_stop(max_launches: int = 4096):
+    """Per-launch durations (ms) of the armed kernel since profile_start."""
+    import numpy as np
+    ms = np.zeros(max_launches, np.float32)
+    n = C.c_int(0)
+    _check(lib().dflash2_profile_stop(ms.ctypes.data_as(C.c_void_p), max_launches, C.byref(n)),
+           "dflash2_profile_stop")
+    return ms[: n.value].astype(float).tolist()

@@ -5,7 +5,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/dflash2.h"
+#include "dflash2.h"
 #include "df2_internal.h"
 
 using namespace df2;
@@ -187,7 +187,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[2].out = hg;
   s[2].ldo = r;
   s[2].gate = gate;
-  hipError_t e = launch_gemm(s, 3, d, 1, 128, stream);
+  hipError_t e = launch_gemm(s, 3, d, 1, 128, "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores (epilogue)");

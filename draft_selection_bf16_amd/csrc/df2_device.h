@@ -59,6 +59,12 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   hi = __shfl_xor(hi, m);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  lo = __shfl(lo, src);
+  hi = __shfl(hi, src);
+  return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
@@ -84,27 +90,56 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return __popcll(m & ((1ull << lane_id()) - 1ull));
 }
 
-// Select the 16 largest keys among n keys held 'per' to a lane (keys[i] of
-// lane l is element l + 64 i); returns the j-th largest in lane j (j < 16),
-// 0 elsewhere or when fewer than j+1 non-empty keys exist.  The selected
-// keys are cleared in 'keys'.
+// The 16th largest of the non-empty keys held PER to a lane (keys are
+// unique), or 0 when there are fewer than 16.  MSB-first bit search: keep a
+// bit when at least 16 keys are >= the prefix with that bit set.  Counts are
+// ballot popcounts, so the search runs on the scalar unit with no cross-lane
+// data movement.
 template <int PER>
-__device__ __forceinline__ uint64_t wave_take16(uint64_t (&keys)[PER]) {
-  uint64_t mine = 0;
-  const int lane = lane_id();
-#pragma unroll 1
-  for (int j = 0; j < 16; ++j) {
-    uint64_t best = 0;
+__device__ __forceinline__ uint64_t kth16(const uint64_t (&keys)[PER]) {
+  uint64_t t = 0;
+#pragma unroll 4
+  for (int bit = 63; bit >= 0; --bit) {
+    const uint64_t cand = t | (1ull << bit);
+    int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) best = keys[i] > best ? keys[i] : best;
-    uint64_t top = wave_max_u64(best);
-    if (top == 0) break;
-    if (lane == j) mine = top;
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      if (keys[i] == top) keys[i] = 0;
+    for (int i = 0; i < PER; ++i) cnt += __popcll(ballot(keys[i] >= cand));
+    if (cnt >= 16) t = cand;
   }
-  return mine;
+  return t;
+}
+
+// Move the keys >= t (non-empty) of every lane to dst[0..n) (in no
+// particular order) and return n.  dst may alias the source buffer only if
+// the keys were already loaded to registers.
+template <int PER>
+__device__ __forceinline__ int gather_at_least(const uint64_t (&keys)[PER], uint64_t t,
+                                               uint64_t* dst) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool keep = keys[i] != 0ull && keys[i] >= t;
+    const uint64_t m = ballot(keep);
+    if (keep) dst[n + lanes_below(m)] = keys[i];
+    n += __popcll(m);
+  }
+  return n;
+}
+
+// buf[0..n) holds n <= 16 distinct keys (LDS, this wave's own); lane j < n
+// returns the j-th largest, other lanes 0.  Each key's rank is the number of
+// larger keys; keys are scattered to their ranks in the same buffer.
+__device__ __forceinline__ uint64_t sorted16(uint64_t* buf, int n) {
+  const int lane = lane_id();
+  const uint64_t mine = lane < n ? buf[lane] : 0ull;
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < n) rank += buf[i] > mine ? 1 : 0;
+  __builtin_amdgcn_wave_barrier();
+  if (lane < n) buf[rank] = mine;
+  __builtin_amdgcn_wave_barrier();
+  return lane < n ? buf[lane] : 0ull;
 }
 
 // ---------------------------------------------------------------- Philox

@@ -8,6 +8,15 @@
 
 namespace df2 {
 
+// Kernel timing hook: brackets launches of the armed kernel tag with events
+// on the launch stream (see dflash2_profile_start).
+struct ProfileScope {
+  ProfileScope(const char* tag, hipStream_t stream);
+  ~ProfileScope();
+  bool on;
+  hipStream_t stream;
+};
+
 // Aligned sub-buffer carving of a caller workspace.
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -41,7 +50,7 @@ struct GemmSeg {
 };
 // out = gate(X W^T) for up to 3 segments in one launch; K = d (multiple of 64)
 hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
-                       hipStream_t stream);
+                       const char* tag, hipStream_t stream);
 
 // ---- pair scores epilogue ---------------------------------------------------
 hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,

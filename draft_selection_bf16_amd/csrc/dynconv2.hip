@@ -24,6 +24,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxTaps = 2048;   // 2G <= 2048  <=>  d <= 16384
+constexpr int kMaxSplit = 16;    // K slices of the tap GEMM
 
 template <bool Y_BF16>
 __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
@@ -36,8 +37,12 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
   const int G = d / 16, NT = 2 * G;
   for (int n = threadIdx.x; n < NT; n += kThreads) {
     const float* p = part + (int64_t)row * NT + n;
+    float v[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) v[s] = s < ksplit ? p[(int64_t)s * kstride] : 0.f;
     float acc = 0.f;
-    for (int s = 0; s < ksplit; ++s) acc += p[(int64_t)s * kstride];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) acc += v[s];   // slices in a fixed order
     sc[n] = acc;
   }
   __syncthreads();
@@ -82,12 +87,18 @@ ConvPlan conv_plan(int B, int L, int d, int group) {
   const int M = B * L, N = 2 * (d / 16);
   const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
   const int nk = d / 64;
-  // smallest divisor of d/64 that gives >= 256 work-groups (at most 16 slices)
+  // one K slice per XCD (8) when d/64 allows it, so each XCD streams its
+  // slice of x and W once; otherwise the smallest divisor of d/64 that gives
+  // >= 256 work-groups (at most 16 slices)
   int ks = 1;
-  for (int s = 1; s <= nk && s <= 16; ++s) {
-    if (nk % s) continue;
-    ks = s;
-    if (tiles * s >= 256) break;
+  if (nk % 8 == 0) {
+    ks = 8;
+  } else {
+    for (int s = 1; s <= nk && s <= 16; ++s) {
+      if (nk % s) continue;
+      ks = s;
+      if (tiles * s >= 256) break;
+    }
   }
   p.ksplit = ks;
   p.ws_bytes = align256((size_t)ks * (size_t)M * (size_t)N * sizeof(float));
@@ -115,8 +126,9 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
   s.ldo = N;
   s.out_kstride = (int64_t)M * N;
   s.gate = 0;
-  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, stream);
+  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, "conv_gemm", stream);
   if (e != hipSuccess) return e;
+  ProfileScope ps("conv_epilogue", stream);
   if (y_dt == 1)
     conv_epilogue_kernel<true><<<dim3(M), dim3(kThreads), 0, stream>>>(
         (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);

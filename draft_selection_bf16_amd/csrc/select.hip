@@ -23,6 +23,7 @@ namespace df2 {
 namespace {
 
 constexpr int kMaxR = 256;
+constexpr int kMaxLattice = 63 * 16 * 16;   // T <= 63, K <= 16
 
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
@@ -30,22 +31,40 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
                                                             const float* __restrict__ cand_val,
                                                             int T, int K, int r,
                                                             float* __restrict__ scores) {
-  __shared__ float sG[16][kMaxR + 1];   // A(pred) * H_t
-  __shared__ float sB[16][kMaxR + 1];   // B(cand)
+  // rows padded to kLd floats: 16-byte aligned, and 16 rows at one column
+  // fall in 16 different 16-byte bank groups
+  constexpr int kLd = kMaxR + 4;
+  __shared__ __attribute__((aligned(16))) float sG[16 * kLd];   // A(pred) * H_t
+  __shared__ __attribute__((aligned(16))) float sB[16 * kLd];   // B(cand)
   const int bt = blockIdx.x, b = bt / T, t = bt % T;
   const int tid = threadIdx.x;
   const int npred = t == 0 ? 1 : K;
-  const float* H = hgate + (int64_t)bt * r;
-  // stage: predecessor rows scaled by the gate, candidate B rows
-  for (int e = tid; e < npred * r; e += blockDim.x) {
-    int i = e / r, q = e % r;
-    float a = t == 0 ? a_last[(int64_t)b * r + q]
-                     : ab[((int64_t)(bt - 1) * K + i) * (2 * r) + q];
-    sG[i][q] = a * H[q];
+  const int r4 = r / 4;
+  const f32x4* H4 = (const f32x4*)(hgate + (int64_t)bt * r);
+  // each thread stages up to 4 float4 of G and 4 of B (16 rows x 64 float4)
+  f32x4 ga[4], gb[4];
+  int gi[4], gq[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int e = tid + u * 256;            // float4 index over [16 rows][r4]
+    gi[u] = e / r4;
+    gq[u] = e % r4;
+    ga[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (gi[u] < npred) {
+      const float* src = t == 0 ? a_last + (int64_t)b * r
+                                : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
+      ga[u] = *(const f32x4*)(src + 4 * gq[u]);
+    }
+    if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
   }
-  for (int e = tid; e < K * r; e += blockDim.x) {
-    int j = e / r, q = e % r;
-    sB[j][q] = ab[((int64_t)bt * K + j) * (2 * r) + r + q];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    if (gi[u] < 16) {
+      f32x4 h = gi[u] < npred ? H4[gq[u]] : f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)&sG[gi[u] * kLd + 4 * gq[u]] = ga[u] * h;
+      *(f32x4*)&sB[gi[u] * kLd + 4 * gq[u]] = gb[u];
+    }
   }
   __syncthreads();
   const int i = tid / 16, j = tid % 16;
@@ -55,8 +74,16 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     *out = -INFINITY;
     return;
   }
+  const f32x4* gr = (const f32x4*)&sG[i * kLd];
+  const f32x4* br = (const f32x4*)&sB[j * kLd];
   float acc = 0.f;
-  for (int q = 0; q < r; ++q) acc = fmaf(sG[i][q], sB[j][q], acc);
+  for (int q = 0; q < r4; ++q) {
+    f32x4 x = gr[q], y = br[q];
+    acc = fmaf(x[0], y[0], acc);
+    acc = fmaf(x[1], y[1], acc);
+    acc = fmaf(x[2], y[2], acc);
+    acc = fmaf(x[3], y[3], acc);
+  }
   *out = cand_val[(int64_t)bt * K + j] + acc;
 }
 
@@ -74,8 +101,35 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
                                                   float* __restrict__ q, float* __restrict__ path_score) {
   __shared__ uint8_t psi[64][16];
   __shared__ int32_t chosen[64];
+  __shared__ __attribute__((aligned(16))) float sS[kMaxLattice];
   const int b = blockIdx.x, lane = threadIdx.x;
-  const float* S = scores + (int64_t)b * T * K * K;
+  // the request's whole lattice (T*K*K floats) in one burst of loads
+  {
+    const float* g = scores + (int64_t)b * T * K * K;
+    const int n = T * K * K;
+    if (((uintptr_t)g & 15) == 0) {
+      const f32x4* g4 = (const f32x4*)g;
+      const int n4 = n / 4;
+      for (int e0 = 0; e0 < n4; e0 += 64 * 8) {   // eight 16-byte loads in flight per lane
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 64 + lane;
+          v[u] = e < n4 ? g4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * 64 + lane;
+          if (e < n4) ((f32x4*)sS)[e] = v[u];
+        }
+      }
+      for (int e = n4 * 4 + lane; e < n; e += 64) sS[e] = g[e];
+    } else {
+      for (int e = lane; e < n; e += 64) sS[e] = g[e];
+    }
+  }
+  __syncthreads();
+  const float* S = sS;
   const int j = lane & 15;
   float total = 0.f;
 
@@ -194,6 +248,7 @@ hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const floa
                                 const float* cand_val, int B, int T, int K, int r, float* scores,
                                 hipStream_t stream) {
   if (B * T == 0) return hipSuccess;
+  ProfileScope ps("pair_epilogue", stream);
   pair_epilogue_kernel<<<dim3(B * T), dim3(256), 0, stream>>>(ab, a_last, hgate, cand_val, T, K, r,
                                                                 scores);
   return hipGetLastError();
@@ -204,6 +259,7 @@ hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int 
                        int32_t* path_tok, float* q, float* path_score, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   float inv_tau = mode == 2 ? 1.0f / temperature : 0.f;
+  ProfileScope ps("path", stream);
   path_kernel<<<dim3(B), dim3(64), 0, stream>>>(scores, cand_idx, T, K, mode, inv_tau, seed_dev,
                                                 path_rank, path_tok, q, path_score);
   return hipGetLastError();

@@ -10,10 +10,11 @@
 //    work-group per (row, chunk); its four waves stream interleaved 1 KB
 //    slices with 16-byte loads (8 bf16 / 4 fp32 per lane), four loads in
 //    flight per lane;
-//  * every wave keeps a running threshold -- the 16th best key it has
-//    buffered -- and only entries at or above it take the slow path, which
-//    appends exact (value, index) keys to a per-wave LDS buffer; a full
-//    buffer is cut back to its 16 best keys with wave-wide max reductions;
+//  * every wave keeps a running threshold -- the largest 16th-best value any
+//    wave of the work-group has published -- and checks one maximum per
+//    16-byte load against it; only entries at or above it are appended, as
+//    exact (value, index) keys, to a per-wave LDS buffer, and a full buffer
+//    is cut back to its 16 best keys with wave-wide max reductions;
 //  * the four wave lists are merged in LDS; with one chunk per row the
 //    result is written directly, otherwise a second small kernel merges the
 //    per-chunk lists of each row.
@@ -27,7 +28,7 @@ namespace {
 
 constexpr int kWaves = 4;        // waves per work-group
 constexpr int kThreads = kWaves * kWave;
-constexpr int kCap = 512;        // LDS keys per wave
+constexpr int kCap = 128;        // LDS keys per wave
 constexpr int kUnroll = 4;       // 16-byte loads in flight per lane
 
 template <typename E>
@@ -65,16 +66,19 @@ struct Vec<F16> {                 // fp16: 8 per 16 bytes
   }
 };
 
-// Per-wave filter state; `buf` is this wave's LDS key buffer.
+// Per-wave filter state.  `buf` is this wave's LDS key buffer; `share` holds
+// one published threshold per wave of the work-group.  Any wave's 16th best
+// value is a lower bound for the work-group's 16th best, so every wave may
+// filter with the largest published value.
 struct Filter {
   uint64_t* buf;
+  volatile float* share;
   int cnt;
-  uint64_t thr_key;  // keys must exceed this to enter
-  float thr_f;       // value part of thr_key (fast pre-check: f >= thr_f)
+  float thr;   // entries with value < thr cannot be in the result
 };
 
-// Cut the buffer back to its 16 best keys and raise the threshold.
-__device__ __forceinline__ void compact(Filter& F) {
+// Cut the buffer back to its 16 best keys; publish and raise the threshold.
+__device__ __forceinline__ void compact(Filter& F, int wave) {
   constexpr int PER = kCap / kWave;
   uint64_t keys[PER];
   const int lane = lane_id();
@@ -83,32 +87,36 @@ __device__ __forceinline__ void compact(Filter& F) {
     int s = lane + i * kWave;
     keys[i] = s < F.cnt ? F.buf[s] : 0ull;
   }
-  uint64_t mine = wave_take16<PER>(keys);
-  if (lane < 16) F.buf[lane] = mine;
-  uint64_t k15 = __shfl(mine, 15);
-  int have = __popcll(ballot(mine != 0ull));
-  F.cnt = have;
-  if (have >= 16) {
-    F.thr_key = k15;
-    F.thr_f = key_value(k15);
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t t = kth16<PER>(keys);
+  F.cnt = gather_at_least<PER>(keys, t, F.buf);
+  if (t != 0ull) {
+    const float v = key_value(t);
+    if (v > F.thr) F.thr = v;
+    if (lane == 0) F.share[wave] = F.thr;
   }
   __builtin_amdgcn_wave_barrier();
 }
 
-// Offer one entry per lane (valid lanes only).  Wave-uniform control flow.
-__device__ __forceinline__ void offer(Filter& F, bool valid, float f, uint32_t idx) {
-  bool pass = valid && (f >= F.thr_f) && (make_key(f, idx) > F.thr_key);
+__device__ __forceinline__ void refresh(Filter& F) {
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) F.thr = fmaxf(F.thr, F.share[w]);
+}
+
+// Append the entries of this lane that reach the threshold (one per call);
+// wave-uniform control flow, keys built only when some lane passes.
+__device__ __forceinline__ void offer(Filter& F, bool valid, float f, uint32_t idx, int wave) {
+  bool pass = valid && f >= F.thr;
   uint64_t m = ballot(pass);
   if (m == 0ull) return;
-  int n = __popcll(m);
-  if (F.cnt + n > kCap) {
-    compact(F);
-    pass = valid && (f >= F.thr_f) && (make_key(f, idx) > F.thr_key);
+  if (F.cnt + __popcll(m) > kCap) {
+    compact(F, wave);
+    pass = valid && f >= F.thr;
     m = ballot(pass);
-    n = __popcll(m);
+    if (m == 0ull) return;
   }
   if (pass) F.buf[F.cnt + lanes_below(m)] = make_key(f, idx);
-  F.cnt += n;
+  F.cnt += __popcll(m);
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -132,12 +140,12 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
     for (int64_t s = lo; s < a0; s += kWave) {
       int64_t i = s + lane;
       bool v = i < a0;
-      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i);
+      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i, wave);
     }
     for (int64_t s = a1; s < hi; s += kWave) {
       int64_t i = s + lane;
       bool v = i < hi;
-      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i);
+      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i, wave);
     }
   }
   const u32x4* vp = (const u32x4*)(base + (uintptr_t)a0 * esz);
@@ -154,16 +162,18 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      bool any = false;
+      float f[VN];
 #pragma unroll
-      for (int e = 0; e < VN; ++e) any |= Vec<E>::get(v[u], e) >= F.thr_f;
-      any &= ok[u];
-      if (ballot(any) == 0ull) continue;
-      int64_t g = g0 + u * stride + lane;
+      for (int e = 0; e < VN; ++e) f[e] = Vec<E>::get(v[u], e);
+      float gm = f[0];
 #pragma unroll
-      for (int e = 0; e < VN; ++e)
-        offer(F, ok[u], Vec<E>::get(v[u], e), (uint32_t)(a0 + g * VN + e));
+      for (int e = 1; e < VN; ++e) gm = fmaxf(gm, f[e]);
+      if (ballot(ok[u] && gm >= F.thr) == 0ull) continue;
+      const uint32_t i0 = (uint32_t)(a0 + (g0 + u * stride + lane) * VN);
+#pragma unroll
+      for (int e = 0; e < VN; ++e) offer(F, ok[u], f[e], i0 + e, wave);
     }
+    refresh(F);
   }
 }
 
@@ -175,6 +185,7 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, uint64_t* __restrict__ part) {
   __shared__ uint64_t sbuf[kWaves][kCap];
   __shared__ uint64_t smerge[kWaves * 16];
+  __shared__ float sthr[kWaves];
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int64_t row = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -183,21 +194,27 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   const int esz = sizeof(u32x4) / Vec<E>::n;
   const void* rowp = (const char*)logits + row * vocab * esz;
 
-  Filter F{sbuf[wave], 0, 0ull, -INFINITY};
+  if (lane == 0) sthr[wave] = -INFINITY;
+  __syncthreads();
+  Filter F{sbuf[wave], sthr, 0, -INFINITY};
   scan_range<E>(F, rowp, lo, hi, wave);
-  compact(F);
+  compact(F, wave);
   if (lane < 16) smerge[wave * 16 + lane] = lane < F.cnt ? F.buf[lane] : 0ull;
   __syncthreads();
   if (wave != 0) return;
   uint64_t keys[1] = {smerge[lane]};
-  uint64_t mine = wave_take16<1>(keys);
+  const uint64_t t = kth16<1>(keys);
+  __builtin_amdgcn_wave_barrier();
+  const int n = gather_at_least<1>(keys, t, smerge);
+  __builtin_amdgcn_wave_barrier();
   if (splits == 1) {
+    const uint64_t mine = sorted16(smerge, n);
     if (lane < k) {
       out_idx[row * k + lane] = (int32_t)key_index(mine);
       out_val[row * k + lane] = key_value(mine);
     }
   } else if (lane < 16) {
-    part[((int64_t)row * splits + split) * 16 + lane] = mine;
+    part[((int64_t)row * splits + split) * 16 + lane] = lane < n ? smerge[lane] : 0ull;
   }
 }
 
@@ -207,8 +224,9 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
                                                               int32_t* __restrict__ out_idx,
                                                               float* __restrict__ out_val) {
   constexpr int PER = 8;
-  const int lane = lane_id();
-  const int64_t row = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+  __shared__ uint64_t sel[kWaves][16];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
   if (row >= rows) return;
   const int n = splits * 16;
   uint64_t keys[PER];
@@ -217,7 +235,10 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
     int s = lane + i * kWave;
     keys[i] = s < n ? part[row * n + s] : 0ull;
   }
-  uint64_t mine = wave_take16<PER>(keys);
+  const uint64_t t = kth16<PER>(keys);
+  const int m = gather_at_least<PER>(keys, t, sel[wave]);
+  __builtin_amdgcn_wave_barrier();
+  const uint64_t mine = sorted16(sel[wave], m);
   if (lane < k) {
     out_idx[row * k + lane] = (int32_t)key_index(mine);
     out_val[row * k + lane] = key_value(mine);
@@ -251,16 +272,20 @@ hipError_t launch_topk(const void* logits, int dt, int64_t rows, int64_t vocab, 
   if (rows == 0) return hipSuccess;
   uint64_t* part = (uint64_t*)ws;
   dim3 grid((unsigned)(rows * plan.splits)), block(kThreads);
-  if (dt == 0)
-    topk_chunk_kernel<float><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
+  {
+    ProfileScope ps("topk_chunk", stream);
+    if (dt == 0)
+      topk_chunk_kernel<float><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
+                                                           out_idx, out_val, part);
+    else if (dt == 1)
+      topk_chunk_kernel<Bf16><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
+                                                          out_idx, out_val, part);
+    else
+      topk_chunk_kernel<F16><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
                                                          out_idx, out_val, part);
-  else if (dt == 1)
-    topk_chunk_kernel<Bf16><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
-                                                        out_idx, out_val, part);
-  else
-    topk_chunk_kernel<F16><<<grid, block, 0, stream>>>(logits, vocab, plan.splits, plan.chunk, k,
-                                                       out_idx, out_val, part);
+  }
   if (plan.splits > 1) {
+    ProfileScope ps("topk_merge", stream);
     dim3 g2((unsigned)((rows + kWaves - 1) / kWaves));
     topk_merge_kernel<<<g2, block, 0, stream>>>(part, rows, plan.splits, k, out_idx, out_val);
   }

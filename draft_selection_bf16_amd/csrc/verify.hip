@@ -169,6 +169,7 @@ __global__ __launch_bounds__(64) void greedy_final_kernel(const uint64_t* __rest
   if (lane <= T) {
     const uint64_t* p = part + ((int64_t)b * (T + 1) + lane) * splits;
     uint64_t k = 0;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) k = p[s] > k ? p[s] : k;
     y = k ? (int)key_index(k) : -1;
   }
@@ -289,6 +290,7 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
   float s = 0.f;
   if (lane <= T) {
     const RowPart* p = part + ((int64_t)b * (T + 1) + lane) * splits;
+#pragma unroll 8
     for (int i = 0; i < splits; ++i) combine_part(k, s, p[i].key, p[i].s, c);
   }
   bool reject = false;
@@ -530,12 +532,16 @@ hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int3
   const int64_t rows = (int64_t)B * (T + 1);
   uint64_t* part = (uint64_t*)((char*)ws + plan.off_part);
   dim3 grid((unsigned)(rows * plan.splits)), block(kThreads);
-  if (dt == 0)
-    argmax_part_kernel<0><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
-  else if (dt == 1)
-    argmax_part_kernel<1><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
-  else
-    argmax_part_kernel<2><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+  {
+    ProfileScope ps("argmax_part", stream);
+    if (dt == 0)
+      argmax_part_kernel<0><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+    else if (dt == 1)
+      argmax_part_kernel<1><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+    else
+      argmax_part_kernel<2><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+  }
+  ProfileScope ps("greedy_final", stream);
   greedy_final_kernel<<<dim3(B), dim3(64), 0, stream>>>(part, plan.splits, T, path_tok, accept_len,
                                                          out_tok);
   return hipGetLastError();
@@ -550,13 +556,23 @@ static void reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
   RowPart* part = (RowPart*)((char*)ws + plan.off_part);
   DecRec* dec = (DecRec*)((char*)ws + plan.off_dec);
   float* rsum = (float*)((char*)ws + plan.off_rsum);
-  sumexp_part_kernel<DT><<<dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream>>>(
-      z, vocab, plan.splits, plan.chunk, c, part);
-  reject_decide_kernel<DT><<<dim3(B), dim3(64), 0, stream>>>(z, vocab, part, plan.splits, T, K, c,
-                                                            path_tok, path_rank, q, seed_dev,
-                                                            accept_len, out_tok, dec);
-  residual_chunk_kernel<DT><<<dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream>>>(
-      z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum);
+  {
+    ProfileScope ps("sumexp_part", stream);
+    sumexp_part_kernel<DT><<<dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream>>>(
+        z, vocab, plan.splits, plan.chunk, c, part);
+  }
+  {
+    ProfileScope ps("reject_decide", stream);
+    reject_decide_kernel<DT><<<dim3(B), dim3(64), 0, stream>>>(z, vocab, part, plan.splits, T, K, c,
+                                                              path_tok, path_rank, q, seed_dev,
+                                                              accept_len, out_tok, dec);
+  }
+  {
+    ProfileScope ps("residual_chunk", stream);
+    residual_chunk_kernel<DT><<<dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream>>>(
+        z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum);
+  }
+  ProfileScope ps("residual_find", stream);
   residual_find_kernel<DT><<<dim3(B), dim3(kThreads), 0, stream>>>(
       z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum, out_tok);
 }

@@ -217,6 +217,21 @@ int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, cons
 int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
                        uint64_t* out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing hook (host).  Arms this thread so that every later launch of
+ * the kernel with tag `kernel` is bracketed by HIP events recorded on the
+ * stream it is launched on (at most max_launches launches).  Tags:
+ *   "topk_chunk", "topk_merge", "project_gemm", "pair_epilogue", "path",
+ *   "argmax_part", "greedy_final", "sumexp_part", "reject_decide",
+ *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue".
+ * dflash2_profile_stop waits for the recorded events, writes up to `max`
+ * per-launch durations in milliseconds to ms (host) and their count to *n,
+ * and disarms.  Not for use during graph capture.  Events are created on
+ * the first use and kept; no device memory is allocated.
+ * ------------------------------------------------------------------------ */
+int dflash2_profile_start(const char* kernel, int max_launches);
+int dflash2_profile_stop(float* ms, int max, int* n);
+
 #ifdef __cplusplus
 }
 #endif
