@@ -84,6 +84,15 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+// index of this wave in its work-group, in a scalar register
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave)); }
+// a value that is the same in every lane, moved to scalar registers so that
+// branches on it are scalar branches
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 // number of set bits of m below this lane
 __device__ __forceinline__ int lanes_below(uint64_t m) {

@@ -87,12 +87,13 @@ ConvPlan conv_plan(int B, int L, int d, int group) {
   const int M = B * L, N = 2 * (d / 16);
   const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
   const int nk = d / 64;
-  // one K slice per XCD (8) when d/64 allows it, so each XCD streams its
-  // slice of x and W once; otherwise the smallest divisor of d/64 that gives
+  // four K slices when d/64 allows it (measured best for B*L = 512..1024 at
+  // d = 5120: slice s runs on the XCDs s and s + 4, whose L2s hold that
+  // slice of x and W); otherwise the smallest divisor of d/64 that gives
   // >= 256 work-groups (at most 16 slices)
   int ks = 1;
-  if (nk % 8 == 0) {
-    ks = 8;
+  if (nk % 4 == 0) {
+    ks = 4;
   } else {
     for (int s = 1; s <= nk && s <= 16; ++s) {
       if (nk % s) continue;

@@ -6,18 +6,26 @@
 // lower index.
 //
 // Design (HBM-streaming, one pass over the logits):
-//  * each row is cut into `splits` contiguous chunks; one 256-thread
-//    work-group per (row, chunk); its four waves stream interleaved 1 KB
-//    slices with 16-byte loads (8 bf16 / 4 fp32 per lane), four loads in
-//    flight per lane;
-//  * every wave keeps a running threshold -- the largest 16th-best value any
-//    wave of the work-group has published -- and checks one maximum per
-//    16-byte load against it; only entries at or above it are appended, as
-//    exact (value, index) keys, to a per-wave LDS buffer, and a full buffer
-//    is cut back to its 16 best keys with wave-wide max reductions;
-//  * the four wave lists are merged in LDS; with one chunk per row the
-//    result is written directly, otherwise a second small kernel merges the
-//    per-chunk lists of each row.
+//  * each row is cut into `splits` contiguous chunks (one per row once there
+//    are a few hundred rows); one 512-thread work-group per (row, chunk);
+//    its eight waves stream interleaved 1 KB slices with 16-byte loads
+//    (8 bf16 / 4 fp32 per lane), four loads in flight per lane;
+//  * every wave filters against a threshold: the largest value any wave of
+//    the work-group has published as a lower bound of its own 16th best (any
+//    such bound is a bound for the work-group).  For bf16 rows and a
+//    positive threshold the check is a packed signed 16-bit maximum of the
+//    eight raw values against the threshold's bits (order-preserving there),
+//    about seven instructions per 16-byte load;
+//  * a 16-byte group that may hold a candidate is queued raw in a per-wave
+//    LDS queue (a few instructions); a full queue is expanded in bulk, one
+//    group per lane, into exact 64-bit (value, index) keys in a per-wave LDS
+//    buffer, which is then cut back with a search over the value bits only
+//    (ballot popcounts on the scalar unit; ties kept) -- this raises the
+//    threshold to the 16th best value seen so far;
+//  * at the end the keys at or above the largest published threshold, a
+//    few dozen, are pooled, one wave selects the exact 16 best (64-bit
+//    search) and, with one chunk per row, rank-sorts and writes them;
+//    otherwise a second kernel merges the per-chunk lists of each row.
 // (value, index) pairs are compared as single 64-bit keys (df2_device.h), so
 // the result does not depend on the order in which entries are seen.
 #include "df2_device.h"
@@ -26,152 +34,304 @@
 namespace df2 {
 namespace {
 
-constexpr int kWaves = 4;        // waves per work-group
+constexpr int kWaves = 8;        // waves per work-group
 constexpr int kThreads = kWaves * kWave;
-constexpr int kCap = 128;        // LDS keys per wave
+constexpr int kCap = 256;        // LDS keys per wave
+constexpr int kPer = kCap / kWave;
 constexpr int kUnroll = 4;       // 16-byte loads in flight per lane
+constexpr int kQueue = 320;      // queued 16-byte groups per wave
+constexpr int kQueueFlush = kQueue - kUnroll * kWave;   // expand above this
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Element access of a 16-byte group: get0 reads element 0, shift drops it
+// (the next element moves to position 0), raw/nan build groups from
+// scalar loads.
 template <typename E>
 struct Vec;
 template <>
 struct Vec<float> {               // fp32: 4 per 16 bytes
   static constexpr int n = 4;
-  __device__ static float get(const u32x4& v, int e) {
-    return __uint_as_float(v[e]);
-  }
-  __device__ static float scalar(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  static constexpr int value_bits = 32;   // bits of the order key that vary
+  __device__ static float get0(const u32x4& v) { return __uint_as_float(v[0]); }
+  __device__ static u32x4 shift(const u32x4& v) { return u32x4{v[1], v[2], v[3], 0u}; }
+  __device__ static float get(const u32x4& v, int e) { return __uint_as_float(v[e]); }
+  __device__ static uint32_t raw(const void* p, int64_t i) { return ((const uint32_t*)p)[i]; }
+  static constexpr uint32_t nan = 0x7fc00000u;
 };
 struct Bf16 {};
-template <>
-struct Vec<Bf16> {                // bf16: 8 per 16 bytes
+struct F16 {};
+template <typename H>
+struct Vec16 {                    // 16-bit types: 8 per 16 bytes
   static constexpr int n = 8;
+  __device__ static u32x4 shift(const u32x4& v) {
+    return u32x4{__builtin_amdgcn_alignbit(v[1], v[0], 16), __builtin_amdgcn_alignbit(v[2], v[1], 16),
+                 __builtin_amdgcn_alignbit(v[3], v[2], 16), v[3] >> 16};
+  }
+  __device__ static uint32_t raw(const void* p, int64_t i) { return ((const uint16_t*)p)[i]; }
+};
+template <>
+struct Vec<Bf16> : Vec16<Bf16> {
+  static constexpr int value_bits = 16;
+  static constexpr uint32_t nan = 0x7fc0u;
+  __device__ static float get0(const u32x4& v) { return bf16_lo(v[0]); }
   __device__ static float get(const u32x4& v, int e) {
     uint32_t w = v[e >> 1];
     return (e & 1) ? bf16_hi(w) : bf16_lo(w);
   }
-  __device__ static float scalar(const void* p, int64_t i) {
-    return bf16_to_f32(((const uint16_t*)p)[i]);
-  }
 };
-struct F16 {};
 template <>
-struct Vec<F16> {                 // fp16: 8 per 16 bytes
-  static constexpr int n = 8;
+struct Vec<F16> : Vec16<F16> {
+  static constexpr int value_bits = 32;
+  static constexpr uint32_t nan = 0x7e00u;
+  __device__ static float get0(const u32x4& v) { return half_to_f32((uint16_t)(v[0] & 0xffffu)); }
   __device__ static float get(const u32x4& v, int e) {
     uint32_t w = v[e >> 1];
     return half_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
   }
-  __device__ static float scalar(const void* p, int64_t i) {
-    return half_to_f32(((const uint16_t*)p)[i]);
-  }
 };
 
-// Per-wave filter state.  `buf` is this wave's LDS key buffer; `share` holds
-// one published threshold per wave of the work-group.  Any wave's 16th best
-// value is a lower bound for the work-group's 16th best, so every wave may
-// filter with the largest published value.
+// The group of entries i0 .. i0 + n - 1 of a row, those outside [lo, hi)
+// replaced by NaN (never a candidate).
+template <typename E>
+__device__ __forceinline__ u32x4 partial_group(const void* rowp, int64_t i0, int64_t lo, int64_t hi) {
+  constexpr int VN = Vec<E>::n, PW = VN / 4;   // elements per 32-bit word
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int64_t i = i0 + h * PW + j;
+      const uint32_t b = (i >= lo && i < hi) ? Vec<E>::raw(rowp, i) : Vec<E>::nan;
+      w |= b << (32 / PW * j);
+    }
+    r[h] = w;
+  }
+  return r;
+}
+
+// Per-wave filter state.  `buf` is this wave's LDS key buffer, `q`/`qi` its
+// queue of 16-byte groups (raw data and index of the first element) that
+// may hold a candidate; `share` holds one published threshold per wave of
+// the work-group.
 struct Filter {
   uint64_t* buf;
-  volatile float* share;
-  int cnt;
+  u32x4* q;
+  uint32_t* qi;
+  float* share;   // read and written with relaxed work-group atomics
+  int cnt;     // keys in buf
+  int qn;      // groups in q
   float thr;   // entries with value < thr cannot be in the result
 };
 
-// Cut the buffer back to its 16 best keys; publish and raise the threshold.
+__device__ __forceinline__ void publish(Filter& F, int wave) {
+  __hip_atomic_store(F.share + wave, F.thr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Largest t (with the low 32 - VB bits zero) such that at least 16 of the
+// order values held N to a lane are >= t (0 stands for "none"); 0 if fewer
+// than 16.  Keys with ord >= t are a superset of the 16 best (ties at the
+// boundary are kept).
+template <int VB, int N>
+__device__ __forceinline__ uint32_t value_cut16(const uint32_t (&ord)[N]) {
+  uint32_t t = 0;
+#pragma unroll 4
+  for (int bit = 31; bit >= 32 - VB; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) cnt += __popcll(ballot(ord[i] >= cand));
+    if (cnt >= 16) t = cand;
+  }
+  return t;
+}
+
+// Cut the buffer back to the keys whose value can still be among the 16
+// best; publish and raise the threshold.  Falls back to the exact 64-bit cut
+// when ties at the boundary would leave the buffer nearly full.
+template <int VB>
 __device__ __forceinline__ void compact(Filter& F, int wave) {
-  constexpr int PER = kCap / kWave;
-  uint64_t keys[PER];
+  uint64_t keys[kPer];
+  uint32_t ord[kPer];
   const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < kPer; ++i) {
     int s = lane + i * kWave;
     keys[i] = s < F.cnt ? F.buf[s] : 0ull;
+    ord[i] = (uint32_t)(keys[i] >> 32);
   }
   __builtin_amdgcn_wave_barrier();
-  const uint64_t t = kth16<PER>(keys);
-  F.cnt = gather_at_least<PER>(keys, t, F.buf);
-  if (t != 0ull) {
-    const float v = key_value(t);
+  const uint32_t t = value_cut16<VB, kPer>(ord);
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) n += __popcll(ballot(keys[i] != 0ull && ord[i] >= t));
+  const uint64_t tk = n > kCap - 2 * kWave ? kth16<kPer>(keys)   // massive ties: exact cut
+                                           : (uint64_t)t << 32;
+  F.cnt = gather_at_least<kPer>(keys, tk, F.buf);
+  if (t != 0u) {
+    const float v = value_of_ord(t);
     if (v > F.thr) F.thr = v;
-    if (lane == 0) F.share[wave] = F.thr;
+    if (lane == 0) publish(F, wave);
   }
   __builtin_amdgcn_wave_barrier();
 }
 
 __device__ __forceinline__ void refresh(Filter& F) {
+  float t = F.thr;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) F.thr = fmaxf(F.thr, F.share[w]);
+  for (int w = 0; w < kWaves; ++w)
+    t = fmaxf(t, __hip_atomic_load(F.share + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  // the same value in every lane: keep it in a scalar register
+  F.thr = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(t)));
 }
 
-// Append the entries of this lane that reach the threshold (one per call);
-// wave-uniform control flow, keys built only when some lane passes.
-__device__ __forceinline__ void offer(Filter& F, bool valid, float f, uint32_t idx, int wave) {
-  bool pass = valid && f >= F.thr;
-  uint64_t m = ballot(pass);
-  if (m == 0ull) return;
-  if (F.cnt + __popcll(m) > kCap) {
-    compact(F, wave);
-    pass = valid && f >= F.thr;
-    m = ballot(pass);
-    if (m == 0ull) return;
+// Expand the queued groups into keys, one group per lane and element by
+// element, keeping the entries that reach the threshold; then cut the
+// buffer back to at most about `keep` keys (raising the threshold to the
+// 16th best value seen so far).
+template <typename E>
+__device__ __forceinline__ void flush(Filter& F, int wave, int keep) {
+  constexpr int VB = Vec<E>::value_bits;
+  const int lane = lane_id();
+  for (int base = 0; base < F.qn; base += kWave) {
+    const int s = base + lane;
+    const bool valid = s < F.qn;
+    u32x4 v = F.q[valid ? s : 0];
+    uint32_t idx = F.qi[valid ? s : 0];
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int e = 0; e < Vec<E>::n; ++e) {
+      const float f = Vec<E>::get0(v);
+      bool pass = valid && f >= F.thr;
+      uint64_t m = ballot(pass);
+      if (m != 0ull) {
+        if (F.cnt + __popcll(m) > kCap) {
+          compact<VB>(F, wave);
+          pass = valid && f >= F.thr;
+          m = ballot(pass);
+        }
+        if (pass) F.buf[F.cnt + lanes_below(m)] = make_key(f, idx);
+        F.cnt += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+      }
+      v = Vec<E>::shift(v);
+      ++idx;
+    }
   }
-  if (pass) F.buf[F.cnt + lanes_below(m)] = make_key(f, idx);
-  F.cnt += __popcll(m);
-  __builtin_amdgcn_wave_barrier();
+  F.qn = 0;
+  if (F.cnt > keep) compact<VB>(F, wave);
+}
+
+// Could any of the eight bf16 values of v reach thr (> 0)?  Positive bf16
+// values order like their bits read as signed 16-bit integers, and every
+// negative value (and -0) reads as negative: one packed maximum decides.
+// (The words are reinterpreted with memcpy: a bit_cast of a vector element
+// reads the wrong element with this compiler.)
+__device__ __forceinline__ bool bf16_may_pass(const u32x4& v, int thr16) {
+  const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+  s16x2 x0, x1, x2, x3;
+  __builtin_memcpy(&x0, &w0, 4);
+  __builtin_memcpy(&x1, &w1, 4);
+  __builtin_memcpy(&x2, &w2, 4);
+  __builtin_memcpy(&x3, &w3, 4);
+  s16x2 a = __builtin_elementwise_max(__builtin_elementwise_max(x0, x1),
+                                      __builtin_elementwise_max(x2, x3));
+  const int m = (int)a[0] > (int)a[1] ? (int)a[0] : (int)a[1];
+  return m >= thr16;
 }
 
 template <typename E>
 __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t lo, int64_t hi,
                                            int wave) {
   constexpr int VN = Vec<E>::n;
+  constexpr int VB = Vec<E>::value_bits;
+  constexpr bool kBf16 = VB == 16;
   const int lane = lane_id();
-  const uintptr_t base = (uintptr_t)rowp;
   const int esz = sizeof(u32x4) / VN;
-  // head / tail elements outside 16-byte alignment: wave 0, one per lane
-  int64_t a0 = lo, a1 = hi;
+  // the body [a0, a1) is 16-byte aligned; the head [lo, a0) and the tail
+  // [a1, hi) have fewer than VN entries each and go to wave 0's queue as
+  // NaN-padded groups (pointer arithmetic stays on typed pointers so that
+  // loads remain global loads)
+  int64_t a0, a1;
   {
-    uintptr_t p0 = base + (uintptr_t)lo * esz;
-    int64_t head = (int64_t)(((16 - (p0 & 15)) & 15) / esz);
+    const unsigned mis = (unsigned)(size_t)((const char*)rowp + lo * esz) & 15u;
+    int64_t head = (int64_t)(((16u - mis) & 15u) / esz);
     a0 = lo + head < hi ? lo + head : hi;
-    int64_t body = (hi - a0) / VN * VN;
-    a1 = a0 + body;
+    a1 = a0 + (hi - a0) / VN * VN;
   }
   if (wave == 0) {
-    for (int64_t s = lo; s < a0; s += kWave) {
-      int64_t i = s + lane;
-      bool v = i < a0;
-      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i, wave);
+    const bool c = (lane == 0 && a0 > lo) || (lane == 1 && hi > a1);
+    const uint64_t m = ballot(c);
+    if (c) {
+      const int64_t i0 = lane == 0 ? lo : a1;
+      F.q[lanes_below(m)] = partial_group<E>(rowp, i0, lo, lane == 0 ? a0 : hi);
+      F.qi[lanes_below(m)] = (uint32_t)i0;
     }
-    for (int64_t s = a1; s < hi; s += kWave) {
-      int64_t i = s + lane;
-      bool v = i < hi;
-      offer(F, v, v ? Vec<E>::scalar(rowp, i) : 0.f, (uint32_t)i, wave);
-    }
+    F.qn = __popcll(m);
+    __builtin_amdgcn_wave_barrier();
   }
-  const u32x4* vp = (const u32x4*)(base + (uintptr_t)a0 * esz);
+  const u32x4* vp = (const u32x4*)((const char*)rowp + a0 * esz);
   const int64_t ngroups = (a1 - a0) / VN;   // 16-byte groups
   const int64_t stride = (int64_t)kWaves * kWave;
-  for (int64_t g0 = (int64_t)wave * kWave; g0 < ngroups; g0 += stride * kUnroll) {
+  if (ngroups > 0) {
+    // prime the threshold with the 16th best value among this wave's first
+    // 64 groups (NaN never qualifies); those entries are seen again below
+    const int64_t g = (int64_t)wave * kWave + lane;
+    const bool ok = g < ngroups;
+    const u32x4 v = __builtin_nontemporal_load(vp + (ok ? g : 0));
+    uint32_t ord[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      const float f = Vec<E>::get(v, e);
+      ord[e] = ok && f == f ? ord_of(f) : 0u;
+    }
+    const uint32_t t = value_cut16<VB, VN>(ord);
+    if (t != 0u) {
+      F.thr = fmaxf(F.thr, value_of_ord(t));
+      if (lane == 0) publish(F, wave);
+    }
+  }
+  const int ng = (int)ngroups;   // < 2^31: rows hold < 2^32 entries
+  for (int g0 = wave * kWave; g0 < ng; g0 += (int)stride * kUnroll) {
+    if (F.qn > kQueueFlush) flush<E>(F, wave, 32);
     u32x4 v[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      int64_t g = g0 + u * stride + lane;
-      ok[u] = g < ngroups;
-      v[u] = ok[u] ? __builtin_nontemporal_load(vp + g) : u32x4{0u, 0u, 0u, 0u};
+      const int g = g0 + u * (int)stride + lane;
+      ok[u] = g < ng;
+      v[u] = __builtin_nontemporal_load(vp + (ok[u] ? g : 0));
     }
+    // the threshold is the same in all lanes: decide the test once per
+    // iteration, on the scalar unit
+    const float thr = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(F.thr)));
+    uint64_t m[kUnroll];
+    if (kBf16 && thr > 0.f) {
+      const int thr16 = (int)(__float_as_uint(thr) >> 16);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) m[u] = ballot(bf16_may_pass(v[u], thr16) & ok[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float gm = Vec<E>::get(v[u], 0);
+#pragma unroll
+        for (int e = 1; e < VN; ++e) gm = fmaxf(gm, Vec<E>::get(v[u], e));
+        m[u] = ballot((gm >= thr) & ok[u]);
+      }
+    }
+    // queue the groups that may hold a candidate (rare once the threshold
+    // is up); flush() expands them in bulk
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float f[VN];
-#pragma unroll
-      for (int e = 0; e < VN; ++e) f[e] = Vec<E>::get(v[u], e);
-      float gm = f[0];
-#pragma unroll
-      for (int e = 1; e < VN; ++e) gm = fmaxf(gm, f[e]);
-      if (ballot(ok[u] && gm >= F.thr) == 0ull) continue;
-      const uint32_t i0 = (uint32_t)(a0 + (g0 + u * stride + lane) * VN);
-#pragma unroll
-      for (int e = 0; e < VN; ++e) offer(F, ok[u], f[e], i0 + e, wave);
+      if (m[u] == 0ull) continue;
+      if ((m[u] >> lane) & 1ull) {
+        const int s = F.qn + lanes_below(m[u]);
+        F.q[s] = v[u];
+        F.qi[s] = (uint32_t)(a0 + (int64_t)(g0 + u * (int)stride + lane) * VN);
+      }
+      F.qn += __popcll(m[u]);
+      __builtin_amdgcn_wave_barrier();
     }
     refresh(F);
   }
@@ -184,9 +344,12 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const void* __restrict__ logits, int64_t vocab, int splits, int64_t chunk, int k,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, uint64_t* __restrict__ part) {
   __shared__ uint64_t sbuf[kWaves][kCap];
+  __shared__ u32x4 squeue[kWaves][kQueue];
+  __shared__ uint32_t sqidx[kWaves][kQueue];
   __shared__ uint64_t smerge[kWaves * 16];
   __shared__ float sthr[kWaves];
-  const int wave = threadIdx.x / kWave, lane = lane_id();
+  __shared__ int scnt[kWaves];
+  const int wave = wave_id(), lane = lane_id();
   const int64_t row = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
   const int64_t lo = (int64_t)split * chunk;
@@ -196,25 +359,78 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
 
   if (lane == 0) sthr[wave] = -INFINITY;
   __syncthreads();
-  Filter F{sbuf[wave], sthr, 0, -INFINITY};
+  Filter F{sbuf[wave], squeue[wave], sqidx[wave], sthr, 0, 0, -INFINITY};
   scan_range<E>(F, rowp, lo, hi, wave);
-  compact(F, wave);
-  if (lane < 16) smerge[wave * 16 + lane] = lane < F.cnt ? F.buf[lane] : 0ull;
+  flush<E>(F, wave, 16);
   __syncthreads();
-  if (wave != 0) return;
-  uint64_t keys[1] = {smerge[lane]};
-  const uint64_t t = kth16<1>(keys);
-  __builtin_amdgcn_wave_barrier();
-  const int n = gather_at_least<1>(keys, t, smerge);
+  // Every entry dropped anywhere was below some published threshold, and
+  // the wave that published the largest one, T, holds >= 16 keys >= T: the
+  // keys >= T of all waves contain the 16 best of the chunk.
+  float T = sthr[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) T = fmaxf(T, sthr[w]);
+  {
+    uint64_t keys[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int s = lane + i * kWave;
+      keys[i] = s < F.cnt ? F.buf[s] : 0ull;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t tk = T == -INFINITY ? 0ull : (uint64_t)ord_of(T) << 32;
+    F.cnt = gather_at_least<kPer>(keys, tk, F.buf);
+    if (lane == 0) scnt[wave] = F.cnt;
+  }
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) total += scnt[w];
+  if (total > kWave) {
+    // many ties at T: exact 16 best of each wave first
+    uint64_t keys[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int s = lane + i * kWave;
+      keys[i] = s < F.cnt ? F.buf[s] : 0ull;
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t t = kth16<kPer>(keys);
+    const int n = gather_at_least<kPer>(keys, t, F.buf);
+    __builtin_amdgcn_wave_barrier();
+    if (lane < 16) smerge[wave * 16 + lane] = lane < n ? F.buf[lane] : 0ull;
+    __syncthreads();
+    if (wave != 0) return;
+    constexpr int MP = kWaves * 16 / kWave;
+    uint64_t mk[MP];
+#pragma unroll
+    for (int i = 0; i < MP; ++i) mk[i] = smerge[lane + i * kWave];
+    const uint64_t tt = kth16<MP>(mk);
+    __builtin_amdgcn_wave_barrier();
+    total = gather_at_least<MP>(mk, tt, smerge);
+  } else {
+    if (wave != 0) return;
+    // lane l takes the l-th key of the concatenated per-wave lists
+    int w = 0, before = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves - 1; ++i)
+      if (lane >= before + scnt[w]) {
+        before += scnt[w];
+        ++w;
+      }
+    uint64_t mk[1] = {lane < total ? sbuf[w][lane - before] : 0ull};
+    const uint64_t tt = kth16<1>(mk);
+    __builtin_amdgcn_wave_barrier();
+    total = gather_at_least<1>(mk, tt, smerge);
+  }
   __builtin_amdgcn_wave_barrier();
   if (splits == 1) {
-    const uint64_t mine = sorted16(smerge, n);
+    const uint64_t mine = sorted16(smerge, total);
     if (lane < k) {
       out_idx[row * k + lane] = (int32_t)key_index(mine);
       out_val[row * k + lane] = key_value(mine);
     }
   } else if (lane < 16) {
-    part[((int64_t)row * splits + split) * 16 + lane] = lane < n ? smerge[lane] : 0ull;
+    part[((int64_t)row * splits + split) * 16 + lane] = lane < total ? smerge[lane] : 0ull;
   }
 }
 
@@ -249,10 +465,12 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
 
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   (void)k;
-  // aim for >= 2048 work-groups, but keep chunks >= 16K entries and
-  // <= 32 chunks per row (the merge holds at most 512 keys per row)
-  int64_t want = (2048 + rows - 1) / (rows > 0 ? rows : 1);
-  int64_t max_by_size = vocab / 16384;
+  // about 448 work-groups of eight waves (two per CU keep enough loads in
+  // flight); one per row when there are that many rows, which also needs no
+  // merge.  Chunks stay >= 8192 entries and <= 32 per row (the merge holds
+  // at most 512 keys per row).
+  int64_t want = (448 + rows - 1) / (rows > 0 ? rows : 1);
+  int64_t max_by_size = vocab / 8192;
   int64_t s = want < max_by_size ? want : max_by_size;
   if (s < 1) s = 1;
   if (s > 32) s = 32;

@@ -47,9 +47,10 @@ def test_topk_validation():
     assert L.dflash2_topk(FAKE, 1, 4, 10, 16, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_SHAPE
     assert L.dflash2_topk(FAKE, 1, 4, 1000, 0, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_SHAPE
     assert L.dflash2_topk(None, 1, 4, 1000, 16, FAKE, FAKE, FAKE, 1 << 20, None) == df2.DF2_ERR_NULL
-    need = df2.dflash2_topk_workspace_bytes(480, 151936, 16)
+    # few rows: the rows are split into chunks whose partial lists need workspace
+    need = df2.dflash2_topk_workspace_bytes(15, 151936, 16)
     assert need > 0
-    assert L.dflash2_topk(FAKE, 1, 480, 151936, 16, FAKE, FAKE, FAKE, need - 1, None) == \
+    assert L.dflash2_topk(FAKE, 1, 15, 151936, 16, FAKE, FAKE, FAKE, need - 1, None) == \
         df2.DF2_ERR_WORKSPACE
     # zero rows is a no-op and succeeds without touching the runtime
     assert L.dflash2_topk(None, 1, 0, 1000, 16, None, None, None, 0, None) == df2.DF2_OK

@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from draft_selection_bf16_amd.cycle import ConvSite, Cycle
-from gpu_util import DEV, NEAR_TIE, bf16_ulp_close, close, report
+from gpu_util import DEV, NEAR_TIE, bf16_ulp_close, close, conv_error_bound, report
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -137,9 +137,9 @@ def check_cycle(cyc, w, rows, label, check_conv_sites=(0,)):
         if s >= len(cyc.conv_sites):
             continue
         site = cyc.conv_sites[s]
-        yo = oracle.dynconv2(site.x[rows].cpu(), site.x_prev[rows].cpu(), site.w.cpu(),
-                             None if site.base is None else site.base.cpu())
-        bf16_ulp_close(site.y[rows], yo)
+        args = (site.x[rows].cpu(), site.x_prev[rows].cpu(), site.w.cpu(),
+                None if site.base is None else site.base.cpu())
+        bf16_ulp_close(site.y[rows], oracle.dynconv2(*args), conv_error_bound(*args))
     report(label, rows=len(rows), S_worst=round(worst, 4), mean_accept=float(ga.mean()),
            reject_near_ties=near_v, **cmp)
 
