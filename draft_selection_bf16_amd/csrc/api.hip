@@ -106,6 +106,12 @@ int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
 
 // ------------------------------------------------------------------ pair scores
 namespace {
+// projection tiling: 128-row tiles in 4 stages (one 128 KB work-group per
+// CU); with the gathered embedding rows cold in cache (as in a decode
+// cycle) this beats two 64-row groups per CU, which re-read W twice as often
+int proj_bm() { return 128; }
+int proj_stages() { return 4; }
+int proj_waves() { return 4; }
 struct PairWs {
   size_t ab, alast, h, total;
 };
@@ -140,6 +146,8 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: d %d is not a positive multiple of 64", d);
   REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: r %d not a multiple of 16 in [16, 256]", r);
   REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores: vocab %lld", (long long)vocab);
+  REQUIRE((uint64_t)vocab * (uint64_t)d * 2u < (1ull << 32), DF2_ERR_UNSUPPORTED,
+          "dflash2_pair_scores: embedding table of %lld x %d bf16 is 4 GiB or more", (long long)vocab, d);
   REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores: gate %d", gate);
   if (B == 0) return DF2_OK;
   REQUIRE(cand_idx && cand_val && last_tok && emb && h && w_a && w_b && w_h && scores, DF2_ERR_NULL,
@@ -152,7 +160,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   float* ab = (float*)((char*)ws + pw.ab);
   float* alast = (float*)((char*)ws + pw.alast);
   float* hg = (float*)((char*)ws + pw.h);
-  GemmSeg s[3] = {};
+  GemmSeg s[4] = {};
   // candidates: [A | B] = E[cand] [W_A; W_B]^T
   s[0].x = (const uint16_t*)emb;
   s[0].gather = cand_idx;
@@ -187,7 +195,20 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[2].out = hg;
   s[2].ldo = r;
   s[2].gate = gate;
-  hipError_t e = launch_gemm(s, 3, d, 1, 128, "project_gemm", stream);
+  // W tiles are 128 rows and may not straddle W_A / W_B: for r not a
+  // multiple of 128 the candidate rows are projected as two problems
+  int nseg = 3;
+  if (r % 128 != 0) {
+    s[3] = s[0];
+    s[0].w1 = s[0].w0;
+    s[0].N = r;
+    s[3].w0 = s[3].w1 = (const uint16_t*)w_b;
+    s[3].n0 = r;
+    s[3].N = r;
+    s[3].out = ab + r;
+    nseg = 4;
+  }
+  hipError_t e = launch_gemm(s, nseg, d, 1, proj_bm(), proj_stages(), proj_waves(), "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores (epilogue)");

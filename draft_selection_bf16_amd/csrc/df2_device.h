@@ -13,6 +13,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family GPUs
+constexpr int kBufferWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- elements
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -133,6 +136,51 @@ __device__ __forceinline__ int gather_at_least(const uint64_t (&keys)[PER], uint
     n += __popcll(m);
   }
   return n;
+}
+
+// Number of the wave's 64 keys (one per lane) that are larger than this
+// lane's (keys distinct or 0).  64 independent compares against values read
+// from each lane -- no ballot/popcount round trips on the critical path.
+__device__ __forceinline__ int rank_in_wave(uint64_t key) {
+  const uint32_t lo = (uint32_t)key, hi = (uint32_t)(key >> 32);
+  int r = 0;
+#pragma unroll 16
+  for (int i = 0; i < kWave; ++i) {
+    // (readlane returns int: widen through uint32_t, not by sign extension)
+    const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, i) << 32) |
+                       (uint64_t)(uint32_t)__builtin_amdgcn_readlane(lo, i);
+    r += o > key ? 1 : 0;
+  }
+  return r;
+}
+
+// Number of the N keys keys[0..N) (LDS, N even) that are larger than `key`.
+// All lanes read the same addresses (broadcast LDS reads), so the loads
+// pipeline and the compares are independent.
+template <int N>
+__device__ __forceinline__ int rank_in_lds(uint64_t key, const uint64_t* keys) {
+  typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+  int r = 0;
+#pragma unroll 16
+  for (int i = 0; i < N; i += 2) {
+    const u64x2 o = *(const u64x2*)(keys + i);
+    r += (o[0] > key ? 1 : 0) + (o[1] > key ? 1 : 0);
+  }
+  return r;
+}
+
+// Exclusive prefix over the lanes of a small count c (0 <= c < 16) and the
+// wave total, from one ballot per bit of c (independent ballots).
+__device__ __forceinline__ int lane_prefix16(int c, int& total) {
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t m = ballot((c >> b) & 1);
+    ex += lanes_below(m) << b;
+    tot += __popcll(m) << b;
+  }
+  total = tot;
+  return ex;
 }
 
 // buf[0..n) holds n <= 16 distinct keys (LDS, this wave's own); lane j < n

@@ -42,15 +42,19 @@ struct GemmSeg {
   const uint16_t* w1;     // W rows n0..N-1 (row n -> w1[n - n0])
   int n0;
   int N;                  // output columns (multiple of 16)
-  float* out;             // out[m * ldo + n] (+ kslice * out_kstride)
+  float* out;             // out[m * ldo + n] (+ slice * out_kstride)
   int64_t ldo;
   int64_t out_kstride;    // elements between K-slice partial outputs
   int gate;               // 0 identity, 1 sigmoid (only when ksplit == 1)
   int tiles_m, tiles_n;   // filled by the launcher
 };
-// out = gate(X W^T) for up to 3 segments in one launch; K = d (multiple of 64)
-hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
-                       const char* tag, hipStream_t stream);
+// out = gate(X W^T) for up to 4 segments in one launch; K = d (multiple of 64).
+// Each segment needs n0 % 128 == 0 or n0 >= N, and x_rows * ldx * 2 < 2^32.
+// (bm, stages, waves) in {(128,3,4), (128,4,4), (128,3,8), (64,3,4), (64,4,4),
+// (64,3,8), (64,4,8)}; K % 64 == 0 and 1 <= ksplit <= K / 64 (slices of
+// K / 64 / ksplit K-tiles, rounded).
+hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int stages,
+                       int waves, const char* tag, hipStream_t stream);
 
 // ---- pair scores epilogue ---------------------------------------------------
 hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
@@ -87,6 +91,8 @@ hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int3
 struct ConvPlan {
   int ksplit;
   int bm;
+  int stages;
+  int waves;
   size_t ws_bytes;
 };
 ConvPlan conv_plan(int B, int L, int d, int group);

@@ -8,10 +8,10 @@
 //   y_t[ch] = (base0[ch] + c_t[ch/16]) x_t[ch] + (base1[ch] + c_t[G + ch/16]) x_{t-1}[ch].
 //
 // Two launches per application:
-//  1. the tap corrections c = X W^T on the matrix cores (gemm.hip), with the
-//     reduction over d split into slices so that a few hundred work-groups
-//     share a skinny problem (M = B*L rows, N = 2G, K = d); each slice
-//     writes its own partial product;
+//  1. the tap corrections c = X W^T on the matrix cores (gemm.hip; M = B*L
+//     rows, N = 2G, K = d: a skinny product), with the reduction over d
+//     split into slices so that a few hundred work-groups share it; each
+//     slice writes its own partial product;
 //  2. a streaming epilogue, one work-group per (b, t) row: sums the slice
 //     partials of its 2G taps in a fixed order into LDS, then reads x_t and
 //     x_{t-1} with 16-byte loads and writes y (bf16 round-to-nearest-even, or
@@ -83,24 +83,21 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
 ConvPlan conv_plan(int B, int L, int d, int group) {
   (void)group;
   ConvPlan p;
+  // 64-row tiles in 3 LDS stages (72 KB): two work-groups per CU, which
+  // keeps the CU's L2-to-LDS path busy (one 4-wave group leaves it about
+  // 40% idle)
   p.bm = 64;
+  p.stages = 3;
+  p.waves = 4;
   const int M = B * L, N = 2 * (d / 16);
   const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
   const int nk = d / 64;
-  // four K slices when d/64 allows it (measured best for B*L = 512..1024 at
-  // d = 5120: slice s runs on the XCDs s and s + 4, whose L2s hold that
-  // slice of x and W); otherwise the smallest divisor of d/64 that gives
-  // >= 256 work-groups (at most 16 slices)
-  int ks = 1;
-  if (nk % 4 == 0) {
-    ks = 4;
-  } else {
-    for (int s = 1; s <= nk && s <= 16; ++s) {
-      if (nk % s) continue;
-      ks = s;
-      if (tiles * s >= 256) break;
-    }
-  }
+  // K slices: about two work-groups per CU (<= 512), slices of >= 4 K-tiles
+  // and at most 16 slices (the epilogue's limit)
+  int ks = 512 / (tiles > 0 ? tiles : 1);
+  if (ks > nk / 4) ks = nk / 4;
+  if (ks > 16) ks = 16;
+  if (ks < 1) ks = 1;
   p.ksplit = ks;
   p.ws_bytes = align256((size_t)ks * (size_t)M * (size_t)N * sizeof(float));
   return p;
@@ -127,7 +124,7 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
   s.ldo = N;
   s.out_kstride = (int64_t)M * N;
   s.gate = 0;
-  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, "conv_gemm", stream);
+  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, plan.stages, plan.waves, "conv_gemm", stream);
   if (e != hipSuccess) return e;
   ProfileScope ps("conv_epilogue", stream);
   if (y_dt == 1)

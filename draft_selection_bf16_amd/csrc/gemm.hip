@@ -8,53 +8,85 @@
 // Both operands are K-contiguous rows (X: [M, K], W: [N, K]), so every lane
 // feeds the MFMA with 16 contiguous bytes of one row.
 //
-// Tiling: work-group = 4 waves (2 x 2), tile BM x 128 x 64 (BM = 128 or 64),
-// double-buffered LDS with rows padded to 144 bytes (conflict-free 16-byte
-// fragment reads), and a ring of P register-staged K-tiles so that P tiles
-// are in flight while the MFMAs of the current one run (one tile of MFMA
-// work is far shorter than a memory round trip).  X rows may be gathered through an index list (candidate tokens
-// into the embedding table).  Up to three independent problems share one
-// launch.  An optional K split writes per-slice partial products (no
-// atomics; the consumer sums the slices in a fixed order).
-// Work-groups are renumbered so that each XCD runs a contiguous range of
-// tiles: the N-tiles of one M-block then share that XCD's L2 for X.
+// Tiling: work-group = 4 or 8 waves (2 x 2 or 2 x 4), tile BM x 128 (BM = 64 or 128),
+// K-tiles of 64.  X rows may be gathered through an index list (candidate
+// tokens into the embedding table).  Up to four independent problems share
+// one launch.  An optional K split writes per-slice partial products (no
+// atomics; the consumer sums the slices in a fixed order).  Work-groups are
+// renumbered so that each XCD runs a contiguous range of tiles (the N-tiles
+// of one M-block then share that XCD's L2 for X), or, with a K split, so
+// that the slice index varies fastest.
+// The MFMA accumulators live in ordinary VGPRs (the file is compiled with
+// the VGPR form of the MFMA instructions), which keeps the accumulate chain
+// free of register copies.
 #include "df2_device.h"
 #include "df2_internal.h"
 
 namespace df2 {
+
+// dynamic LDS of the GEMM (declared outside the anonymous namespace: an
+// extern with internal linkage keeps the host-side launch stub from being
+// emitted)
+extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+
 namespace {
 
-constexpr int BN = 128, BK = 64, LDSW = BK + 8;  // LDS row = 72 bf16 = 144 bytes
-constexpr int kThreads = 256;
+constexpr int BN = 128, BK = 64;
 constexpr int kXcds = 8;
 
+constexpr int kMaxSeg = 4;
+
 struct Problem {
-  GemmSeg s[3];
-  int tile_begin[4];
+  GemmSeg s[kMaxSeg];
+  int tile_begin[kMaxSeg + 1];
   int nseg;
   int K;       // full reduction length; W rows are K apart
-  int ksplit;
-  int kslice;  // K elements per slice (multiple of BK)
+  int ksplit;  // slice s covers K-tiles [s nkt / ksplit, (s + 1) nkt / ksplit)
 };
 
 __device__ __forceinline__ float apply_gate(float z, int gate) {
   return gate == 1 ? 1.0f / (1.0f + expf(-z)) : z;
 }
 
-template <int BM, int P>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(Problem Pb) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int XCH = BM * BK / 8 / kThreads;
-  constexpr int WCH = BN * BK / 8 / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t sX[2][BM * LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * LDSW];
+// The K-tiles are copied by direct buffer-to-LDS loads (no register
+// staging) into S LDS stages, S - 1 of them in flight while the MFMAs of the
+// current one run; one barrier per K-tile.
+//
+// LDS stage = X tile [BM][64] then W tile [128][64], rows of 128 bytes.  One
+// load instruction of a wave fills 1 KB = 8 rows: lane i writes the 16-byte
+// slot (row i / 8, slot i % 8) and fetches the chunk slot ^ swz(row) of that
+// row, so the 16-byte chunks of a row are stored in swizzled order.  The
+// MFMA fragment reads (16 rows, one chunk each) then hit 16 distinct
+// 16-byte bank groups.  Rows outside the problem get an out-of-range lane
+// offset: the hardware writes zeros for them.
 
-  // XCD-aware numbering (work-group i runs on XCD i % 8).  Without a K
-  // split, each XCD takes a contiguous range of tiles, so the N-tiles of one
-  // M-block share that XCD's L2 for their X rows.  With a K split, the slice
-  // index is the fastest-varying part of the id, so each XCD holds one
-  // K-slice of X and W in its L2 and every byte comes from HBM once.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// One direct buffer-to-LDS load of 16 bytes per lane (a plain device
+// function: called from the kernel template directly, the builtin keeps the
+// host-side launch stub from being emitted).
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt left unconstrained)
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
+}
+
+// NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8) over the tile.
+template <int BM, int S, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
+  constexpr int kThreads = NW * 64;
+  constexpr int WCOL = NW / 2;                  // waves along N
+  constexpr int WM = BM / 2, WN = BN / WCOL;
+  constexpr int FM = WM / 16, FN = WN / 16;
+  constexpr int ALD = BM / (8 * NW), BLD = BN / (8 * NW);   // load instructions per wave per stage
+  constexpr int LPW = ALD + BLD;
+  constexpr int STAGE = (BM + BN) * BK * 2;     // bytes
+
   const int nb = gridDim.x;
   int bid = blockIdx.x;
   int tile, ks;
@@ -69,69 +101,64 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Problem Pb) {
   }
   int si = 0;
   while (si + 1 < Pb.nseg && tile >= Pb.tile_begin[si + 1]) ++si;
-  const GemmSeg& S = Pb.s[si];
+  const GemmSeg& S_ = Pb.s[si];
   const int local = tile - Pb.tile_begin[si];
-  const int m0 = (local / S.tiles_n) * BM, n0 = (local % S.tiles_n) * BN;
-  const int k_begin = ks * Pb.kslice;
-  const int nk = Pb.kslice / BK;
+  const int m0 = (local / S_.tiles_n) * BM, n0 = (local % S_.tiles_n) * BN;
+  const int nkt = Pb.K / BK;
+  const int kt0 = ks * nkt / Pb.ksplit, kt1 = (ks + 1) * nkt / Pb.ksplit;
+  const int k_begin = kt0 * BK;
+  const int nk = kt1 - kt0;
+  const int wave = wave_id(), lane = lane_id();
+  const int wm = wave / WCOL, wn = wave % WCOL;
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  const bool from_w0 = n0 < S_.n0;
+  const uint16_t* wbase = from_w0 ? S_.w0 + (int64_t)n0 * Pb.K : S_.w1 + (int64_t)(n0 - S_.n0) * Pb.K;
+  const int wrows = (from_w0 ? (S_.n0 < S_.N ? S_.n0 : S_.N) : S_.N) - n0;
+  const uint32_t xbytes = (uint32_t)(S_.x_rows * S_.ldx * 2);
+  const uint32_t wbytes = (uint32_t)((int64_t)wrows * Pb.K * 2);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)S_.x, 0, (int)xbytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, (int)wbytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xnone = __builtin_amdgcn_make_buffer_rsrc((void*)S_.x, 0, 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t wnone = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, 0, kBufferWord3);
+  // out of range for the whole K walk, whether or not the range check adds
+  // the scalar offset (the launcher keeps bytes + 2K + 16 <= 2^32)
+  const uint32_t kOut = 0xFFFFFFF0u - (uint32_t)Pb.K * 2u;
 
-  // Per-thread source rows for the 16-byte chunks it stages.  Loads are
-  // unconditional (so the compiler can count them and keep several K-tiles
-  // in flight): rows outside the problem read row 0 and are replaced by
-  // zeros when staged into LDS.
-  const uint16_t* xp[XCH];
-  const uint16_t* wp[WCH];
-  bool xv[XCH], wv[WCH];
+  // lane offsets of this wave's load instructions: instruction a fills rows
+  // 8 (wave + NW a) .. + 7 of the X tile, b likewise of the W tile
+  const int sub = lane >> 3, slot = lane & 7;
+  uint32_t xo[ALD], wo[BLD];
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    int c = tid + i * kThreads, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-    int m = m0 + row;
-    int64_t src = 0;
-    bool ok = false;
-    if (m < S.M) {
-      src = S.gather ? (int64_t)S.gather[m] : (int64_t)m;
-      ok = src >= 0 && src < S.x_rows;
-      if (!ok) src = 0;
+  for (int a = 0; a < ALD; ++a) {
+    const int row = 8 * (wave + NW * a) + sub;
+    const int c = slot ^ swz(row);
+    const int m = m0 + row;
+    int64_t src = -1;
+    if (m < S_.M) {
+      src = S_.gather ? (int64_t)S_.gather[m] : (int64_t)m;
+      if (src < 0 || src >= S_.x_rows) src = -1;
     }
-    xv[i] = ok;
-    xp[i] = S.x + src * S.ldx + k_begin + col;
+    xo[a] = src < 0 ? kOut : (uint32_t)((src * S_.ldx + k_begin + c * 8) * 2);
   }
 #pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    int c = tid + i * kThreads, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-    int n = n0 + row;
-    wv[i] = n < S.N;
-    const uint16_t* p = !wv[i] ? S.w0 : n < S.n0 ? S.w0 + (int64_t)n * Pb.K
-                                               : S.w1 + (int64_t)(n - S.n0) * Pb.K;
-    wp[i] = p + k_begin + col;
+  for (int b = 0; b < BLD; ++b) {
+    const int row = 8 * (wave + NW * b) + sub;
+    const int c = slot ^ swz(row);
+    wo[b] = row < wrows ? (uint32_t)(((int64_t)row * Pb.K + k_begin + c * 8) * 2) : kOut;
   }
-
-  // Register ring of P staged K-tiles: tile t lives in slot t % P.  While
-  // the MFMAs of tile k run from LDS, tiles k+1 .. k+P are in flight.
-  // Tiles past the end re-read the last tile (never stored).
-  u32x4 rx[P][XCH], rw[P][WCH];
-  auto gload = [&](int kt, u32x4 (&dx)[XCH], u32x4 (&dw)[WCH]) {
-    const int off = (kt < nk ? kt : nk - 1) * BK;
+  // K-tile t goes to stage t % S; tiles past the end read nothing (empty
+  // resources: zeros, no traffic) so that every step issues the same loads
+  auto issue = [&](int t) {
+    const bool in = t < nk;
+    uint8_t* sb = dyn_lds + (t % S) * STAGE;
+    const int so = __builtin_amdgcn_readfirstlane(in ? t * BK * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rx = in ? xres : xnone, rw = in ? wres : wnone;
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) dx[i] = *(const u32x4*)(xp[i] + off);
+    for (int a = 0; a < ALD; ++a)
+      load_lds16(rx, sb + (wave + NW * a) * 8 * 128, xo[a], so);
 #pragma unroll
-    for (int i = 0; i < WCH; ++i) dw[i] = *(const u32x4*)(wp[i] + off);
-  };
-  const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
-  auto sstore = [&](int buf, const u32x4 (&dx)[XCH], const u32x4 (&dw)[WCH]) {
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      int c = tid + i * kThreads, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      *(u32x4*)&sX[buf][row * LDSW + col] = xv[i] ? dx[i] : z4;
-    }
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) {
-      int c = tid + i * kThreads, row = c / (BK / 8), col = (c % (BK / 8)) * 8;
-      *(u32x4*)&sW[buf][row * LDSW + col] = wv[i] ? dw[i] : z4;
-    }
+    for (int b = 0; b < BLD; ++b)
+      load_lds16(rw, sb + BM * 128 + (wave + NW * b) * 8 * 128, wo[b], so);
   };
 
   f32x4 acc[FM][FN];
@@ -139,69 +166,103 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Problem Pb) {
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fq = lane >> 4;
+  // fragment byte offsets inside a stage (rows fixed per lane, chunk 4 s + fq)
+  int ao[FM][2], bo[FN][2];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * WM + i * 16 + fr;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) ao[i][s2] = r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int r = wn * WN + j * 16 + fr;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) bo[j][s2] = BM * 128 + r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
+  }
 
 #pragma unroll
-  for (int t = 0; t < P; ++t) gload(t, rx[t], rw[t]);
-  sstore(0, rx[0], rw[0]);
-  gload(P, rx[0], rw[0]);
-  __syncthreads();
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  // nk is a multiple of P: the unrolled group below has no guards, so the
-  // compiler can count outstanding loads and wait only for the tile it
-  // stores.  The last step stores a tile nobody reads.
-  for (int k0 = 0; k0 < nk; k0 += P) {
+  for (int t = 0; t < S - 1; ++t) issue(t);
+  for (int t = 0; t < nk; ++t) {
+    // this wave's copies of tile t are done; the barrier makes everyone's
+    // visible and frees the stage read in step t - 1 for tile t + S - 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPW));
+    __builtin_amdgcn_s_barrier();
+    issue(t + S - 1);
+    const uint8_t* st = dyn_lds + (t % S) * STAGE;
 #pragma unroll
-    for (int st = 0; st < P; ++st) {
-      const int kt = k0 + st;
-      const int buf = kt & 1;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      bf16x8 a[FM], b[FN];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        bf16x8 a[FM], b[FN];
+      for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)(st + ao[i][s2]);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          a[i] = *(const bf16x8*)&sX[buf][(wm * WM + i * 16 + fr) * LDSW + s * 32 + fk];
+      for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)(st + bo[j][s2]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          b[j] = *(const bf16x8*)&sW[buf][(wn * WN + j * 16 + fr) * LDSW + s * 32 + fk];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-      const int nx = (st + 1) % P;   // slot of tile kt + 1 (a constant once unrolled)
-      sstore(buf ^ 1, rx[nx], rw[nx]);
-      gload(kt + 1 + P, rx[nx], rw[nx]);
-      __syncthreads();
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
 
-  // D[i][j] of a 16x16 tile: lane holds column (lane & 15), rows 4*(lane>>4)+e
-  float* out = S.out + (int64_t)ks * S.out_kstride;
-  const int gate = S.gate;
+  // Output through LDS: the accumulators (lane holds column lane & 15, rows
+  // 4 (lane >> 4) + e of each 16 x 16 block) go to a row-major tile (rows
+  // padded to BN + 4 floats), then whole rows leave with 16-byte stores.
+  constexpr int OLD = BN + 4;
+  static_assert(BM * OLD * 4 <= S * STAGE, "output tile must fit the stages");
+  float* so = (float*)dyn_lds;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();   // every wave is done with the stages
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int n = n0 + wn * WN + j * 16 + fr;
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + e;
-        if (m < S.M && n < S.N) out[(int64_t)m * S.ldo + n] = apply_gate(acc[i][j][e], gate);
-      }
+      for (int e = 0; e < 4; ++e)
+        so[(wm * WM + i * 16 + fq * 4 + e) * OLD + wn * WN + j * 16 + fr] = acc[i][j][e];
+  __syncthreads();
+  float* out = S_.out + (int64_t)ks * S_.out_kstride;
+  const int gate = S_.gate;
+  for (int q = threadIdx.x; q < BM * BN / 4; q += kThreads) {
+    const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
+    const int m = m0 + r, n = n0 + c;
+    if (m < S_.M && n < S_.N) {   // N % 4 == 0: a group of 4 is all in or all out
+      f32x4 v = *(const f32x4*)&so[r * OLD + c];
+      if (gate)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = apply_gate(v[e], gate);
+      *(f32x4*)(out + (int64_t)m * S_.ldo + n) = v;
     }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
-                       const char* tag, hipStream_t stream) {
+// Raise the dynamic-LDS limit of a kernel once (idempotent; a race between
+// threads only repeats the call).
+static hipError_t allow_lds(const void* fn, int bytes, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done = true;
+  return e;
+}
+
+hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int stages,
+                       int waves, const char* tag, hipStream_t stream) {
   Problem P;
   int tiles = 0;
   P.nseg = 0;
+  if (nseg > kMaxSeg || K % BK != 0 || ksplit < 1 || ksplit > K / BK) return hipErrorInvalidValue;
   for (int i = 0; i < nseg; ++i) {
     if (segs[i].M <= 0) continue;
     GemmSeg s = segs[i];
+    // lane offsets are 32-bit and must be able to point past the data for
+    // the whole K walk; W tiles must not straddle w0 / w1
+    const uint64_t lim = (1ull << 32) - 16u - 2u * (uint64_t)K;
+    if ((uint64_t)s.x_rows * (uint64_t)s.ldx * 2u > lim) return hipErrorInvalidValue;
+    if ((uint64_t)s.N * (uint64_t)K * 2u > lim) return hipErrorInvalidValue;
+    if (s.n0 < s.N && s.n0 % BN != 0) return hipErrorInvalidValue;
     s.tiles_m = (s.M + bm - 1) / bm;
     s.tiles_n = (s.N + BN - 1) / BN;
     P.s[P.nseg] = s;
@@ -213,26 +274,26 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
   if (tiles == 0) return hipSuccess;
   P.K = K;
   P.ksplit = ksplit;
-  P.kslice = K / ksplit;
-  dim3 grid((unsigned)(tiles * ksplit)), block(kThreads);
+  dim3 grid((unsigned)(tiles * ksplit));
   ProfileScope ps(tag, stream);
-  // pipeline depth: the largest of 4, 5, 2, 1 that divides the K-tile count
-  const int nk = P.kslice / BK;
-  const int depth = nk % 4 == 0 ? 4 : nk % 5 == 0 ? 5 : nk % 2 == 0 ? 2 : 1;
-#define DF2_GEMM_LAUNCH(BMV, PV) gemm_kernel<BMV, PV><<<grid, block, 0, stream>>>(P)
-  if (bm == 128) {
-    if (depth == 4) DF2_GEMM_LAUNCH(128, 4);
-    else if (depth == 5) DF2_GEMM_LAUNCH(128, 5);
-    else if (depth == 2) DF2_GEMM_LAUNCH(128, 2);
-    else DF2_GEMM_LAUNCH(128, 1);
-  } else {
-    if (depth == 4) DF2_GEMM_LAUNCH(64, 4);
-    else if (depth == 5) DF2_GEMM_LAUNCH(64, 5);
-    else if (depth == 2) DF2_GEMM_LAUNCH(64, 2);
-    else DF2_GEMM_LAUNCH(64, 1);
-  }
+#define DF2_GEMM_LAUNCH(BMV, SV, NWV)                                                   \
+  do {                                                                                \
+    constexpr int kLds = SV * (BMV + BN) * BK * 2;                                    \
+    static bool done = false;                                                         \
+    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, SV, NWV>, kLds, done); \
+    if (e != hipSuccess) return e;                                                    \
+    gemm_dma_kernel<BMV, SV, NWV><<<grid, dim3(NWV * 64), kLds, stream>>>(P);         \
+    return hipGetLastError();                                                         \
+  } while (0)
+  if (bm == 128 && stages == 3 && waves == 4) DF2_GEMM_LAUNCH(128, 3, 4);
+  if (bm == 128 && stages == 4 && waves == 4) DF2_GEMM_LAUNCH(128, 4, 4);
+  if (bm == 128 && stages == 3 && waves == 8) DF2_GEMM_LAUNCH(128, 3, 8);
+  if (bm == 64 && stages == 3 && waves == 4) DF2_GEMM_LAUNCH(64, 3, 4);
+  if (bm == 64 && stages == 4 && waves == 4) DF2_GEMM_LAUNCH(64, 4, 4);
+  if (bm == 64 && stages == 3 && waves == 8) DF2_GEMM_LAUNCH(64, 3, 8);
+  if (bm == 64 && stages == 4 && waves == 8) DF2_GEMM_LAUNCH(64, 4, 8);
 #undef DF2_GEMM_LAUNCH
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace df2

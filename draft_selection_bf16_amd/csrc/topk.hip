@@ -22,10 +22,11 @@
 //    buffer, which is then cut back with a search over the value bits only
 //    (ballot popcounts on the scalar unit; ties kept) -- this raises the
 //    threshold to the 16th best value seen so far;
-//  * at the end the keys at or above the largest published threshold, a
-//    few dozen, are pooled, one wave selects the exact 16 best (64-bit
-//    search) and, with one chunk per row, rank-sorts and writes them;
-//    otherwise a second kernel merges the per-chunk lists of each row.
+//  * at the end each wave ranks its remaining keys (a few dozen) and keeps
+//    its 16 best, and one wave ranks those 8 x 16 (each key's rank is the
+//    number of larger keys: independent compares, no serial search); with
+//    one chunk per row it writes the result in order, otherwise a second
+//    kernel merges the per-chunk lists of each row.
 // (value, index) pairs are compared as single 64-bit keys (df2_device.h), so
 // the result does not depend on the order in which entries are seen.
 #include "df2_device.h"
@@ -186,37 +187,61 @@ __device__ __forceinline__ void refresh(Filter& F) {
   F.thr = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(t)));
 }
 
-// Expand the queued groups into keys, one group per lane and element by
-// element, keeping the entries that reach the threshold; then cut the
-// buffer back to at most about `keep` keys (raising the threshold to the
-// 16th best value seen so far).
+// Expand the queued groups into keys, one group per lane: each lane counts
+// the entries of its group that reach the threshold, a prefix over the
+// counts gives every lane its slots, and the keys are written in one go.
+// (When they would overflow the buffer, it is cut back first; if they still
+// would, the round goes element by element with a cut whenever needed.)
+// Then the buffer is cut back to at most about `keep` keys, which raises the
+// threshold to the 16th best value seen so far.
 template <typename E>
 __device__ __forceinline__ void flush(Filter& F, int wave, int keep) {
   constexpr int VB = Vec<E>::value_bits;
+  constexpr int VN = Vec<E>::n;
   const int lane = lane_id();
   for (int base = 0; base < F.qn; base += kWave) {
     const int s = base + lane;
     const bool valid = s < F.qn;
-    u32x4 v = F.q[valid ? s : 0];
-    uint32_t idx = F.qi[valid ? s : 0];
+    const u32x4 v = F.q[valid ? s : 0];
+    const uint32_t i0 = F.qi[valid ? s : 0];
     __builtin_amdgcn_wave_barrier();
+    float f[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) f[e] = Vec<E>::get(v, e);
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < VN; ++e) c += (valid && f[e] >= F.thr) ? 1 : 0;
+    int total;
+    int ex = lane_prefix16(c, total);
+    if (F.cnt + total > kCap) {
+      compact<VB>(F, wave);
+      c = 0;
+#pragma unroll
+      for (int e = 0; e < VN; ++e) c += (valid && f[e] >= F.thr) ? 1 : 0;
+      ex = lane_prefix16(c, total);
+    }
+    if (F.cnt + total <= kCap) {
+      int slot = F.cnt + ex;
+#pragma unroll
+      for (int e = 0; e < VN; ++e)
+        if (valid && f[e] >= F.thr) F.buf[slot++] = make_key(f[e], i0 + e);
+      F.cnt += total;
+      __builtin_amdgcn_wave_barrier();
+    } else {
 #pragma unroll 1
-    for (int e = 0; e < Vec<E>::n; ++e) {
-      const float f = Vec<E>::get0(v);
-      bool pass = valid && f >= F.thr;
-      uint64_t m = ballot(pass);
-      if (m != 0ull) {
+      for (int e = 0; e < VN; ++e) {
+        bool pass = valid && f[e] >= F.thr;
+        uint64_t m = ballot(pass);
+        if (m == 0ull) continue;
         if (F.cnt + __popcll(m) > kCap) {
           compact<VB>(F, wave);
-          pass = valid && f >= F.thr;
+          pass = valid && f[e] >= F.thr;
           m = ballot(pass);
         }
-        if (pass) F.buf[F.cnt + lanes_below(m)] = make_key(f, idx);
+        if (pass) F.buf[F.cnt + lanes_below(m)] = make_key(f[e], i0 + e);
         F.cnt += __popcll(m);
         __builtin_amdgcn_wave_barrier();
       }
-      v = Vec<E>::shift(v);
-      ++idx;
     }
   }
   F.qn = 0;
@@ -343,12 +368,11 @@ template <typename E>
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     const void* __restrict__ logits, int64_t vocab, int splits, int64_t chunk, int k,
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, uint64_t* __restrict__ part) {
-  __shared__ uint64_t sbuf[kWaves][kCap];
+  __shared__ __attribute__((aligned(16))) uint64_t sbuf[kWaves][kCap];
   __shared__ u32x4 squeue[kWaves][kQueue];
   __shared__ uint32_t sqidx[kWaves][kQueue];
-  __shared__ uint64_t smerge[kWaves * 16];
+  __shared__ __attribute__((aligned(16))) uint64_t smerge[kWaves * 16];
   __shared__ float sthr[kWaves];
-  __shared__ int scnt[kWaves];
   const int wave = wave_id(), lane = lane_id();
   const int64_t row = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -362,75 +386,48 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   Filter F{sbuf[wave], squeue[wave], sqidx[wave], sthr, 0, 0, -INFINITY};
   scan_range<E>(F, rowp, lo, hi, wave);
   flush<E>(F, wave, 16);
-  __syncthreads();
-  // Every entry dropped anywhere was below some published threshold, and
-  // the wave that published the largest one, T, holds >= 16 keys >= T: the
-  // keys >= T of all waves contain the 16 best of the chunk.
-  float T = sthr[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) T = fmaxf(T, sthr[w]);
-  {
-    uint64_t keys[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      int s = lane + i * kWave;
-      keys[i] = s < F.cnt ? F.buf[s] : 0ull;
-    }
+  // The 16 best keys of this wave: normally at most 64 keys are left, and
+  // each one's rank among them is its place; with many ties at the cut, an
+  // exact 64-bit search first.
+  uint64_t* mine16 = smerge + wave * 16;
+  if (lane < 16) mine16[lane] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  if (F.cnt <= kWave) {
+    const uint64_t key = lane < F.cnt ? F.buf[lane] : 0ull;
+    if (lane >= F.cnt) F.buf[lane] = 0ull;   // pad to 64 keys
     __builtin_amdgcn_wave_barrier();
-    const uint64_t tk = T == -INFINITY ? 0ull : (uint64_t)ord_of(T) << 32;
-    F.cnt = gather_at_least<kPer>(keys, tk, F.buf);
-    if (lane == 0) scnt[wave] = F.cnt;
-  }
-  __syncthreads();
-  int total = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) total += scnt[w];
-  if (total > kWave) {
-    // many ties at T: exact 16 best of each wave first
+    const int r = rank_in_lds<kWave>(key, F.buf);
+    if (key != 0ull && r < 16) mine16[r] = key;
+  } else {
     uint64_t keys[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      int s = lane + i * kWave;
-      keys[i] = s < F.cnt ? F.buf[s] : 0ull;
+      int s2 = lane + i * kWave;
+      keys[i] = s2 < F.cnt ? F.buf[s2] : 0ull;
     }
     __builtin_amdgcn_wave_barrier();
     const uint64_t t = kth16<kPer>(keys);
-    const int n = gather_at_least<kPer>(keys, t, F.buf);
-    __builtin_amdgcn_wave_barrier();
-    if (lane < 16) smerge[wave * 16 + lane] = lane < n ? F.buf[lane] : 0ull;
-    __syncthreads();
-    if (wave != 0) return;
-    constexpr int MP = kWaves * 16 / kWave;
-    uint64_t mk[MP];
-#pragma unroll
-    for (int i = 0; i < MP; ++i) mk[i] = smerge[lane + i * kWave];
-    const uint64_t tt = kth16<MP>(mk);
-    __builtin_amdgcn_wave_barrier();
-    total = gather_at_least<MP>(mk, tt, smerge);
-  } else {
-    if (wave != 0) return;
-    // lane l takes the l-th key of the concatenated per-wave lists
-    int w = 0, before = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves - 1; ++i)
-      if (lane >= before + scnt[w]) {
-        before += scnt[w];
-        ++w;
-      }
-    uint64_t mk[1] = {lane < total ? sbuf[w][lane - before] : 0ull};
-    const uint64_t tt = kth16<1>(mk);
-    __builtin_amdgcn_wave_barrier();
-    total = gather_at_least<1>(mk, tt, smerge);
+    gather_at_least<kPer>(keys, t, mine16);   // exactly 16 keys (all distinct)
   }
+  __syncthreads();
+  if (wave != 0) return;
+  // wave 0: the 16 best of the 8 x 16 candidates (two per lane), by rank
+  const uint64_t k0 = smerge[lane], k1 = smerge[kWave + lane];
+  const int r0 = rank_in_lds<kWaves * 16>(k0, smerge), r1 = rank_in_lds<kWaves * 16>(k1, smerge);
+  __shared__ uint64_t sbest[16];
+  if (lane < 16) sbest[lane] = 0ull;
+  __builtin_amdgcn_wave_barrier();
+  if (k0 != 0ull && r0 < 16) sbest[r0] = k0;
+  if (k1 != 0ull && r1 < 16) sbest[r1] = k1;
   __builtin_amdgcn_wave_barrier();
   if (splits == 1) {
-    const uint64_t mine = sorted16(smerge, total);
     if (lane < k) {
-      out_idx[row * k + lane] = (int32_t)key_index(mine);
-      out_val[row * k + lane] = key_value(mine);
+      const uint64_t key = sbest[lane];
+      out_idx[row * k + lane] = (int32_t)key_index(key);
+      out_val[row * k + lane] = key_value(key);
     }
   } else if (lane < 16) {
-    part[((int64_t)row * splits + split) * 16 + lane] = lane < total ? smerge[lane] : 0ull;
+    part[((int64_t)row * splits + split) * 16 + lane] = sbest[lane];
   }
 }
 

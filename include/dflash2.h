@@ -112,7 +112,8 @@ int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
  *   scores   [B, T, K, K] float  S[b,t,a,b']: a = predecessor rank (t >= 1)
  *            or 0 = last verified token (t = 0; rows a >= 1 of t = 0 are
  *            -inf), b' = candidate rank at t.
- * Limits: d % 64 == 0, 16 <= r <= 256, r % 16 == 0.  Token ids outside
+ * Limits: d % 64 == 0, 16 <= r <= 256, r % 16 == 0, and the embedding
+ * table under 4 GiB (vocab * d * 2 < 2^32; else DF2_ERR_UNSUPPORTED).  Token ids outside
  * [0, vocab) read a zero embedding.  Accumulation: fp32 (MFMA bf16 inputs).
  * ws layout (float, each part 256-byte aligned): AB [B*T*K, 2r] (A in
  * columns 0..r-1, B in r..2r-1), A_last [B, r], H [B*T, r].
