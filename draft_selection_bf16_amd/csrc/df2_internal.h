@@ -2,20 +2,45 @@
 // Internal; the C ABI (api.hip) validates arguments and calls these.
 #pragma once
 
+#include <hip/hip_ext.h>
+#include <tuple>
+#include <utility>
+
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace df2 {
 
-// Kernel timing hook: brackets launches of the armed kernel tag with events
-// on the launch stream (see dflash2_profile_start).
+// Kernel timing hook (see dflash2_profile_start): a scope names the kernel
+// tag of the launch it wraps; when that tag is armed and slots are left, the
+// launch records a start and a stop event in its dispatch (the kernel's own
+// duration, no stream-side overhead).
 struct ProfileScope {
   ProfileScope(const char* tag, hipStream_t stream);
-  ~ProfileScope();
   bool on;
-  hipStream_t stream;
+  hipEvent_t start, stop;
+  void used();   // the events of this scope were recorded
 };
+
+// Launch `k` with arguments converted to its exact parameter types; timed
+// through the scope's events when it is armed.
+template <typename... P, typename... A>
+inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, unsigned shmem, hipStream_t stream,
+                         ProfileScope& ps, A&&... a) {
+  std::tuple<P...> vals(std::forward<A>(a)...);
+  void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+  std::apply([&](auto&... x) {
+    int i = 0;
+    ((ptrs[i++] = (void*)&x), ...);
+  }, vals);
+  if (ps.on) {
+    hipError_t e = hipExtLaunchKernel((const void*)k, grid, block, ptrs, shmem, stream, ps.start, ps.stop, 0);
+    if (e == hipSuccess) ps.used();
+    return e;
+  }
+  return hipLaunchKernel((const void*)k, grid, block, ptrs, shmem, stream);
+}
 
 // Aligned sub-buffer carving of a caller workspace.
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }

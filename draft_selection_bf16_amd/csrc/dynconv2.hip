@@ -83,18 +83,18 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
 ConvPlan conv_plan(int B, int L, int d, int group) {
   (void)group;
   ConvPlan p;
-  // 64-row tiles in 3 LDS stages (72 KB): two work-groups per CU, which
-  // keeps the CU's L2-to-LDS path busy (one 4-wave group leaves it about
-  // 40% idle)
+  // 64-row tiles in 3 LDS stages (72 KB)
   p.bm = 64;
   p.stages = 3;
   p.waves = 4;
   const int M = B * L, N = 2 * (d / 16);
   const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
   const int nk = d / 64;
-  // K slices: about two work-groups per CU (<= 512), slices of >= 4 K-tiles
-  // and at most 16 slices (the epilogue's limit)
-  int ks = 512 / (tiles > 0 ? tiles : 1);
+  // K slices: about one work-group per CU (one round, balanced; measured
+  // better than two per CU, which doubles the partial sums the epilogue
+  // reads), slices of >= 4 K-tiles and at most 16 slices (the epilogue's
+  // limit)
+  int ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks > nk / 4) ks = nk / 4;
   if (ks > 16) ks = 16;
   if (ks < 1) ks = 1;
@@ -128,10 +128,10 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
   if (e != hipSuccess) return e;
   ProfileScope ps("conv_epilogue", stream);
   if (y_dt == 1)
-    conv_epilogue_kernel<true><<<dim3(M), dim3(kThreads), 0, stream>>>(
+    launch(conv_epilogue_kernel<true>, dim3(M), dim3(kThreads), 0, stream, ps,
         (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
   else
-    conv_epilogue_kernel<false><<<dim3(M), dim3(kThreads), 0, stream>>>(
+    launch(conv_epilogue_kernel<false>, dim3(M), dim3(kThreads), 0, stream, ps,
         (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
   return hipGetLastError();
 }
@@ -151,7 +151,8 @@ __global__ void philox_kernel(const uint64_t* __restrict__ seed_dev, const int32
 hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
                          uint64_t* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  philox_kernel<<<dim3((n + 255) / 256), dim3(256), 0, stream>>>(seed_dev, b, t, n, out);
+  ProfileScope ps("philox", stream);
+  launch(philox_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ps, seed_dev, b, t, n, out);
   return hipGetLastError();
 }
 

@@ -282,8 +282,7 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
     static bool done = false;                                                         \
     hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, SV, NWV>, kLds, done); \
     if (e != hipSuccess) return e;                                                    \
-    gemm_dma_kernel<BMV, SV, NWV><<<grid, dim3(NWV * 64), kLds, stream>>>(P);         \
-    return hipGetLastError();                                                         \
+    return launch(gemm_dma_kernel<BMV, SV, NWV>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
   } while (0)
   if (bm == 128 && stages == 3 && waves == 4) DF2_GEMM_LAUNCH(128, 3, 4);
   if (bm == 128 && stages == 4 && waves == 4) DF2_GEMM_LAUNCH(128, 4, 4);

@@ -1,6 +1,7 @@
 // profile.hip -- kernel timing hook of the C ABI (dflash2_profile_start /
-// dflash2_profile_stop): HIP events recorded on the launch stream around
-// each launch of one armed kernel tag.  Host code only.
+// dflash2_profile_stop): for each launch of one armed kernel tag, a start and
+// a stop event recorded by the kernel's dispatch itself (hipExtLaunchKernel),
+// i.e. the kernel's own execution interval.  Host code only.
 #include <string.h>
 
 #include <vector>
@@ -23,17 +24,16 @@ thread_local ProfState g_prof;
 
 namespace df2 {
 
-ProfileScope::ProfileScope(const char* tag, hipStream_t s) : on(false), stream(s) {
+ProfileScope::ProfileScope(const char* tag, hipStream_t s) : on(false), start(nullptr), stop(nullptr) {
+  (void)s;
   ProfState& P = g_prof;
-  if (!P.armed || P.n >= P.max || strcmp(tag, P.tag) != 0) return;
-  on = hipEventRecord(P.start[P.n], s) == hipSuccess;
+  if (!tag || !P.armed || P.n >= P.max || strcmp(tag, P.tag) != 0) return;
+  start = P.start[P.n];
+  stop = P.stop[P.n];
+  on = true;
 }
 
-ProfileScope::~ProfileScope() {
-  if (!on) return;
-  ProfState& P = g_prof;
-  if (hipEventRecord(P.stop[P.n], stream) == hipSuccess) P.n++;
-}
+void ProfileScope::used() { g_prof.n++; }
 
 }  // namespace df2
 

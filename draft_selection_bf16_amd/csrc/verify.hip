@@ -608,14 +608,14 @@ hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int3
   {
     ProfileScope ps("argmax_part", stream);
     if (dt == 0)
-      argmax_part_kernel<0><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+      launch(argmax_part_kernel<0>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
     else if (dt == 1)
-      argmax_part_kernel<1><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+      launch(argmax_part_kernel<1>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
     else
-      argmax_part_kernel<2><<<grid, block, 0, stream>>>(z, vocab, plan.splits, plan.chunk, part);
+      launch(argmax_part_kernel<2>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
   }
   ProfileScope ps("greedy_final", stream);
-  greedy_final_kernel<<<dim3(B), dim3(64), 0, stream>>>(part, plan.splits, T, path_tok, accept_len,
+  launch(greedy_final_kernel, dim3(B), dim3(64), 0, stream, ps, part, plan.splits, T, path_tok, accept_len,
                                                          out_tok);
   return hipGetLastError();
 }
@@ -631,22 +631,22 @@ static void reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
   float* rsum = (float*)((char*)ws + plan.off_rsum);
   {
     ProfileScope ps("sumexp_part", stream);
-    sumexp_part_kernel<DT><<<dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream>>>(
+    launch(sumexp_part_kernel<DT>, dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream, ps,
         z, vocab, plan.splits, plan.chunk, c, part);
   }
   {
     ProfileScope ps("reject_decide", stream);
-    reject_decide_kernel<DT><<<dim3(B), dim3(64), 0, stream>>>(z, vocab, part, plan.splits, T, K, c,
+    launch(reject_decide_kernel<DT>, dim3(B), dim3(64), 0, stream, ps, z, vocab, part, plan.splits, T, K, c,
                                                               path_tok, path_rank, q, seed_dev,
                                                               accept_len, out_tok, dec);
   }
   {
     ProfileScope ps("residual_chunk", stream);
-    residual_chunk_kernel<DT><<<dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream>>>(
+    launch(residual_chunk_kernel<DT>, dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream, ps,
         z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum);
   }
   ProfileScope ps("residual_find", stream);
-  residual_find_kernel<DT><<<dim3(B), dim3(kThreads), 0, stream>>>(
+  launch(residual_find_kernel<DT>, dim3(B), dim3(kThreads), 0, stream, ps,
       z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum, out_tok);
 }
 

@@ -220,11 +220,12 @@ int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t
 
 /* ------------------------------------------------------------------------
  * Kernel timing hook (host).  Arms this thread so that every later launch of
- * the kernel with tag `kernel` is bracketed by HIP events recorded on the
- * stream it is launched on (at most max_launches launches).  Tags:
+ * the kernel with tag `kernel` records a start and a stop HIP event in its
+ * own dispatch (hipExtLaunchKernel: the kernel's execution interval, without
+ * stream-side overhead), for at most max_launches launches.  Tags:
  *   "topk_chunk", "topk_merge", "project_gemm", "pair_epilogue", "path",
  *   "argmax_part", "greedy_final", "sumexp_part", "reject_decide",
- *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue".
+ *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue", "philox".
  * dflash2_profile_stop waits for the recorded events, writes up to `max`
  * per-launch durations in milliseconds to ms (host) and their count to *n,
  * and disarms.  Not for use during graph capture.  Events are created on
