@@ -109,9 +109,7 @@ namespace {
 // projection tiling: 128-row tiles in 4 stages (one 128 KB work-group per
 // CU); with the gathered embedding rows cold in cache (as in a decode
 // cycle) this beats two 64-row groups per CU, which re-read W twice as often
-int proj_bm() { return 128; }
-int proj_stages() { return 4; }
-int proj_waves() { return 4; }
+constexpr GemmTiling kProjTiling{128, 128, 4, 4};
 struct PairWs {
   size_t ab, alast, h, total;
 };
@@ -208,7 +206,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
     s[3].out = ab + r;
     nseg = 4;
   }
-  hipError_t e = launch_gemm(s, nseg, d, 1, proj_bm(), proj_stages(), proj_waves(), "project_gemm", stream);
+  hipError_t e = launch_gemm(s, nseg, d, 1, kProjTiling, "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores (epilogue)");

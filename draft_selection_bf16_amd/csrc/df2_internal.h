@@ -42,6 +42,13 @@ inline hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, unsigned shmem,
   return hipLaunchKernel((const void*)k, grid, block, ptrs, shmem, stream);
 }
 
+// Return a launch failure from the enclosing launcher.
+#define DF2_TRY(call)                     \
+  do {                                    \
+    const hipError_t df2_e_ = (call);     \
+    if (df2_e_ != hipSuccess) return df2_e_; \
+  } while (0)
+
 // Aligned sub-buffer carving of a caller workspace.
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -73,13 +80,17 @@ struct GemmSeg {
   int gate;               // 0 identity, 1 sigmoid (only when ksplit == 1)
   int tiles_m, tiles_n;   // filled by the launcher
 };
+// Work-group tile BM x BN, LDS stages, waves per work-group.
+struct GemmTiling {
+  int bm, bn, stages, waves;
+};
 // out = gate(X W^T) for up to 4 segments in one launch; K = d (multiple of 64).
-// Each segment needs n0 % 128 == 0 or n0 >= N, and x_rows * ldx * 2 < 2^32.
-// (bm, stages, waves) in {(128,3,4), (128,4,4), (128,3,8), (64,3,4), (64,4,4),
-// (64,3,8), (64,4,8)}; K % 64 == 0 and 1 <= ksplit <= K / 64 (slices of
-// K / 64 / ksplit K-tiles, rounded).
-hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int stages,
-                       int waves, const char* tag, hipStream_t stream);
+// Each segment needs n0 % bn == 0 or n0 >= N, and x_rows * ldx * 2 < 2^32.
+// (bm, bn, stages, waves) in {(128,128,3,4), (128,128,4,4), (128,128,3,8),
+// (64,128,3,4), (64,128,4,4), (64,128,3,8), (64,128,4,8)}; K % 64 == 0 and
+// 1 <= ksplit <= K / 64 (slices of K / 64 / ksplit K-tiles, rounded).
+hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const GemmTiling& t,
+                       const char* tag, hipStream_t stream);
 
 // ---- pair scores epilogue ---------------------------------------------------
 hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
@@ -115,10 +126,8 @@ hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int3
 // ---- two-tap dynamic conv ---------------------------------------------------
 struct ConvPlan {
   int ksplit;
-  int bm;
-  int stages;
-  int waves;
-  size_t ws_bytes;
+  GemmTiling tiling;
+  size_t ws_bytes;    // the slices' partial products
 };
 ConvPlan conv_plan(int B, int L, int d, int group);
 hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, const float* base,

@@ -10,7 +10,7 @@
 // Two launches per application:
 //  1. the tap corrections c = X W^T on the matrix cores (gemm.hip; M = B*L
 //     rows, N = 2G, K = d: a skinny product), with the reduction over d
-//     split into slices so that a few hundred work-groups share it; each
+//     split into slices so that about one work-group per CU shares it; each
 //     slice writes its own partial product;
 //  2. a streaming epilogue, one work-group per (b, t) row: sums the slice
 //     partials of its 2G taps in a fixed order into LDS, then reads x_t and
@@ -25,6 +25,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxTaps = 2048;   // 2G <= 2048  <=>  d <= 16384
 constexpr int kMaxSplit = 16;    // K slices of the tap GEMM
+constexpr int kCUs = 256;        // MI355X
 
 template <bool Y_BF16>
 __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
@@ -83,20 +84,21 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
 ConvPlan conv_plan(int B, int L, int d, int group) {
   (void)group;
   ConvPlan p;
-  // 64-row tiles in 3 LDS stages (72 KB)
-  p.bm = 64;
-  p.stages = 3;
-  p.waves = 4;
+  // 64 x 128 tiles in 3 LDS stages (72 KB)
+  p.tiling = GemmTiling{64, 128, 3, 4};
   const int M = B * L, N = 2 * (d / 16);
-  const int tiles = ((M + p.bm - 1) / p.bm) * ((N + 127) / 128);
+  const int tiles = ((M + 63) / 64) * ((N + 127) / 128);
   const int nk = d / 64;
-  // K slices: about one work-group per CU (one round, balanced; measured
-  // better than two per CU, which doubles the partial sums the epilogue
-  // reads), slices of >= 4 K-tiles and at most 16 slices (the epilogue's
-  // limit)
-  int ks = 256 / (tiles > 0 ? tiles : 1);
+  // K slices: about one work-group per CU (one balanced round; two per CU
+  // doubles the partial sums the epilogue reads), slices of >= 4 K-tiles and
+  // at most kMaxSplit slices (the epilogue's limit).  Measured at M = 512,
+  // d = 5120 in a replayed graph: 40 tiles x 6 slices 20.1 us per
+  // application; 64 x 160 tiles x 8 slices, whose slices line up with the
+  // XCDs (a quarter of the HBM fetch), 20.9 us: 1.3x the partial sums cost
+  // more than the saved fetch.
+  int ks = kCUs / (tiles > 0 ? tiles : 1);
   if (ks > nk / 4) ks = nk / 4;
-  if (ks > 16) ks = 16;
+  if (ks > kMaxSplit) ks = kMaxSplit;
   if (ks < 1) ks = 1;
   p.ksplit = ks;
   p.ws_bytes = align256((size_t)ks * (size_t)M * (size_t)N * sizeof(float));
@@ -124,15 +126,15 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
   s.ldo = N;
   s.out_kstride = (int64_t)M * N;
   s.gate = 0;
-  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.bm, plan.stages, plan.waves, "conv_gemm", stream);
+  hipError_t e = launch_gemm(&s, 1, d, plan.ksplit, plan.tiling, "conv_gemm", stream);
   if (e != hipSuccess) return e;
   ProfileScope ps("conv_epilogue", stream);
   if (y_dt == 1)
-    launch(conv_epilogue_kernel<true>, dim3(M), dim3(kThreads), 0, stream, ps,
-        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
+    DF2_TRY(launch(conv_epilogue_kernel<true>, dim3(M), dim3(kThreads), 0, stream, ps,
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y));
   else
-    launch(conv_epilogue_kernel<false>, dim3(M), dim3(kThreads), 0, stream, ps,
-        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y);
+    DF2_TRY(launch(conv_epilogue_kernel<false>, dim3(M), dim3(kThreads), 0, stream, ps,
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y));
   return hipGetLastError();
 }
 
@@ -152,7 +154,7 @@ hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32
                          uint64_t* out, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   ProfileScope ps("philox", stream);
-  launch(philox_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ps, seed_dev, b, t, n, out);
+  DF2_TRY(launch(philox_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, ps, seed_dev, b, t, n, out));
   return hipGetLastError();
 }
 

@@ -1,5 +1,4 @@
-// gemm.hip -- out = gate(X W^T) with bf16 operands on the gfx950 matrix
-// cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.
+// gemm.hip -- bf16 MFMA GEMM (out = gate(X W^T), fp32 accumulation).
 //
 // Used for the rank-r projections of the path selector (A(tok) = W_A E[tok],
 // B(tok) = W_B E[tok], H = gate(W_H h_t); "DFlash 2: Keep Drafting Parallel",
@@ -8,40 +7,43 @@
 // Both operands are K-contiguous rows (X: [M, K], W: [N, K]), so every lane
 // feeds the MFMA with 16 contiguous bytes of one row.
 //
-// Tiling: work-group = 4 or 8 waves (2 x 2 or 2 x 4), tile BM x 128 (BM = 64 or 128),
-// K-tiles of 64.  X rows may be gathered through an index list (candidate
-// tokens into the embedding table).  Up to four independent problems share
-// one launch.  An optional K split writes per-slice partial products (no
-// atomics; the consumer sums the slices in a fixed order).  Work-groups are
-// renumbered so that each XCD runs a contiguous range of tiles (the N-tiles
-// of one M-block then share that XCD's L2 for X), or, with a K split, so
-// that the slice index varies fastest.
-// The MFMA accumulators live in ordinary VGPRs (the file is compiled with
-// the VGPR form of the MFMA instructions), which keeps the accumulate chain
-// free of register copies.
+// Tiling: work-group = 4 or 8 waves (2 x 2 or 2 x 4), tile BM x BN (BM = 64
+// or 128; BN = 128 in the instantiations), K-tiles of 64.  X rows may be
+// gathered through an index list (candidate tokens into the embedding table).  Up to four independent
+// problems share one launch.  An optional K split writes per-slice partial
+// products (no atomics; the consumer sums the slices in a fixed order).
+// Work-groups are renumbered so that each XCD runs a contiguous range of
+// tiles (the N-tiles of one M-block then share that XCD's L2 for X), or,
+// with a K split, so that the slice index varies fastest.
+// This file is compiled with the VGPR form of the MFMA instructions: the
+// accumulators live in ordinary VGPRs, which keeps the accumulate chain free
+// of register copies.
 #include "df2_device.h"
 #include "df2_internal.h"
 
 namespace df2 {
 
-// dynamic LDS of the GEMM (declared outside the anonymous namespace: an
+// dynamic LDS of the GEMM (declared outside any anonymous namespace: an
 // extern with internal linkage keeps the host-side launch stub from being
 // emitted)
 extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
-namespace {
+namespace gemm {
 
-constexpr int BN = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int kXcds = 8;
 
 constexpr int kMaxSeg = 4;
 
+// The scalars every work-group needs first lead the kernel arguments, so
+// that one scalar load fetches them all (the segment's fields follow in a
+// second round trip, once the segment index is known).
 struct Problem {
-  GemmSeg s[kMaxSeg];
-  int tile_begin[kMaxSeg + 1];
-  int nseg;
-  int K;       // full reduction length; W rows are K apart
   int ksplit;  // slice s covers K-tiles [s nkt / ksplit, (s + 1) nkt / ksplit)
+  int K;       // full reduction length; W rows are K apart
+  int nseg;
+  int tile_begin[kMaxSeg + 1];   // entries from nseg on hold the tile total
+  GemmSeg s[kMaxSeg];
 };
 
 __device__ __forceinline__ float apply_gate(float z, int gate) {
@@ -52,7 +54,7 @@ __device__ __forceinline__ float apply_gate(float z, int gate) {
 // staging) into S LDS stages, S - 1 of them in flight while the MFMAs of the
 // current one run; one barrier per K-tile.
 //
-// LDS stage = X tile [BM][64] then W tile [128][64], rows of 128 bytes.  One
+// LDS stage = X tile [BM][64] then W tile [BN][64], rows of 128 bytes.  One
 // load instruction of a wave fills 1 KB = 8 rows: lane i writes the 16-byte
 // slot (row i / 8, slot i % 8) and fetches the chunk slot ^ swz(row) of that
 // row, so the 16-byte chunks of a row are stored in swizzled order.  The
@@ -76,9 +78,12 @@ __host__ __device__ constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
 }
 
-// NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8) over the tile.
-template <int BM, int S, int NW>
-__global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
+// The tile of work-group `bid` of a grid of `nb` (the body of the GEMM
+// kernel; NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8)).
+template <int BM, int BN, int S, int NW>
+__device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
+  static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
   constexpr int kThreads = NW * 64;
   constexpr int WCOL = NW / 2;                  // waves along N
   constexpr int WM = BM / 2, WN = BN / WCOL;
@@ -87,64 +92,82 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
   constexpr int LPW = ALD + BLD;
   constexpr int STAGE = (BM + BN) * BK * 2;     // bytes
 
-  const int nb = gridDim.x;
-  int bid = blockIdx.x;
-  int tile, ks;
-  if (Pb.ksplit == 1) {
-    const int full = nb / kXcds * kXcds;
-    if (bid < full) bid = (bid % kXcds) * (full / kXcds) + bid / kXcds;
-    tile = bid;
-    ks = 0;
-  } else {
-    tile = bid / Pb.ksplit;
-    ks = bid % Pb.ksplit;
-  }
-  int si = 0;
-  while (si + 1 < Pb.nseg && tile >= Pb.tile_begin[si + 1]) ++si;
+  // Every kernel-argument scalar is read up front and every choice below is
+  // a select, not a branch: the scalar loads then go out together instead
+  // of one dependent round trip each.
+  const int ksplit = Pb.ksplit, K = Pb.K;
+  const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
+  asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
+  const int full = nb / kXcds * kXcds;
+  const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
+  const int tile = ksplit == 1 ? bx : bid / ksplit;
+  const int ks = ksplit == 1 ? 0 : bid % ksplit;
+  // tile_begin[i] for i >= nseg is the tile total
+  const int si = (tile >= tb1 ? 1 : 0) + (tile >= tb2 ? 1 : 0) + (tile >= tb3 ? 1 : 0);
+  static_assert(kMaxSeg == 4, "segment index select");
   const GemmSeg& S_ = Pb.s[si];
-  const int local = tile - Pb.tile_begin[si];
-  const int m0 = (local / S_.tiles_n) * BM, n0 = (local % S_.tiles_n) * BN;
-  const int nkt = Pb.K / BK;
-  const int kt0 = ks * nkt / Pb.ksplit, kt1 = (ks + 1) * nkt / Pb.ksplit;
+  const uint16_t* sx = S_.x;
+  const int32_t* sgather = S_.gather;
+  const int x_rows = S_.x_rows, ldx = S_.ldx, M = S_.M, N = S_.N, sn0 = S_.n0;
+  const uint16_t *w0 = S_.w0, *w1 = S_.w1;
+  const int tiles_n = S_.tiles_n;
+  float* const sout = S_.out;
+  const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
+  const int gate = S_.gate;
+  const int tbegin = Pb.tile_begin[si];
+  asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
+               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate),
+               "s"(tbegin));   // one round trip
+  const int local = tile - tbegin;
+  const int m0 = (local / tiles_n) * BM, n0 = (local % tiles_n) * BN;
+  const int nkt = K / BK;
+  const int kt0 = ks * nkt / ksplit, kt1 = (ks + 1) * nkt / ksplit;
   const int k_begin = kt0 * BK;
   const int nk = kt1 - kt0;
   const int wave = wave_id(), lane = lane_id();
   const int wm = wave / WCOL, wn = wave % WCOL;
 
-  const bool from_w0 = n0 < S_.n0;
-  const uint16_t* wbase = from_w0 ? S_.w0 + (int64_t)n0 * Pb.K : S_.w1 + (int64_t)(n0 - S_.n0) * Pb.K;
-  const int wrows = (from_w0 ? (S_.n0 < S_.N ? S_.n0 : S_.N) : S_.N) - n0;
-  const uint32_t xbytes = (uint32_t)(S_.x_rows * S_.ldx * 2);
-  const uint32_t wbytes = (uint32_t)((int64_t)wrows * Pb.K * 2);
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)S_.x, 0, (int)xbytes, kBufferWord3);
+  const bool from_w0 = n0 < sn0;
+  const uint16_t* wbase = from_w0 ? w0 + (int64_t)n0 * K : w1 + (int64_t)(n0 - sn0) * K;
+  const int wrows = (from_w0 ? (sn0 < N ? sn0 : N) : N) - n0;
+  const uint32_t xbytes = (uint32_t)(x_rows * ldx * 2);
+  const uint32_t wbytes = (uint32_t)((int64_t)wrows * K * 2);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)sx, 0, (int)xbytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, (int)wbytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t xnone = __builtin_amdgcn_make_buffer_rsrc((void*)S_.x, 0, 0, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t xnone = __builtin_amdgcn_make_buffer_rsrc((void*)sx, 0, 0, kBufferWord3);
   const __amdgpu_buffer_rsrc_t wnone = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, 0, kBufferWord3);
   // out of range for the whole K walk, whether or not the range check adds
   // the scalar offset (the launcher keeps bytes + 2K + 16 <= 2^32)
-  const uint32_t kOut = 0xFFFFFFF0u - (uint32_t)Pb.K * 2u;
+  const uint32_t kOut = 0xFFFFFFF0u - (uint32_t)K * 2u;
 
   // lane offsets of this wave's load instructions: instruction a fills rows
-  // 8 (wave + NW a) .. + 7 of the X tile, b likewise of the W tile
+  // 8 (wave + NW a) .. + 7 of the X tile, b likewise of the W tile.  X rows
+  // come through the gather list when there is one: its entries are loaded
+  // unconditionally (clamped row) so that all of them are in flight at once.
   const int sub = lane >> 3, slot = lane & 7;
   uint32_t xo[ALD], wo[BLD];
+  int src[ALD];
+#pragma unroll
+  for (int a = 0; a < ALD; ++a) {
+    const int m = m0 + 8 * (wave + NW * a) + sub;
+    src[a] = m < M ? m : M - 1;
+  }
+  if (sgather) {
+#pragma unroll
+    for (int a = 0; a < ALD; ++a) src[a] = sgather[src[a]];
+  }
 #pragma unroll
   for (int a = 0; a < ALD; ++a) {
     const int row = 8 * (wave + NW * a) + sub;
     const int c = slot ^ swz(row);
-    const int m = m0 + row;
-    int64_t src = -1;
-    if (m < S_.M) {
-      src = S_.gather ? (int64_t)S_.gather[m] : (int64_t)m;
-      if (src < 0 || src >= S_.x_rows) src = -1;
-    }
-    xo[a] = src < 0 ? kOut : (uint32_t)((src * S_.ldx + k_begin + c * 8) * 2);
+    const bool ok = m0 + row < M && src[a] >= 0 && src[a] < x_rows;
+    xo[a] = ok ? (uint32_t)(((int64_t)src[a] * ldx + k_begin + c * 8) * 2) : kOut;
   }
 #pragma unroll
   for (int b = 0; b < BLD; ++b) {
     const int row = 8 * (wave + NW * b) + sub;
     const int c = slot ^ swz(row);
-    wo[b] = row < wrows ? (uint32_t)(((int64_t)row * Pb.K + k_begin + c * 8) * 2) : kOut;
+    wo[b] = row < wrows ? (uint32_t)(((int64_t)row * K + k_begin + c * 8) * 2) : kOut;
   }
   // K-tile t goes to stage t % S; tiles past the end read nothing (empty
   // resources: zeros, no traffic) so that every step issues the same loads
@@ -222,36 +245,52 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
       for (int e = 0; e < 4; ++e)
         so[(wm * WM + i * 16 + fq * 4 + e) * OLD + wn * WN + j * 16 + fr] = acc[i][j][e];
   __syncthreads();
-  float* out = S_.out + (int64_t)ks * S_.out_kstride;
-  const int gate = S_.gate;
+  float* out = sout + (int64_t)ks * out_kstride;
   for (int q = threadIdx.x; q < BM * BN / 4; q += kThreads) {
     const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
     const int m = m0 + r, n = n0 + c;
-    if (m < S_.M && n < S_.N) {   // N % 4 == 0: a group of 4 is all in or all out
+    if (m < M && n < N) {   // N % 4 == 0: a group of 4 is all in or all out
       f32x4 v = *(const f32x4*)&so[r * OLD + c];
       if (gate)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = apply_gate(v[e], gate);
-      *(f32x4*)(out + (int64_t)m * S_.ldo + n) = v;
+      *(f32x4*)(out + (int64_t)m * ldo + n) = v;
     }
   }
+}
+
+// Fill P for up to kMaxSeg problems (hipErrorInvalidValue for shapes the
+// kernel does not take), and raise a kernel's dynamic-LDS limit once.
+hipError_t make_problem(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int bn, Problem& P,
+                        int& tiles);
+hipError_t allow_lds(const void* fn, int bytes, bool& done);
+
+}  // namespace gemm
+}  // namespace df2
+
+namespace df2 {
+using namespace gemm;
+namespace {
+
+template <int BM, int BN, int S, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
+  run_tile<BM, BN, S, NW>(Pb, blockIdx.x, gridDim.x);
 }
 
 }  // namespace
 
 // Raise the dynamic-LDS limit of a kernel once (idempotent; a race between
 // threads only repeats the call).
-static hipError_t allow_lds(const void* fn, int bytes, bool& done) {
+hipError_t gemm::allow_lds(const void* fn, int bytes, bool& done) {
   if (done) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e == hipSuccess) done = true;
   return e;
 }
 
-hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int stages,
-                       int waves, const char* tag, hipStream_t stream) {
-  Problem P;
-  int tiles = 0;
+hipError_t gemm::make_problem(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int bn,
+                              Problem& P, int& tiles) {
+  tiles = 0;
   P.nseg = 0;
   if (nseg > kMaxSeg || K % BK != 0 || ksplit < 1 || ksplit > K / BK) return hipErrorInvalidValue;
   for (int i = 0; i < nseg; ++i) {
@@ -262,35 +301,44 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, int bm,
     const uint64_t lim = (1ull << 32) - 16u - 2u * (uint64_t)K;
     if ((uint64_t)s.x_rows * (uint64_t)s.ldx * 2u > lim) return hipErrorInvalidValue;
     if ((uint64_t)s.N * (uint64_t)K * 2u > lim) return hipErrorInvalidValue;
-    if (s.n0 < s.N && s.n0 % BN != 0) return hipErrorInvalidValue;
+    if (s.n0 < s.N && s.n0 % bn != 0) return hipErrorInvalidValue;
     s.tiles_m = (s.M + bm - 1) / bm;
-    s.tiles_n = (s.N + BN - 1) / BN;
+    s.tiles_n = (s.N + bn - 1) / bn;
     P.s[P.nseg] = s;
     P.tile_begin[P.nseg] = tiles;
     tiles += s.tiles_m * s.tiles_n;
     P.nseg++;
   }
-  P.tile_begin[P.nseg] = tiles;
-  if (tiles == 0) return hipSuccess;
+  for (int i = P.nseg; i <= kMaxSeg; ++i) P.tile_begin[i] = tiles;
   P.K = K;
   P.ksplit = ksplit;
+  return hipSuccess;
+}
+
+hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const GemmTiling& t,
+                       const char* tag, hipStream_t stream) {
+  Problem P;
+  int tiles = 0;
+  hipError_t pe = make_problem(segs, nseg, K, ksplit, t.bm, t.bn, P, tiles);
+  if (pe != hipSuccess) return pe;
+  if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)(tiles * ksplit));
   ProfileScope ps(tag, stream);
-#define DF2_GEMM_LAUNCH(BMV, SV, NWV)                                                   \
-  do {                                                                                \
-    constexpr int kLds = SV * (BMV + BN) * BK * 2;                                    \
-    static bool done = false;                                                         \
-    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, SV, NWV>, kLds, done); \
-    if (e != hipSuccess) return e;                                                    \
-    return launch(gemm_dma_kernel<BMV, SV, NWV>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
-  } while (0)
-  if (bm == 128 && stages == 3 && waves == 4) DF2_GEMM_LAUNCH(128, 3, 4);
-  if (bm == 128 && stages == 4 && waves == 4) DF2_GEMM_LAUNCH(128, 4, 4);
-  if (bm == 128 && stages == 3 && waves == 8) DF2_GEMM_LAUNCH(128, 3, 8);
-  if (bm == 64 && stages == 3 && waves == 4) DF2_GEMM_LAUNCH(64, 3, 4);
-  if (bm == 64 && stages == 4 && waves == 4) DF2_GEMM_LAUNCH(64, 4, 4);
-  if (bm == 64 && stages == 3 && waves == 8) DF2_GEMM_LAUNCH(64, 3, 8);
-  if (bm == 64 && stages == 4 && waves == 8) DF2_GEMM_LAUNCH(64, 4, 8);
+#define DF2_GEMM_LAUNCH(BMV, BNV, SV, NWV)                                                      \
+  if (t.bm == BMV && t.bn == BNV && t.stages == SV && t.waves == NWV) {                         \
+    constexpr int kLds = SV * (BMV + BNV) * BK * 2;                                             \
+    static bool done = false;                                                                   \
+    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, BNV, SV, NWV>, kLds, done);      \
+    if (e != hipSuccess) return e;                                                              \
+    return launch(gemm_dma_kernel<BMV, BNV, SV, NWV>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
+  }
+  DF2_GEMM_LAUNCH(128, 128, 3, 4)
+  DF2_GEMM_LAUNCH(128, 128, 4, 4)
+  DF2_GEMM_LAUNCH(128, 128, 3, 8)
+  DF2_GEMM_LAUNCH(64, 128, 3, 4)
+  DF2_GEMM_LAUNCH(64, 128, 4, 4)
+  DF2_GEMM_LAUNCH(64, 128, 3, 8)
+  DF2_GEMM_LAUNCH(64, 128, 4, 8)
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
 }

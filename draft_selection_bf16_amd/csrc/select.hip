@@ -249,8 +249,8 @@ hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const floa
                                 hipStream_t stream) {
   if (B * T == 0) return hipSuccess;
   ProfileScope ps("pair_epilogue", stream);
-  launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, hgate, cand_val, T, K, r,
-                                                                scores);
+  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, hgate, cand_val, T, K, r,
+                                                                scores));
   return hipGetLastError();
 }
 
@@ -260,8 +260,8 @@ hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int 
   if (B == 0) return hipSuccess;
   float inv_tau = mode == 2 ? 1.0f / temperature : 0.f;
   ProfileScope ps("path", stream);
-  launch(path_kernel, dim3(B), dim3(64), 0, stream, ps, scores, cand_idx, T, K, mode, inv_tau, seed_dev,
-                                                path_rank, path_tok, q, path_score);
+  DF2_TRY(launch(path_kernel, dim3(B), dim3(64), 0, stream, ps, scores, cand_idx, T, K, mode, inv_tau, seed_dev,
+                                                path_rank, path_tok, q, path_score));
   return hipGetLastError();
 }
 

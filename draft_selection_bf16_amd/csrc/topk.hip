@@ -490,19 +490,19 @@ hipError_t launch_topk(const void* logits, int dt, int64_t rows, int64_t vocab, 
   {
     ProfileScope ps("topk_chunk", stream);
     if (dt == 0)
-      launch(topk_chunk_kernel<float>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
-                                                           out_idx, out_val, part);
+      DF2_TRY(launch(topk_chunk_kernel<float>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                           out_idx, out_val, part));
     else if (dt == 1)
-      launch(topk_chunk_kernel<Bf16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
-                                                          out_idx, out_val, part);
+      DF2_TRY(launch(topk_chunk_kernel<Bf16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                          out_idx, out_val, part));
     else
-      launch(topk_chunk_kernel<F16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
-                                                         out_idx, out_val, part);
+      DF2_TRY(launch(topk_chunk_kernel<F16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                         out_idx, out_val, part));
   }
   if (plan.splits > 1) {
     ProfileScope ps("topk_merge", stream);
     dim3 g2((unsigned)((rows + kWaves - 1) / kWaves));
-    launch(topk_merge_kernel, g2, block, 0, stream, ps, part, rows, plan.splits, k, out_idx, out_val);
+    DF2_TRY(launch(topk_merge_kernel, g2, block, 0, stream, ps, part, rows, plan.splits, k, out_idx, out_val));
   }
   return hipGetLastError();
 }

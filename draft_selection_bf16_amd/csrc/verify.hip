@@ -608,20 +608,20 @@ hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int3
   {
     ProfileScope ps("argmax_part", stream);
     if (dt == 0)
-      launch(argmax_part_kernel<0>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
+      DF2_TRY(launch(argmax_part_kernel<0>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part));
     else if (dt == 1)
-      launch(argmax_part_kernel<1>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
+      DF2_TRY(launch(argmax_part_kernel<1>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part));
     else
-      launch(argmax_part_kernel<2>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part);
+      DF2_TRY(launch(argmax_part_kernel<2>, grid, block, 0, stream, ps, z, vocab, plan.splits, plan.chunk, part));
   }
   ProfileScope ps("greedy_final", stream);
-  launch(greedy_final_kernel, dim3(B), dim3(64), 0, stream, ps, part, plan.splits, T, path_tok, accept_len,
-                                                         out_tok);
+  DF2_TRY(launch(greedy_final_kernel, dim3(B), dim3(64), 0, stream, ps, part, plan.splits, T, path_tok, accept_len,
+                                                         out_tok));
   return hipGetLastError();
 }
 
 template <int DT>
-static void reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
+static hipError_t reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
                           const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
                           int T, int K, float c, const uint64_t* seed_dev, int32_t* accept_len,
                           int32_t* out_tok, void* ws, const VerifyPlan& plan, hipStream_t stream) {
@@ -631,23 +631,24 @@ static void reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
   float* rsum = (float*)((char*)ws + plan.off_rsum);
   {
     ProfileScope ps("sumexp_part", stream);
-    launch(sumexp_part_kernel<DT>, dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream, ps,
-        z, vocab, plan.splits, plan.chunk, c, part);
+    DF2_TRY(launch(sumexp_part_kernel<DT>, dim3((unsigned)(rows * plan.splits)), dim3(kThreads), 0, stream, ps,
+        z, vocab, plan.splits, plan.chunk, c, part));
   }
   {
     ProfileScope ps("reject_decide", stream);
-    launch(reject_decide_kernel<DT>, dim3(B), dim3(64), 0, stream, ps, z, vocab, part, plan.splits, T, K, c,
+    DF2_TRY(launch(reject_decide_kernel<DT>, dim3(B), dim3(64), 0, stream, ps, z, vocab, part, plan.splits, T, K, c,
                                                               path_tok, path_rank, q, seed_dev,
-                                                              accept_len, out_tok, dec);
+                                                              accept_len, out_tok, dec));
   }
   {
     ProfileScope ps("residual_chunk", stream);
-    launch(residual_chunk_kernel<DT>, dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream, ps,
-        z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum);
+    DF2_TRY(launch(residual_chunk_kernel<DT>, dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream, ps,
+        z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum));
   }
   ProfileScope ps("residual_find", stream);
-  launch(residual_find_kernel<DT>, dim3(B), dim3(kThreads), 0, stream, ps,
-      z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum, out_tok);
+  DF2_TRY(launch(residual_find_kernel<DT>, dim3(B), dim3(kThreads), 0, stream, ps,
+      z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum, out_tok));
+  return hipSuccess;
 }
 
 hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
@@ -658,15 +659,13 @@ hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int3
   if (B == 0) return hipSuccess;
   const float c = kLog2e / temperature;
   if (dt == 0)
-    reject_launch<0>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
-                     out_tok, ws, plan, stream);
-  else if (dt == 1)
-    reject_launch<1>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
-                     out_tok, ws, plan, stream);
-  else
-    reject_launch<2>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
-                     out_tok, ws, plan, stream);
-  return hipGetLastError();
+    return reject_launch<0>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                            out_tok, ws, plan, stream);
+  if (dt == 1)
+    return reject_launch<1>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                            out_tok, ws, plan, stream);
+  return reject_launch<2>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+                          out_tok, ws, plan, stream);
 }
 
 }  // namespace df2
