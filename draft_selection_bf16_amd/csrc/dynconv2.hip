@@ -13,9 +13,9 @@
 //     split into slices so that about one work-group per CU shares it; each
 //     slice writes its own partial product;
 //  2. a streaming epilogue, one work-group per (b, t) row: sums the slice
-//     partials of its 2G taps in a fixed order into LDS, then reads x_t and
-//     x_{t-1} with 16-byte loads and writes y (bf16 round-to-nearest-even, or
-//     fp32).
+//     partials of its 2G taps in a fixed order into LDS and combines them
+//     with x_t and x_{t-1} (16-byte loads, issued together with the partial
+//     loads) into y (bf16 round-to-nearest-even, or fp32).
 #include "df2_device.h"
 #include "df2_internal.h"
 
@@ -27,42 +27,86 @@ constexpr int kMaxTaps = 2048;   // 2G <= 2048  <=>  d <= 16384
 constexpr int kMaxSplit = 16;    // K slices of the tap GEMM
 constexpr int kCUs = 256;        // MI355X
 
+constexpr int kChunks = 3;       // 16-byte x chunks per thread kept in flight (d <= 6144)
+
+// One work-group per (b, t) row.  Everything the row needs is requested
+// before the first wait: the thread's x_t / x_{t-1} chunks, and, for
+// threads < 2G/4, four taps' partial products of every slice (16-byte
+// loads).  The taps are summed over the slices in a fixed order into LDS;
+// after one barrier every thread writes its chunks of y.  Rows are spread so
+// that consecutive rows run on one XCD (work-group i on XCD i mod 8), where
+// x_{t-1} is the previous row's x_t, already in that XCD's L2.
 template <bool Y_BF16>
 __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ x_prev,
     const float* __restrict__ base, const float* __restrict__ part, int ksplit, int64_t kstride,
     int L, int d, void* __restrict__ y) {
-  __shared__ float sc[kMaxTaps];
-  const int row = blockIdx.x;          // b * L + t
+  __shared__ __attribute__((aligned(16))) float sc[kMaxTaps];
+  const int nb = gridDim.x, full = nb / 8 * 8;
+  const int bid = blockIdx.x;
+  const int row = bid < full ? (bid % 8) * (full / 8) + bid / 8 : bid;   // b * L + t
   const int b = row / L, t = row % L;
-  const int G = d / 16, NT = 2 * G;
-  for (int n = threadIdx.x; n < NT; n += kThreads) {
-    const float* p = part + (int64_t)row * NT + n;
-    float v[kMaxSplit];
-#pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) v[s] = s < ksplit ? p[(int64_t)s * kstride] : 0.f;
-    float acc = 0.f;
-#pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) acc += v[s];   // slices in a fixed order
-    sc[n] = acc;
-  }
-  __syncthreads();
+  const int G = d / 16, NT = 2 * G, nch = d / 8;
+  const int tid = threadIdx.x;
   const uint16_t* xt = x + (int64_t)row * d;
   const uint16_t* xp = t > 0 ? x + (int64_t)(row - 1) * d : (x_prev ? x_prev + (int64_t)b * d : nullptr);
-  // 8 channels per 16-byte load; channel groups of 16 never straddle a load
-  for (int c8 = threadIdx.x; c8 < d / 8; c8 += kThreads) {
+  u32x4 vx[kChunks], vp[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int c8 = tid + kThreads * i;
+    const int cc = c8 < nch ? c8 : nch - 1;   // clamped: loaded, not used
+    vx[i] = *(const u32x4*)(xt + cc * 8);
+    vp[i] = xp ? *(const u32x4*)(xp + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int n4 = tid; n4 < NT / 4; n4 += kThreads) {
+    const float* p = part + (int64_t)row * NT + n4 * 4;
+    // slices in a fixed order, in blocks of 8 loads in flight (a slice past
+    // ksplit reloads slice 0 and is not added)
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ksplit; s0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = *(const f32x4*)(p + (int64_t)(s0 + u < ksplit ? s0 + u : 0) * kstride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < ksplit) acc += v[u];
+    }
+    *(f32x4*)(sc + n4 * 4) = acc;
+  }
+  __syncthreads();
+  // 8 channels per 16-byte chunk; channel groups of 16 never straddle one
+  for (int c8 = tid; c8 < nch; c8 += kThreads) {
+    const int i = c8 / kThreads;   // the same for the whole work-group
+    u32x4 ax = {0u, 0u, 0u, 0u}, ap = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < kChunks; ++q)
+      if (q == i) {
+        ax = vx[q];
+        ap = vp[q];
+      }
+    if (i >= kChunks) {
+      ax = *(const u32x4*)(xt + c8 * 8);
+      ap = xp ? *(const u32x4*)(xp + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
     const int ch0 = c8 * 8, g = ch0 / 16;
-    const u32x4 vx = *(const u32x4*)(xt + ch0);
-    const u32x4 vp = xp ? *(const u32x4*)(xp + ch0) : u32x4{0u, 0u, 0u, 0u};
     const float c0 = sc[g], c1 = sc[G + g];
+    // base kernels: four 16-byte loads under one uniform branch
+    f32x4 b0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, b1[2] = {b0[0], b0[0]};
+    if (base) {
+      b0[0] = *(const f32x4*)(base + ch0);
+      b0[1] = *(const f32x4*)(base + ch0 + 4);
+      b1[0] = *(const f32x4*)(base + d + ch0);
+      b1[1] = *(const f32x4*)(base + d + ch0 + 4);
+    }
     float out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t wx = vx[e >> 1], wp = vp[e >> 1];
+      const uint32_t wx = ax[e >> 1], wp = ap[e >> 1];
       const float fx = (e & 1) ? bf16_hi(wx) : bf16_lo(wx);
       const float fp = (e & 1) ? bf16_hi(wp) : bf16_lo(wp);
-      const float k0 = base ? base[ch0 + e] + c0 : c0;
-      const float k1 = base ? base[d + ch0 + e] + c1 : c1;
+      const float k0 = base ? b0[e >> 2][e & 3] + c0 : c0;
+      const float k1 = base ? b1[e >> 2][e & 3] + c1 : c1;
       out[e] = fmaf(k0, fx, k1 * fp);
     }
     if (Y_BF16) {
