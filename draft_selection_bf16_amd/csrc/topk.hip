@@ -318,16 +318,21 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
     }
   }
   const int ng = (int)ngroups;   // < 2^31: rows hold < 2^32 entries
-  for (int g0 = wave * kWave; g0 < ng; g0 += (int)stride * kUnroll) {
-    if (F.qn > kQueueFlush) flush<E>(F, wave, 32);
-    u32x4 v[kUnroll];
-    bool ok[kUnroll];
+  // Software-pipelined over two register sets: the loads of the next
+  // iteration are issued before this one's groups are tested (no register
+  // copy, which would wait for the loads), so two iterations' loads (8 KB
+  // per wave) are in flight.
+  const int step = (int)stride * kUnroll;
+  auto load = [&](int g0, u32x4 (&v)[kUnroll], bool (&ok)[kUnroll]) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int g = g0 + u * (int)stride + lane;
       ok[u] = g < ng;
       v[u] = __builtin_nontemporal_load(vp + (ok[u] ? g : 0));
     }
+  };
+  auto process = [&](int g0, const u32x4 (&v)[kUnroll], const bool (&ok)[kUnroll]) {
+    if (F.qn > kQueueFlush) flush<E>(F, wave, 32);
     // the threshold is the same in all lanes: decide the test once per
     // iteration, on the scalar unit
     const float thr = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(F.thr)));
@@ -359,6 +364,19 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
       __builtin_amdgcn_wave_barrier();
     }
     refresh(F);
+  };
+  u32x4 va[kUnroll], vb[kUnroll];
+  bool oka[kUnroll], okb[kUnroll];
+  int g0 = wave * kWave;
+  if (g0 < ng) load(g0, va, oka);
+  while (g0 < ng) {   // the same in all lanes
+    if (g0 + step < ng) load(g0 + step, vb, okb);
+    process(g0, va, oka);
+    g0 += step;
+    if (g0 >= ng) break;
+    if (g0 + step < ng) load(g0 + step, va, oka);
+    process(g0, vb, okb);
+    g0 += step;
   }
 }
 
@@ -385,41 +403,139 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   __syncthreads();
   Filter F{sbuf[wave], squeue[wave], sqidx[wave], sthr, 0, 0, -INFINITY};
   scan_range<E>(F, rowp, lo, hi, wave);
-  flush<E>(F, wave, 16);
-  // The 16 best keys of this wave: normally at most 64 keys are left, and
-  // each one's rank among them is its place; with many ties at the cut, an
-  // exact 64-bit search first.
-  uint64_t* mine16 = smerge + wave * 16;
-  if (lane < 16) mine16[lane] = 0ull;
-  __builtin_amdgcn_wave_barrier();
-  if (F.cnt <= kWave) {
-    const uint64_t key = lane < F.cnt ? F.buf[lane] : 0ull;
-    if (lane >= F.cnt) F.buf[lane] = 0ull;   // pad to 64 keys
-    __builtin_amdgcn_wave_barrier();
-    const int r = rank_in_lds<kWave>(key, F.buf);
-    if (key != 0ull && r < 16) mine16[r] = key;
-  } else {
-    uint64_t keys[kPer];
+  // Keep up to 64 keys per wave (no final cut), then filter every wave's
+  // keys by two lower bounds on the chunk's 16th best key: the largest
+  // published threshold (a value some wave saw at least 16 keys reach) and
+  // the smallest of the waves' second-best keys (the waves' best and second
+  // best are 16 distinct keys).  The 16 best all pass; a few dozen keys
+  // survive at V = 151,936.  Survivors are ranked against each other by all
+  // threads.  With massive ties (more than 512 survivors) every wave first
+  // takes its own 16 best and wave 0 merges the 8 x 16.
+  flush<E>(F, wave, kWave);
+  if (lane == 0) publish(F, wave);
+  __shared__ __attribute__((aligned(16))) uint64_t ssurv[kThreads + 16];
+  __shared__ int srank[kThreads];
+  __shared__ int snsurv;
+  __shared__ uint64_t sbest[16];
+  __shared__ uint64_t s2nd[kWaves];
+  uint64_t keys[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int s2 = lane + i * kWave;
+    keys[i] = s2 < F.cnt ? F.buf[s2] : 0ull;
+  }
+  {
+    uint64_t m1 = 0ull;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) m1 = keys[i] > m1 ? keys[i] : m1;
+    m1 = wave_max_u64(m1);
+    uint64_t m2 = 0ull;   // keys are distinct: only m1 itself is excluded
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) m2 = (keys[i] != m1 && keys[i] > m2) ? keys[i] : m2;
+    m2 = wave_max_u64(m2);
+    if (lane == 0) s2nd[wave] = m2;
+  }
+  if (threadIdx.x == 0) snsurv = 0;
+  if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;
+  __syncthreads();
+  {
+    float g = -INFINITY;
+    uint64_t kb = ~0ull;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      g = fmaxf(g, __hip_atomic_load(F.share + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+      kb = s2nd[w] < kb ? s2nd[w] : kb;
+    }
+    const uint32_t go = ord_of(g);
+    bool keep[kPer];
+    int n = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
-      int s2 = lane + i * kWave;
-      keys[i] = s2 < F.cnt ? F.buf[s2] : 0ull;
+      keep[i] = keys[i] != 0ull && (uint32_t)(keys[i] >> 32) >= go && keys[i] >= kb;
+      n += __popcll(ballot(keep[i]));
     }
-    __builtin_amdgcn_wave_barrier();
-    const uint64_t t = kth16<kPer>(keys);
-    gather_at_least<kPer>(keys, t, mine16);   // exactly 16 keys (all distinct)
+    int base = 0;
+    if (lane == 0 && n > 0) base = atomicAdd(&snsurv, n);
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (base + n <= kThreads) {
+      int off = base;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const uint64_t m = ballot(keep[i]);
+        if (keep[i]) ssurv[off + lanes_below(m)] = keys[i];
+        off += __popcll(m);
+      }
+    }
   }
   __syncthreads();
-  if (wave != 0) return;
-  // wave 0: the 16 best of the 8 x 16 candidates (two per lane), by rank
-  const uint64_t k0 = smerge[lane], k1 = smerge[kWave + lane];
-  const int r0 = rank_in_lds<kWaves * 16>(k0, smerge), r1 = rank_in_lds<kWaves * 16>(k1, smerge);
-  __shared__ uint64_t sbest[16];
-  if (lane < 16) sbest[lane] = 0ull;
-  __builtin_amdgcn_wave_barrier();
-  if (k0 != 0ull && r0 < 16) sbest[r0] = k0;
-  if (k1 != 0ull && r1 < 16) sbest[r1] = k1;
-  __builtin_amdgcn_wave_barrier();
+  const int ns = snsurv;   // the same in every wave
+  if (ns <= kThreads) {
+    // rank = number of larger survivors (keys are distinct).  The list is
+    // padded with empty keys to a multiple of 16; P = 512 / n16 threads share
+    // a survivor, each counting the larger keys in its 1/P of the list (two
+    // keys per LDS load, eight loads in flight), the counts meeting in LDS.
+    const int tid = threadIdx.x;
+    const int n16 = (ns + 15) & ~15;
+    if (tid < n16 - ns) ssurv[ns + tid] = 0ull;
+    srank[tid] = 0;
+    __syncthreads();
+    const int P = n16 > 0 ? kThreads / n16 : 1;   // >= 1
+    const int len = n16 / P > 16 ? ((n16 / P) + 15) & ~15 : 16;   // parts past n16 count nothing
+    const int part = tid / (n16 > 0 ? n16 : 1), i = tid - part * n16;
+    uint64_t key = 0ull;
+    if (part < P && i < ns) {
+      key = ssurv[i];
+      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+      const int j1 = (part + 1) * len < n16 ? (part + 1) * len : n16;
+      int c = 0;
+      for (int j = part * len; j < j1; j += 16) {
+        u64x2 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = *(const u64x2*)(ssurv + j + 2 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += (o[u][0] > key ? 1 : 0) + (o[u][1] > key ? 1 : 0);
+      }
+      if (c > 0) atomicAdd(&srank[i], c);
+    }
+    __syncthreads();
+    key = tid < ns ? ssurv[tid] : 0ull;
+    const int r = tid < ns ? srank[tid] : kThreads;
+    if (key != 0ull && r < 16) sbest[r] = key;
+    __syncthreads();
+    if (wave != 0) return;
+  } else {
+    // The 16 best keys of this wave: normally at most 64 keys are left, and
+    // each one's rank among them is its place; with many ties at the cut, an
+    // exact 64-bit search first.
+    uint64_t* mine16 = smerge + wave * 16;
+    if (lane < 16) mine16[lane] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    if (F.cnt <= kWave) {
+      const uint64_t key = lane < F.cnt ? F.buf[lane] : 0ull;
+      if (lane >= F.cnt) F.buf[lane] = 0ull;   // pad to 64 keys
+      __builtin_amdgcn_wave_barrier();
+      const int r = rank_in_lds<kWave>(key, F.buf);
+      if (key != 0ull && r < 16) mine16[r] = key;
+    } else {
+      uint64_t keys[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        int s2 = lane + i * kWave;
+        keys[i] = s2 < F.cnt ? F.buf[s2] : 0ull;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t t = kth16<kPer>(keys);
+      gather_at_least<kPer>(keys, t, mine16);   // exactly 16 keys (all distinct)
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // wave 0: the 16 best of the 8 x 16 candidates (two per lane), by rank
+    const uint64_t k0 = smerge[lane], k1 = smerge[kWave + lane];
+    const int r0 = rank_in_lds<kWaves * 16>(k0, smerge), r1 = rank_in_lds<kWaves * 16>(k1, smerge);
+    if (k0 != 0ull && r0 < 16) sbest[r0] = k0;
+    if (k1 != 0ull && r1 < 16) sbest[r1] = k1;
+    __builtin_amdgcn_wave_barrier();
+  }
   if (splits == 1) {
     if (lane < k) {
       const uint64_t key = sbest[lane];
