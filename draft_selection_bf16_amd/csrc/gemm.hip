@@ -57,12 +57,14 @@ __device__ __forceinline__ float apply_gate(float z, int gate) {
 // LDS stage = X tile [BM][64] then W tile [BN][64], rows of 128 bytes.  One
 // load instruction of a wave fills 1 KB = 8 rows: lane i writes the 16-byte
 // slot (row i / 8, slot i % 8) and fetches the chunk slot ^ swz(row) of that
-// row, so the 16-byte chunks of a row are stored in swizzled order.  The
-// MFMA fragment reads (16 rows, one chunk each) then hit 16 distinct
-// 16-byte bank groups.  Rows outside the problem get an out-of-range lane
-// offset: the hardware writes zeros for them.
+// row, so the 16-byte chunks of a row are stored in swizzled order.  With
+// chunk c of row r stored at c ^ (r mod 8), the MFMA fragment reads (16
+// consecutive rows, one chunk each) are free of bank conflicts: 4 LDS cycles
+// per 16-byte read of a wave, measured with the bank-conflict counter (an
+// extra ^ (r / 8 mod 2) term doubles it to 8).  Rows outside the problem get
+// an out-of-range lane offset: the hardware writes zeros for them.
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // One direct buffer-to-LDS load of 16 bytes per lane (a plain device
 // function: called from the kernel template directly, the builtin keeps the
