@@ -91,6 +91,21 @@ def time_graph(cyc, steps, warmup):
     return a.elapsed_time(b) / steps, wall
 
 
+def replay_spread(cyc, n):
+    """Median and 90th percentile of single replays (events around each
+    replay; outside the timed region)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        cyc.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return dict(median=round(ms[n // 2], 5), p90=round(ms[min(n - 1, (9 * n) // 10)], 5), n=n)
+
+
 def profile_kernels(cyc, steps):
     """Per-launch durations of each kernel tag over `steps` eager cycles."""
     import torch
@@ -269,6 +284,7 @@ def main():
     log("timing the full cycle")
     ms, wall = time_graph(cyc, args.steps, args.warmup)
     value = w.B / (ms / 1e3)
+    spread = replay_spread(cyc, min(args.steps, 100))
 
     # the same cycle without the conv sites (top-K + select + verify only)
     cyc_nc, _ = build_cycle(w, dev, E=E, conv=False)
@@ -329,6 +345,7 @@ def main():
                    "step": "20 x dynconv2 + topk + pair_scores + path + verify, one HIP graph"},
         "tokens_scored_per_s": round(w.B * w.T * w.K / (ms / 1e3), 1),
         "value_without_conv": round(w.B / (ms_nc / 1e3), 1),
+        "replay_ms": spread,
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
