@@ -106,10 +106,11 @@ int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
 
 // ------------------------------------------------------------------ pair scores
 namespace {
-// projection tiling: 128-row tiles in 4 stages (one 128 KB work-group per
-// CU); with the gathered embedding rows cold in cache (as in a decode
-// cycle) this beats two 64-row groups per CU, which re-read W twice as often
-constexpr GemmTiling kProjTiling{128, 128, 4, 4};
+// projection tiling: 128-row tiles, one work-group per CU, 8 waves (two per
+// SIMD) over 3 LDS stages.  In the batch-32 / block-16 cycle (replayed
+// graph, top-K + pair scores + path + verify): 142.1 us against 144.7 us
+// with 4 waves over 4 stages and 143.9-145.2 us with 64-row tiles.
+constexpr GemmTiling kProjTiling{128, 128, 3, 8};
 struct PairWs {
   size_t ab, alast, h, total;
 };
