@@ -111,27 +111,46 @@ namespace {
 // graph, top-K + pair scores + path + verify): 142.1 us against 144.7 us
 // with 4 waves over 4 stages and 143.9-145.2 us with 64-row tiles.
 constexpr GemmTiling kProjTiling{128, 128, 3, 8};
+// The projection's K split: with few tiles (small batches) the reduction
+// over d is split so that up to about one work-group per CU takes part
+// (slices of >= 4 K-tiles, at most 8: the pair epilogue, which adds the
+// slices in a fixed order and gates H, loads all of them at once).
+int proj_split(int B, int T, int K, int d, int r) {
+  const int bm = kProjTiling.bm, bn = kProjTiling.bn;
+  auto tl = [&](int m, int n) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
+  const int mc = B * T * K;
+  const int tiles = (r % bn == 0 ? tl(mc, 2 * r) : 2 * tl(mc, r)) + tl(B, r) + tl(B * T, r);
+  int ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks > d / 64 / 4) ks = d / 64 / 4;
+  if (ks > 8) ks = 8;
+  return ks < 1 ? 1 : ks;
+}
 struct PairWs {
-  size_t ab, alast, h, total;
+  int split;
+  size_t ab, alast, h, total;       // per-slice sizes are [rows, cols] fp32
+  size_t ab_k, alast_k, h_k;        // floats between slices
 };
-PairWs pair_ws(int B, int T, int K, int r) {
+PairWs pair_ws(int B, int T, int K, int d, int r) {
   PairWs w;
+  w.split = proj_split(B, T, K, d, r);
+  w.ab_k = (size_t)B * T * K * 2 * r;
+  w.alast_k = (size_t)B * r;
+  w.h_k = (size_t)B * T * r;
   size_t off = 0;
   w.ab = off;
-  off += align256((size_t)B * T * K * 2 * r * sizeof(float));
+  off += align256(w.split * w.ab_k * sizeof(float));
   w.alast = off;
-  off += align256((size_t)B * r * sizeof(float));
+  off += align256(w.split * w.alast_k * sizeof(float));
   w.h = off;
-  off += align256((size_t)B * T * r * sizeof(float));
+  off += align256(w.split * w.h_k * sizeof(float));
   w.total = off;
   return w;
 }
 }  // namespace
 
 size_t dflash2_pair_scores_workspace_bytes(int B, int T, int K, int d, int r) {
-  (void)d;
-  if (B <= 0 || T <= 0 || K <= 0 || r <= 0) return 0;
-  return pair_ws(B, T, K, r).total;
+  if (B <= 0 || T <= 0 || K <= 0 || r <= 0 || d < 64) return 0;
+  return pair_ws(B, T, K, d, r).total;
 }
 
 int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
@@ -153,7 +172,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
           "dflash2_pair_scores: null pointer argument");
   REQUIRE(aligned16(emb) && aligned16(h) && aligned16(w_a) && aligned16(w_b) && aligned16(w_h),
           DF2_ERR_SHAPE, "dflash2_pair_scores: emb/h/w_* must be 16-byte aligned");
-  PairWs pw = pair_ws(B, T, K, r);
+  PairWs pw = pair_ws(B, T, K, d, r);
   REQUIRE(ws && ws_bytes >= pw.total, DF2_ERR_WORKSPACE, "dflash2_pair_scores: workspace %zu < %zu bytes",
           ws_bytes, pw.total);
   float* ab = (float*)((char*)ws + pw.ab);
@@ -172,6 +191,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[0].N = 2 * r;
   s[0].out = ab;
   s[0].ldo = 2 * r;
+  s[0].out_kstride = (int64_t)pw.ab_k;
   s[0].gate = DF2_GATE_IDENTITY;
   // last verified tokens: A only
   s[1] = s[0];
@@ -181,7 +201,8 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[1].N = r;
   s[1].out = alast;
   s[1].ldo = r;
-  // gate: H = gate(h W_H^T)
+  s[1].out_kstride = (int64_t)pw.alast_k;
+  // gate: H = gate(h W_H^T), the gate applied by the epilogue
   s[2].x = (const uint16_t*)h;
   s[2].gather = nullptr;
   s[2].x_rows = (int64_t)B * T;
@@ -193,7 +214,8 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[2].N = r;
   s[2].out = hg;
   s[2].ldo = r;
-  s[2].gate = gate;
+  s[2].out_kstride = (int64_t)pw.h_k;
+  s[2].gate = DF2_GATE_IDENTITY;
   // W tiles are 128 rows and may not straddle W_A / W_B: for r not a
   // multiple of 128 the candidate rows are projected as two problems
   int nseg = 3;
@@ -207,9 +229,10 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
     s[3].out = ab + r;
     nseg = 4;
   }
-  hipError_t e = launch_gemm(s, nseg, d, 1, kProjTiling, "project_gemm", stream);
+  hipError_t e = launch_gemm(s, nseg, d, pw.split, kProjTiling, "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
-  return hip_status(launch_pair_epilogue(ab, alast, hg, cand_val, B, T, K, r, scores, stream),
+  return hip_status(launch_pair_epilogue(ab, alast, hg, pw.split, (int64_t)pw.ab_k, (int64_t)pw.alast_k,
+                                         (int64_t)pw.h_k, gate, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores (epilogue)");
 }
 

@@ -93,7 +93,10 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
                        const char* tag, hipStream_t stream);
 
 // ---- pair scores epilogue ---------------------------------------------------
-hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
+// ab, a_last, h: `split` (1..8) slices of partial products, kstrides floats apart
+// (added in slice order); h ungated (the gate is applied after the sum).
+hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* h, int split,
+                                int64_t ab_k, int64_t alast_k, int64_t h_k, int gate,
                                 const float* cand_val, int B, int T, int K, int r,
                                 float* scores, hipStream_t stream);
 

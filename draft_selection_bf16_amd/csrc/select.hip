@@ -25,9 +25,26 @@ namespace {
 constexpr int kMaxR = 256;
 constexpr int kMaxLattice = 63 * 16 * 16;   // T <= 63, K <= 16
 
+// The sum of the `split` (<= 8) slices of partial products at p (k floats
+// apart), in slice order; the 8 loads go out together (a slice past `split`
+// reloads slice 0 and is not added).
+constexpr int kMaxProjSplit = 8;
+__device__ __forceinline__ f32x4 slice_sum4(const float* p, int split, int64_t k) {
+  f32x4 v[kMaxProjSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxProjSplit; ++s) v[s] = *(const f32x4*)(p + (s < split ? s : 0) * k);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < kMaxProjSplit; ++s)
+    if (s < split) acc += v[s];
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
-                                                            const float* __restrict__ hgate,
+                                                            const float* __restrict__ h_part,
+                                                            int split, int64_t ab_k, int64_t alast_k,
+                                                            int64_t h_k, int gate,
                                                             const float* __restrict__ cand_val,
                                                             int T, int K, int r,
                                                             float* __restrict__ scores) {
@@ -40,7 +57,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
   const int tid = threadIdx.x;
   const int npred = t == 0 ? 1 : K;
   const int r4 = r / 4;
-  const f32x4* H4 = (const f32x4*)(hgate + (int64_t)bt * r);
+  const float* Hp = h_part + (int64_t)bt * r;
   // each thread stages up to 4 float4 of G and 4 of B (16 rows x 64 float4)
   f32x4 ga[4], gb[4];
   int gi[4], gq[4];
@@ -54,14 +71,20 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     if (gi[u] < npred) {
       const float* src = t == 0 ? a_last + (int64_t)b * r
                                 : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
-      ga[u] = *(const f32x4*)(src + 4 * gq[u]);
+      ga[u] = slice_sum4(src + 4 * gq[u], split, t == 0 ? alast_k : ab_k);
     }
-    if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
+    if (gi[u] < K) gb[u] = slice_sum4(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u], split, ab_k);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (gi[u] < 16) {
-      f32x4 h = gi[u] < npred ? H4[gq[u]] : f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 h = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (gi[u] < npred) {
+        h = slice_sum4(Hp + 4 * gq[u], split, h_k);
+        if (gate == 1)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) h[e] = 1.0f / (1.0f + expf(-h[e]));
+      }
       *(f32x4*)&sG[gi[u] * kLd + 4 * gq[u]] = ga[u] * h;
       *(f32x4*)&sB[gi[u] * kLd + 4 * gq[u]] = gb[u];
     }
@@ -244,13 +267,14 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
 
 }  // namespace
 
-hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* hgate,
+hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* h, int split,
+                                int64_t ab_k, int64_t alast_k, int64_t h_k, int gate,
                                 const float* cand_val, int B, int T, int K, int r, float* scores,
                                 hipStream_t stream) {
   if (B * T == 0) return hipSuccess;
   ProfileScope ps("pair_epilogue", stream);
-  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, hgate, cand_val, T, K, r,
-                                                                scores));
+  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, split, ab_k,
+                 alast_k, h_k, gate, cand_val, T, K, r, scores));
   return hipGetLastError();
 }
 

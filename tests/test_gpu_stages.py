@@ -177,16 +177,30 @@ def _pair_gpu(cand_idx, cand_val, last, E, h, wa, wb, wh, gate=0):
     return S.cpu().numpy(), w
 
 
-def _ws_views(w, B, T, K, r):
+def _ws_views(w, B, T, K, r, gate=0):
+    """The projection's results in the pair-scores workspace: [A|B] of the
+    candidates, A of the last tokens and H, each stored as S slices of
+    partial products over the hidden size (S found from the workspace size),
+    summed here in slice order; H is stored before its gate."""
     def a256(n):
         return (n + 255) // 256 * 256
+    n_ab, n_al, n_h = B * T * K * 2 * r, B * r, B * T * r
+    nbytes = w.numel()
+    S = next(s for s in range(1, 9) if a256(s * n_ab * 4) + a256(s * n_al * 4) + a256(s * n_h * 4) == nbytes)
     f = w.view(torch.float32)
-    n_ab = B * T * K * 2 * r
-    off_al = a256(n_ab * 4) // 4
-    off_h = off_al + a256(B * r * 4) // 4
-    ab = f[:n_ab].view(B, T, K, 2 * r).cpu().numpy()
-    al = f[off_al:off_al + B * r].view(B, r).cpu().numpy()
-    hg = f[off_h:off_h + B * T * r].view(B, T, r).cpu().numpy()
+    off_al = a256(S * n_ab * 4) // 4
+    off_h = off_al + a256(S * n_al * 4) // 4
+
+    def summed(off, n):
+        acc = f[off:off + n].clone()
+        for k in range(1, S):
+            acc += f[off + k * n:off + (k + 1) * n]
+        return acc.cpu().numpy()
+    ab = summed(0, n_ab).reshape(B, T, K, 2 * r)
+    al = summed(off_al, n_al).reshape(B, r)
+    hg = summed(off_h, n_h).reshape(B, T, r)
+    if gate == 1:
+        hg = 1.0 / (1.0 + np.exp(-hg))
     return ab, al, hg
 
 
@@ -203,19 +217,21 @@ def test_pair_scores_tiny(gate):
     close(Sg, So)
 
 
-def test_pair_scores_mid_with_intermediates():
+@pytest.mark.parametrize("gate", [0, 1])
+def test_pair_scores_mid_with_intermediates(gate):
     """B=3, T=7, K=16, V=4096, d=512, r=256: several GEMM tiles, a ragged
-    M tail (3*7*16 = 336 rows), gathered rows."""
+    M tail (3*7*16 = 336 rows), gathered rows, the projection split over d
+    into slices (few tiles), the gate applied after the slices are added."""
     w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=3, V=4096, d=512)
     z, _, _ = synth.drafter_logits(w)
     idx, val = oracle.topk(z, 16)
     E = synth.embeddings(w)
     wa, wb, wh = synth.selector_weights(w)
     h, last = synth.context_hidden(w), synth.last_tokens(w)
-    Sg, wsp = _pair_gpu(torch.from_numpy(idx), torch.from_numpy(val), last, E, h, wa, wb, wh)
-    So, inter = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, intermediates=True)
+    Sg, wsp = _pair_gpu(torch.from_numpy(idx), torch.from_numpy(val), last, E, h, wa, wb, wh, gate)
+    So, inter = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, gate=gate, intermediates=True)
     worst = close(Sg, So)
-    ab, al, hg = _ws_views(wsp, 3, 7, 16, 256)
+    ab, al, hg = _ws_views(wsp, 3, 7, 16, 256, gate)
     close(ab[..., :256], inter["a_cand"])
     close(ab[..., 256:], inter["b_cand"])
     close(al, inter["a_last"])
