@@ -547,16 +547,23 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
   }
 }
 
-// one wave per row: merge splits * 16 keys (splits <= 32)
+// One wave per row: merge splits * 16 keys (splits <= 32), each split's 16
+// best-first (empty slots 0).  Two lower bounds on the row's 16th best key:
+// the largest of the splits' 16th keys (that split holds 16 keys at least
+// as large), and with >= 16 splits the 16th largest of their heads (16
+// distinct keys at least as large).  The keys that reach both are few; they
+// are ranked against each other by broadcast LDS compares.  More than 64
+// of them (ties at the cut) falls back to the exact 64-bit search.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ part,
                                                               int64_t rows, int splits, int k,
                                                               int32_t* __restrict__ out_idx,
                                                               float* __restrict__ out_val) {
   constexpr int PER = 8;
   __shared__ uint64_t sel[kWaves][16];
+  __shared__ __attribute__((aligned(16))) uint64_t ssv[kWaves][kWave];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if (row >= rows) return;
+  if (row >= rows) return;   // the same in the whole wave; no work-group barrier below
   const int n = splits * 16;
   uint64_t keys[PER];
 #pragma unroll
@@ -564,10 +571,59 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
     int s = lane + i * kWave;
     keys[i] = s < n ? part[row * n + s] : 0ull;
   }
-  const uint64_t t = kth16<PER>(keys);
-  const int m = gather_at_least<PER>(keys, t, sel[wave]);
-  __builtin_amdgcn_wave_barrier();
-  const uint64_t mine = sorted16(sel[wave], m);
+  uint64_t b1 = 0ull;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = lane + i * kWave;
+    if (s < n && (s & 15) == 15 && keys[i] > b1) b1 = keys[i];
+  }
+  b1 = wave_max_u64(b1);
+  uint64_t b2 = 0ull;
+  if (splits >= 16) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int s = lane + i * kWave;
+      if (s < n && (s & 15) == 0) ssv[wave][s >> 4] = keys[i];
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t hk = lane < splits ? ssv[wave][lane] : 0ull;
+    int rk = 0;
+    for (int l = 0; l < splits; ++l) rk += ssv[wave][l] > hk ? 1 : 0;
+    const uint64_t m = ballot(lane < splits && hk != 0ull && rk == 15);
+    if (m) b2 = shfl_u64(hk, __ffsll((unsigned long long)m) - 1);
+    __builtin_amdgcn_wave_barrier();
+  }
+  const uint64_t bound = b1 > b2 ? b1 : b2;
+  bool keep[PER];
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    keep[i] = keys[i] != 0ull && keys[i] >= bound;
+    cnt += __popcll(ballot(keep[i]));
+  }
+  uint64_t mine;
+  if (cnt <= kWave) {
+    if (lane < 16) sel[wave][lane] = 0ull;
+    int off = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint64_t m = ballot(keep[i]);
+      if (keep[i]) ssv[wave][off + lanes_below(m)] = keys[i];
+      off += __popcll(m);
+    }
+    if (lane >= cnt) ssv[wave][lane] = 0ull;   // pad to 64 keys
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t key = ssv[wave][lane];
+    const int r = rank_in_lds<kWave>(key, ssv[wave]);
+    if (key != 0ull && r < 16) sel[wave][r] = key;
+    __builtin_amdgcn_wave_barrier();
+    mine = lane < 16 ? sel[wave][lane] : 0ull;
+  } else {
+    const uint64_t t = kth16<PER>(keys);
+    const int m = gather_at_least<PER>(keys, t, sel[wave]);
+    __builtin_amdgcn_wave_barrier();
+    mine = sorted16(sel[wave], m);
+  }
   if (lane < k) {
     out_idx[row * k + lane] = (int32_t)key_index(mine);
     out_val[row * k + lane] = key_value(mine);

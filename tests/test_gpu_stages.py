@@ -85,6 +85,26 @@ def test_topk_ties_and_signed_zero():
     _check_topk(z, 16)
 
 
+def test_topk_merge_many_survivors_falls_back_exactly():
+    """Few rows, so every row is split into 15 chunks and the per-chunk
+    lists are merged.  Each chunk holds the same 16 large values, so every
+    chunk's 16th best has the same value and about 15 x 16 keys reach the
+    merge's lower bound: the exact fallback has to pick the 16 best (equal
+    values: lowest index first)."""
+    V = 15 * 8192
+    g = torch.Generator().manual_seed(21)
+    z = torch.randn(2, V, generator=g)
+    top = 10.0 + 0.0625 * torch.arange(16, dtype=torch.float32)   # exact in bf16
+    for c in range(15):
+        pos = c * 8192 + torch.randperm(8192, generator=g)[:16]
+        z[0, pos] = top
+        z[1, pos] = top.flip(0)
+    z = z.to(torch.bfloat16)
+    gi, gv = _topk_gpu(dev(z), 16)
+    oi, ov = oracle.topk(z.float(), 16)
+    assert np.array_equal(gi, oi) and np.array_equal(gv, ov)
+
+
 def test_topk_fp16():
     g = torch.Generator().manual_seed(2)
     z = (3 * torch.randn(4, 32771, generator=g)).to(torch.float16)
