@@ -489,7 +489,8 @@ __global__ __launch_bounds__(kThreads) void residual_find_kernel(
   __shared__ const void* srow;
   __shared__ float s_target;
   __shared__ int s_chunk;
-  __shared__ float sscan[kThreads];
+  __shared__ float swsum[kWaves];
+  __shared__ int shit[kWaves], snz[kWaves];
   const int b = blockIdx.x, tid = threadIdx.x;
   const DecRec d = dec[b];
   if (tid < kWave) {  // wave 0: prefix over chunk sums (rchunks <= 64)
@@ -534,37 +535,60 @@ __global__ __launch_bounds__(kThreads) void residual_find_kernel(
   const int64_t t0 = lo + tid * per, t1 = t0 + per < hi ? t0 + per : hi;
   float mine = 0.f;
   for (int64_t v = t0; v < t1; ++v) mine += R.w(Elt<DT>::one(srow, v), v);
-  sscan[tid] = mine;
-  __syncthreads();
-  if (tid == 0) {  // sequential prefix over the 256 thread sums
-    float run = 0.f;
-    int hit = -1, last_nz = -1;
-    for (int i = 0; i < kThreads; ++i) {
-      float nx = run + sscan[i];
-      if (sscan[i] > 0.f) last_nz = i;
-      if (hit < 0 && nx > s_target) hit = i;
-      if (hit < 0) run = nx;
-    }
-    int tsel = hit >= 0 ? hit : last_nz;
-    int y = -1;
-    if (tsel >= 0) {
-      const int64_t s0 = lo + tsel * per, s1 = s0 + per < hi ? s0 + per : hi;
-      float acc = hit >= 0 ? run : 0.f;
-      int64_t lastv = -1;
-      for (int64_t v = s0; v < s1; ++v) {
-        float wv = R.w(Elt<DT>::one(srow, v), v);
-        if (wv > 0.f) lastv = v;
-        acc += wv;
-        if (hit >= 0 && acc > s_target) {
-          y = (int)v;
-          break;
-        }
-      }
-      if (y < 0) y = (int)lastv;
-    }
-    if (y < 0) y = d.argmax;
-    out_tok[(int64_t)b * (T + 1) + d.n] = y;
+  // prefix over the thread sums: a wave scan, then the earlier waves'
+  // totals added in wave order
+  const int lane = lane_id(), wave = tid / kWave;
+  float incl = mine;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) {
+    const float o = __shfl_up(incl, m);
+    if (lane >= m) incl += o;
   }
+  float excl = __shfl_up(incl, 1);
+  if (lane == 0) excl = 0.f;
+  if (lane == kWave - 1) swsum[wave] = incl;
+  __syncthreads();
+  float pre = 0.f;
+  for (int w = 0; w < wave; ++w) pre += swsum[w];
+  incl += pre;
+  excl += pre;
+  // the first thread whose range takes the running sum past the target,
+  // else the last thread with residual mass
+  const uint64_t over = ballot(incl > s_target), nz = ballot(mine > 0.f);
+  if (lane == 0) {
+    shit[wave] = over ? wave * kWave + __ffsll((unsigned long long)over) - 1 : kThreads;
+    snz[wave] = nz ? wave * kWave + 63 - __clzll((unsigned long long)nz) : -1;
+  }
+  __syncthreads();
+  int hit = kThreads, last_nz = -1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    hit = shit[w] < hit ? shit[w] : hit;
+    last_nz = snz[w] > last_nz ? snz[w] : last_nz;
+  }
+  const bool found = hit < kThreads;
+  const int tsel = found ? hit : last_nz;
+  if (tsel < 0) {
+    if (tid == 0) out_tok[(int64_t)b * (T + 1) + d.n] = d.argmax;
+    return;
+  }
+  if (tid != tsel) return;
+  // the selected thread walks its own range in index order
+  int y = -1;
+  float acc = found ? excl : 0.f;
+  int64_t lastv = -1;
+  for (int64_t v = t0; v < t1; ++v) {
+    const float wv = R.w(Elt<DT>::one(srow, v), v);
+    if (wv > 0.f) lastv = v;
+    acc += wv;
+    if (found && acc > s_target) {
+      y = (int)v;
+      break;
+    }
+  }
+  if (y < 0) y = (int)lastv;
+  if (y < 0) y = d.argmax;
+  out_tok[(int64_t)b * (T + 1) + d.n] = y;
 }
 
 }  // namespace
