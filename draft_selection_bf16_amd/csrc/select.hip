@@ -30,6 +30,7 @@ constexpr int kMaxLattice = 63 * 16 * 16;   // T <= 63, K <= 16
 // reloads slice 0 and is not added).
 constexpr int kMaxProjSplit = 8;
 __device__ __forceinline__ f32x4 slice_sum4(const float* p, int split, int64_t k) {
+  if (split == 1) return *(const f32x4*)p;   // the same for the whole grid
   f32x4 v[kMaxProjSplit];
 #pragma unroll
   for (int s = 0; s < kMaxProjSplit; ++s) v[s] = *(const f32x4*)(p + (s < split ? s : 0) * k);
