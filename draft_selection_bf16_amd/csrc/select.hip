@@ -59,6 +59,9 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
   const int npred = t == 0 ? 1 : K;
   const int r4 = r / 4;
   const float* Hp = h_part + (int64_t)bt * r;
+  // U_t(b) of this thread's output, requested before the staging loads
+  const int oi = tid / 16, oj = tid % 16;
+  const float u_j = (oi < K && oj < K) ? cand_val[(int64_t)bt * K + oj] : 0.f;
   // each thread stages up to 4 float4 of G and 4 of B (16 rows x 64 float4)
   f32x4 ga[4], gb[4];
   int gi[4], gq[4];
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     }
   }
   __syncthreads();
-  const int i = tid / 16, j = tid % 16;
+  const int i = oi, j = oj;
   if (i >= K || j >= K) return;
   float* out = scores + ((int64_t)bt * K + i) * K + j;
   if (i >= npred) {
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     acc = fmaf(x[2], y[2], acc);
     acc = fmaf(x[3], y[3], acc);
   }
-  *out = cand_val[(int64_t)bt * K + j] + acc;
+  *out = u_j + acc;
 }
 
 // (value, rank) comparison: larger value, then lower rank
@@ -116,7 +119,15 @@ __device__ __forceinline__ bool better(float v1, int i1, float v0, int i0) {
   return v1 > v0 || (v1 == v0 && i1 < i0);
 }
 
-__global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scores,
+// One work-group of four waves per request: all 256 threads stage the
+// request's lattice (T*K*K floats) and its candidate ids in LDS with one
+// round of loads; the first wave then runs the recursion (the other waves
+// compute the same values in step, write nothing and only keep the
+// work-group barriers uniform).
+constexpr int kPathThreads = 256;
+constexpr int kPathLoads = 4;   // 16-byte lattice loads in flight per thread
+
+__global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restrict__ scores,
                                                   const int32_t* __restrict__ cand_idx, int T,
                                                   int K, int mode, float inv_tau,
                                                   const uint64_t* __restrict__ seed_dev,
@@ -125,31 +136,47 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
                                                   float* __restrict__ q, float* __restrict__ path_score) {
   __shared__ uint8_t psi[64][16];
   __shared__ int32_t chosen[64];
+  __shared__ int32_t sIdx[kMaxLattice / 16];
   __shared__ __attribute__((aligned(16))) float sS[kMaxLattice];
-  const int b = blockIdx.x, lane = threadIdx.x;
-  // the request's whole lattice (T*K*K floats) in one burst of loads
+  const int b = blockIdx.x, lane = threadIdx.x & 63;
+  const bool w0 = threadIdx.x < 64;   // the wave that writes
   {
     const float* g = scores + (int64_t)b * T * K * K;
     const int n = T * K * K;
+    const int nk = T * K;
+    const int32_t* ci = cand_idx + (int64_t)b * nk;
+    // candidate ids (T*K <= 1008: at most four per thread), issued with the
+    // lattice loads below
+    int32_t cv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = threadIdx.x + u * kPathThreads;
+      cv[u] = e < nk ? ci[e] : 0;
+    }
     if (((uintptr_t)g & 15) == 0) {
       const f32x4* g4 = (const f32x4*)g;
       const int n4 = n / 4;
-      for (int e0 = 0; e0 < n4; e0 += 64 * 8) {   // eight 16-byte loads in flight per lane
-        f32x4 v[8];
+      for (int e0 = 0; e0 < n4; e0 += kPathThreads * kPathLoads) {
+        f32x4 v[kPathLoads];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 64 + lane;
+        for (int u = 0; u < kPathLoads; ++u) {
+          const int e = e0 + u * kPathThreads + threadIdx.x;
           v[u] = e < n4 ? g4[e] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * 64 + lane;
+        for (int u = 0; u < kPathLoads; ++u) {
+          const int e = e0 + u * kPathThreads + threadIdx.x;
           if (e < n4) ((f32x4*)sS)[e] = v[u];
         }
       }
-      for (int e = n4 * 4 + lane; e < n; e += 64) sS[e] = g[e];
+      for (int e = n4 * 4 + threadIdx.x; e < n; e += kPathThreads) sS[e] = g[e];
     } else {
-      for (int e = lane; e < n; e += 64) sS[e] = g[e];
+      for (int e = threadIdx.x; e < n; e += kPathThreads) sS[e] = g[e];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = threadIdx.x + u * kPathThreads;
+      if (e < nk) sIdx[e] = cv[u];
     }
   }
   __syncthreads();
@@ -184,7 +211,7 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
           arg = oa;
         }
       }
-      if (lane < 16) psi[t][lane] = (uint8_t)arg;
+      if (w0 && lane < 16) psi[t][lane] = (uint8_t)arg;
       delta = (j < K) ? best : -INFINITY;
     }
     // end argmax over j (lowest rank on ties)
@@ -199,7 +226,7 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
       }
     }
     __syncthreads();
-    if (lane == 0) {
+    if (w0 && lane == 0) {
       int c = bi;
       chosen[T - 1] = c;
       for (int t = T - 1; t >= 1; --t) {
@@ -227,7 +254,7 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
           }
         }
         pick = bi;
-        if (lane < K) q[((int64_t)b * T + t) * K + lane] = lane == pick ? 1.f : 0.f;
+        if (w0 && lane < K) q[((int64_t)b * T + t) * K + lane] = lane == pick ? 1.f : 0.f;
       } else {  // SAMPLE
         float mx = wave_max_f32(v);
         float e = (lane < K) ? expf((v - mx) * inv_tau) : 0.f;
@@ -247,19 +274,20 @@ __global__ __launch_bounds__(64) void path_kernel(const float* __restrict__ scor
           uint64_t nz = ballot(lane < K && p > 0.f);
           pick = nz ? 63 - __clzll((unsigned long long)nz) : 0;
         }
-        if (lane < K) q[((int64_t)b * T + t) * K + lane] = p;
+        if (w0 && lane < K) q[((int64_t)b * T + t) * K + lane] = p;
       }
       float sv = __shfl(v, pick);
       total = (t == 0) ? sv : total + sv;
-      if (lane == 0) chosen[t] = pick;
+      if (w0 && lane == 0) chosen[t] = pick;
       prev = pick;
     }
     __syncthreads();
   }
+  if (!w0) return;
   for (int t = lane; t < T; t += 64) {
     int c = chosen[t];
     path_rank[(int64_t)b * T + t] = c;
-    path_tok[(int64_t)b * T + t] = cand_idx[((int64_t)b * T + t) * K + c];
+    path_tok[(int64_t)b * T + t] = sIdx[t * K + c];
     if (mode == 0)
       for (int k = 0; k < K; ++k) q[((int64_t)b * T + t) * K + k] = k == c ? 1.f : 0.f;
   }
@@ -285,7 +313,7 @@ hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int 
   if (B == 0) return hipSuccess;
   float inv_tau = mode == 2 ? 1.0f / temperature : 0.f;
   ProfileScope ps("path", stream);
-  DF2_TRY(launch(path_kernel, dim3(B), dim3(64), 0, stream, ps, scores, cand_idx, T, K, mode, inv_tau, seed_dev,
+  DF2_TRY(launch(path_kernel, dim3(B), dim3(kPathThreads), 0, stream, ps, scores, cand_idx, T, K, mode, inv_tau, seed_dev,
                                                 path_rank, path_tok, q, path_score));
   return hipGetLastError();
 }
