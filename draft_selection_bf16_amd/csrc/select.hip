@@ -119,6 +119,18 @@ __device__ __forceinline__ bool better(float v1, int i1, float v0, int i0) {
   return v1 > v0 || (v1 == v0 && i1 < i0);
 }
 
+// Keep the better of this lane's (value, rank) and that of the lane the DPP
+// quad permutation CTRL names (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ void quad_better(float& best, int& arg) {
+  const float ob = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(best), CTRL, 0xF, 0xF, false));
+  const int oa = __builtin_amdgcn_update_dpp(0, arg, CTRL, 0xF, 0xF, false);
+  if (better(ob, oa, best, arg)) {
+    best = ob;
+    arg = oa;
+  }
+}
+
 // One work-group of four waves per request: all 256 threads stage the
 // request's lattice (T*K*K floats) and its candidate ids in LDS with one
 // round of loads; the first wave then runs the recursion (the other waves
@@ -137,6 +149,7 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
   __shared__ uint8_t psi[64][16];
   __shared__ int32_t chosen[64];
   __shared__ int32_t sIdx[kMaxLattice / 16];
+  __shared__ __attribute__((aligned(16))) float sD[kPathThreads / 64][2][16];
   __shared__ __attribute__((aligned(16))) float sS[kMaxLattice];
   const int b = blockIdx.x, lane = threadIdx.x & 63;
   const bool w0 = threadIdx.x < 64;   // the wave that writes
@@ -185,35 +198,38 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
   float total = 0.f;
 
   if (mode == 0) {  // VITERBI
-    const int ig = lane >> 4;
-    float delta = (j < K) ? S[j] : -INFINITY;   // held by lanes with ig == 0 (all groups copy)
+    // lane = 4 j + g: target rank j, predecessors i = 4 g .. 4 g + 3; the
+    // four lanes of a quad combine their (value, rank) pairs with two DPP
+    // quad permutations.  delta_{t-1} reaches the lanes through a 16-float
+    // LDS row of the wave's own (double-buffered by step parity).
+    const int jv = lane >> 2, gv = lane & 3, wv = threadIdx.x >> 6;
+    if (lane < 16) sD[wv][0][lane] = lane < K ? S[lane] : -INFINITY;
+    __builtin_amdgcn_wave_barrier();
     for (int t = 1; t < T; ++t) {
+      const float* St = S + (int64_t)t * K * K;
+      const f32x4 dp = *(const f32x4*)&sD[wv][(t - 1) & 1][4 * gv];
       float best = -INFINITY;
-      int arg = ig * 4;
+      int arg = 4 * gv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        int i = ig * 4 + e;
-        float di = __shfl(delta, i);   // delta_{t-1}[i] from lane i
-        if (i < K && j < K) {
-          float v = di + S[((int64_t)t * K + i) * K + j];
+        const int i = 4 * gv + e;
+        if (i < K && jv < K) {
+          const float v = dp[e] + St[i * K + jv];
           if (v > best) {
             best = v;
             arg = i;
           }
         }
       }
-#pragma unroll
-      for (int m = 16; m <= 32; m <<= 1) {
-        float ob = __shfl_xor(best, m);
-        int oa = __shfl_xor(arg, m);
-        if (better(ob, oa, best, arg)) {
-          best = ob;
-          arg = oa;
-        }
+      quad_better<0xB1>(best, arg);   // lane ^ 1
+      quad_better<0x4E>(best, arg);   // lane ^ 2
+      if (gv == 0) {
+        if (w0) psi[t][jv] = (uint8_t)arg;
+        sD[wv][t & 1][jv] = jv < K ? best : -INFINITY;
       }
-      if (w0 && lane < 16) psi[t][lane] = (uint8_t)arg;
-      delta = (j < K) ? best : -INFINITY;
+      __builtin_amdgcn_wave_barrier();
     }
+    const float delta = sD[wv][(T - 1) & 1][lane & 15];
     // end argmax over j (lowest rank on ties)
     float bv = (lane < K) ? delta : -INFINITY;
     int bi = lane < K ? lane : 64;
