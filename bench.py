@@ -29,7 +29,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm",
-               "pair_epilogue", "path", "argmax_part", "greedy_final"]
+               "proj_reduce", "pair_epilogue", "path", "argmax_part", "greedy_final",
+               "sumexp_part", "reject_decide", "residual_chunk", "residual_find"]
 
 
 def parse():

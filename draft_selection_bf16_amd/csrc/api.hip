@@ -113,8 +113,10 @@ namespace {
 constexpr GemmTiling kProjTiling{128, 128, 3, 8};
 // The projection's K split: with few tiles (small batches) the reduction
 // over d is split so that up to about one work-group per CU takes part
-// (slices of >= 4 K-tiles, at most 8: the pair epilogue, which adds the
-// slices in a fixed order and gates H, loads all of them at once).
+// (slices of >= 4 K-tiles, at most kMaxProjSplit).  The slices are summed
+// in a fixed order by a reduce pass spread over many work-groups before the
+// pair epilogue, which gates H after the sum.
+constexpr int kMaxProjSplit = 8;
 int proj_split(int B, int T, int K, int d, int r) {
   const int bm = kProjTiling.bm, bn = kProjTiling.bn;
   auto tl = [&](int m, int n) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
@@ -122,7 +124,7 @@ int proj_split(int B, int T, int K, int d, int r) {
   const int tiles = (r % bn == 0 ? tl(mc, 2 * r) : 2 * tl(mc, r)) + tl(B, r) + tl(B * T, r);
   int ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks > d / 64 / 4) ks = d / 64 / 4;
-  if (ks > 8) ks = 8;
+  if (ks > kMaxProjSplit) ks = kMaxProjSplit;
   return ks < 1 ? 1 : ks;
 }
 struct PairWs {

@@ -93,9 +93,11 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
                        const char* tag, hipStream_t stream);
 
 // ---- pair scores epilogue ---------------------------------------------------
-// ab, a_last, h: `split` (1..8) slices of partial products, kstrides floats apart
-// (added in slice order); h ungated (the gate is applied after the sum).
-hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* h, int split,
+// ab, a_last, h: `split` slices of partial products, kstrides floats apart;
+// with split > 1 a reduce pass first sums them in slice order into slice 0
+// (in place: the buffers are workspace); h ungated (the gate is applied
+// after the sum).
+hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
                                 int64_t ab_k, int64_t alast_k, int64_t h_k, int gate,
                                 const float* cand_val, int B, int T, int K, int r,
                                 float* scores, hipStream_t stream);

@@ -25,27 +25,43 @@ namespace {
 constexpr int kMaxR = 256;
 constexpr int kMaxLattice = 63 * 16 * 16;   // T <= 63, K <= 16
 
-// The sum of the `split` (<= 8) slices of partial products at p (k floats
-// apart), in slice order; the 8 loads go out together (a slice past `split`
-// reloads slice 0 and is not added).
-constexpr int kMaxProjSplit = 8;
-__device__ __forceinline__ f32x4 slice_sum4(const float* p, int split, int64_t k) {
-  if (split == 1) return *(const f32x4*)p;   // the same for the whole grid
-  f32x4 v[kMaxProjSplit];
+// In place: slice 0 of three partial-product buffers (n0, n1, n2 float4 per
+// slice, slices k* floats apart) becomes the sum of their `split` slices,
+// added in slice order.  One thread per float4; its slices are requested in
+// blocks of eight.
+__global__ __launch_bounds__(64) void slice_reduce_kernel(float* __restrict__ p0, int64_t n0, int64_t k0,
+                                                           float* __restrict__ p1, int64_t n1, int64_t k1,
+                                                           float* __restrict__ p2, int64_t n2, int64_t k2,
+                                                           int split) {
+  int64_t e = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  float* p;
+  int64_t k;
+  if (e < n0) {
+    p = p0; k = k0;
+  } else if (e < n0 + n1) {
+    e -= n0; p = p1; k = k1;
+  } else if (e < n0 + n1 + n2) {
+    e -= n0 + n1; p = p2; k = k2;
+  } else {
+    return;
+  }
+  float* q = p + 4 * e;
+  f32x4 acc = *(const f32x4*)q;
+  for (int s0 = 1; s0 < split; s0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-  for (int s = 0; s < kMaxProjSplit; ++s) v[s] = *(const f32x4*)(p + (s < split ? s : 0) * k);
-  f32x4 acc = v[0];
+    for (int u = 0; u < 8; ++u) v[u] = *(const f32x4*)(q + (int64_t)(s0 + u < split ? s0 + u : 0) * k);
 #pragma unroll
-  for (int s = 1; s < kMaxProjSplit; ++s)
-    if (s < split) acc += v[s];
-  return acc;
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < split) acc += v[u];
+  }
+  *(f32x4*)q = acc;
 }
 
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
                                                             const float* __restrict__ h_part,
-                                                            int split, int64_t ab_k, int64_t alast_k,
-                                                            int64_t h_k, int gate,
+                                                            int gate,
                                                             const float* __restrict__ cand_val,
                                                             int T, int K, int r,
                                                             float* __restrict__ scores) {
@@ -75,16 +91,16 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     if (gi[u] < npred) {
       const float* src = t == 0 ? a_last + (int64_t)b * r
                                 : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
-      ga[u] = slice_sum4(src + 4 * gq[u], split, t == 0 ? alast_k : ab_k);
+      ga[u] = *(const f32x4*)(src + 4 * gq[u]);
     }
-    if (gi[u] < K) gb[u] = slice_sum4(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u], split, ab_k);
+    if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (gi[u] < 16) {
       f32x4 h = f32x4{0.f, 0.f, 0.f, 0.f};
       if (gi[u] < npred) {
-        h = slice_sum4(Hp + 4 * gq[u], split, h_k);
+        h = *(const f32x4*)(Hp + 4 * gq[u]);
         if (gate == 1)
 #pragma unroll
           for (int e = 0; e < 4; ++e) h[e] = 1.0f / (1.0f + expf(-h[e]));
@@ -312,14 +328,23 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
 
 }  // namespace
 
-hipError_t launch_pair_epilogue(const float* ab, const float* a_last, const float* h, int split,
+hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
                                 int64_t ab_k, int64_t alast_k, int64_t h_k, int gate,
                                 const float* cand_val, int B, int T, int K, int r, float* scores,
                                 hipStream_t stream) {
   if (B * T == 0) return hipSuccess;
+  if (split > 1) {
+    // sum the slices into slice 0 over many work-groups first; the epilogue
+    // then reads one slice
+    const int64_t n0 = (int64_t)B * T * K * 2 * r / 4, n1 = (int64_t)B * r / 4, n2 = (int64_t)B * T * r / 4;
+    const int64_t n = n0 + n1 + n2;
+    ProfileScope pr("proj_reduce", stream);
+    DF2_TRY(launch(slice_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, pr,
+                   ab, n0, ab_k, a_last, n1, alast_k, h, n2, h_k, split));
+  }
   ProfileScope ps("pair_epilogue", stream);
-  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, split, ab_k,
-                 alast_k, h_k, gate, cand_val, T, K, r, scores));
+  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, gate, cand_val,
+                 T, K, r, scores));
   return hipGetLastError();
 }
 

@@ -200,22 +200,20 @@ def _pair_gpu(cand_idx, cand_val, last, E, h, wa, wb, wh, gate=0):
 def _ws_views(w, B, T, K, r, gate=0):
     """The projection's results in the pair-scores workspace: [A|B] of the
     candidates, A of the last tokens and H, each stored as S slices of
-    partial products over the hidden size (S found from the workspace size),
-    summed here in slice order; H is stored before its gate."""
+    partial products over the hidden size (S found from the workspace size);
+    with S > 1 the library has summed the slices into slice 0 (in place)
+    before the epilogue.  H is stored before its gate."""
     def a256(n):
         return (n + 255) // 256 * 256
     n_ab, n_al, n_h = B * T * K * 2 * r, B * r, B * T * r
     nbytes = w.numel()
-    S = next(s for s in range(1, 9) if a256(s * n_ab * 4) + a256(s * n_al * 4) + a256(s * n_h * 4) == nbytes)
+    S = next(s for s in range(1, 33) if a256(s * n_ab * 4) + a256(s * n_al * 4) + a256(s * n_h * 4) == nbytes)
     f = w.view(torch.float32)
     off_al = a256(S * n_ab * 4) // 4
     off_h = off_al + a256(S * n_al * 4) // 4
 
     def summed(off, n):
-        acc = f[off:off + n].clone()
-        for k in range(1, S):
-            acc += f[off + k * n:off + (k + 1) * n]
-        return acc.cpu().numpy()
+        return f[off:off + n].cpu().numpy()
     ab = summed(0, n_ab).reshape(B, T, K, 2 * r)
     al = summed(off_al, n_al).reshape(B, r)
     hg = summed(off_h, n_h).reshape(B, T, r)
