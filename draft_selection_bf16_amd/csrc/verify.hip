@@ -429,28 +429,40 @@ struct ResidualSum {
   __device__ void vec(const u32x4& v, int64_t i0) { vec_as_floats<DT>(*this, v, i0); }
 };
 
-// load the decision and the candidates of the resampled row that lie in
-// [lo, hi) into LDS (thread 0), return the row pointer
+// The resampled row of request b (row n = the first rejected position, or T
+// for the bonus draw).
 template <int DT>
-__device__ __forceinline__ const void* residual_setup(
-    Residual& R, const void* z, int64_t vocab, int T, int K, float c, int b,
-    const DecRec* dec, const int32_t* cand_idx, const float* q, int64_t lo, int64_t hi) {
-  const DecRec d = dec[b];
-  R.m = d.m;
-  R.s = d.s;
-  R.c = c;
-  R.ncand = 0;
-  if (d.n < T) {
-    for (int kk = 0; kk < K; ++kk) {
-      int32_t v = cand_idx[((int64_t)b * T + d.n) * K + kk];
-      if (v >= lo && v < hi) {
-        R.cid[R.ncand] = v;
-        R.cq[R.ncand] = q[((int64_t)b * T + d.n) * K + kk];
-        R.ncand++;
-      }
-    }
+__device__ __forceinline__ const void* residual_row(const void* z, int64_t vocab, int T, int b, int n) {
+  return (const char*)z + ((int64_t)b * (T + 1) + n) * vocab * Elt<DT>::ESZ;
+}
+
+// Fill R (wave 0): the row's softmax constants, and the candidates of the
+// rejected position that lie in [lo, hi) with their proposal q, in rank
+// order; lane k < K fetches candidate k (one round of loads).  The caller
+// synchronises the work-group before R is read.
+__device__ __forceinline__ void residual_fill(Residual& R, const DecRec& d, int T, int K, float c, int b,
+                                              const int32_t* cand_idx, const float* q, int64_t lo,
+                                              int64_t hi) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  int32_t v = -1;
+  float qq = 0.f;
+  if (d.n < T && lane < K) {
+    v = cand_idx[((int64_t)b * T + d.n) * K + lane];
+    qq = q[((int64_t)b * T + d.n) * K + lane];
   }
-  return (const char*)z + ((int64_t)b * (T + 1) + d.n) * vocab * Elt<DT>::ESZ;
+  const bool in = v >= lo && v < hi;
+  const uint64_t m = ballot(in);
+  if (in) {
+    R.cid[lanes_below(m)] = v;
+    R.cq[lanes_below(m)] = qq;
+  }
+  if (lane == 0) {
+    R.m = d.m;
+    R.s = d.s;
+    R.c = c;
+    R.ncand = __popcll(m);
+  }
 }
 
 template <int DT>
@@ -462,12 +474,13 @@ __global__ __launch_bounds__(kThreads) void residual_chunk_kernel(
   __shared__ float sred[kWaves];
   const int b = blockIdx.x / rchunks, ch = blockIdx.x % rchunks;
   const int64_t lo = (int64_t)ch * rchunk, hi = lo + rchunk < vocab ? lo + rchunk : vocab;
-  __shared__ const void* srow;
-  if (threadIdx.x == 0) srow = residual_setup<DT>(R, z, vocab, T, K, c, b, dec, cand_idx, q, lo, hi);
+  const DecRec d = dec[b];
+  const void* row = residual_row<DT>(z, vocab, T, b, d.n);
+  residual_fill(R, d, T, K, c, b, cand_idx, q, lo, hi);
   __syncthreads();
   ResidualSum f;
   f.R = &R;
-  if (lo < hi) stream_row<DT>(srow, lo, hi, f);
+  if (lo < hi) stream_row<DT>(row, lo, hi, f);
   float v = wave_sum_f32(f.acc);
   if (lane_id() == 0) sred[threadIdx.x / kWave] = v;
   __syncthreads();
@@ -478,6 +491,8 @@ __global__ __launch_bounds__(kThreads) void residual_chunk_kernel(
   }
 }
 
+constexpr int kFindBlock = 8;   // entries per block of loads in the in-chunk search
+
 // one work-group per request: find the chunk where the running mass passes
 // u2 * total, then the entry inside it
 template <int DT>
@@ -486,7 +501,6 @@ __global__ __launch_bounds__(kThreads) void residual_find_kernel(
     const DecRec* __restrict__ dec, const int32_t* __restrict__ cand_idx,
     const float* __restrict__ q, const float* __restrict__ rsum, int32_t* __restrict__ out_tok) {
   __shared__ Residual R;
-  __shared__ const void* srow;
   __shared__ float s_target;
   __shared__ int s_chunk;
   __shared__ float swsum[kWaves];
@@ -528,13 +542,29 @@ __global__ __launch_bounds__(kThreads) void residual_find_kernel(
     return;
   }
   const int64_t lo = (int64_t)ch * rchunk, hi = lo + rchunk < vocab ? lo + rchunk : vocab;
-  if (tid == 0) srow = residual_setup<DT>(R, z, vocab, T, K, c, b, dec, cand_idx, q, lo, hi);
-  __syncthreads();
-  // contiguous sub-range per thread, in index order
+  const void* srow = residual_row<DT>(z, vocab, T, b, d.n);
+  // contiguous sub-range per thread, in index order; its entries are
+  // loaded in blocks of kFindBlock (all loads of a block in flight, clamped
+  // to the range); the first block goes out together with the candidate
+  // loads, before the barrier, and is kept for the walk below
   const int64_t per = (rchunk + kThreads - 1) / kThreads;
   const int64_t t0 = lo + tid * per, t1 = t0 + per < hi ? t0 + per : hi;
+  float x0[kFindBlock];
+#pragma unroll
+  for (int u = 0; u < kFindBlock; ++u)   // unconditional, clamped into [lo, hi)
+    x0[u] = Elt<DT>::one(srow, t0 + u < t1 ? t0 + u : (t1 > t0 ? t1 - 1 : lo));
+  residual_fill(R, d, T, K, c, b, cand_idx, q, lo, hi);
+  __syncthreads();
   float mine = 0.f;
-  for (int64_t v = t0; v < t1; ++v) mine += R.w(Elt<DT>::one(srow, v), v);
+  for (int64_t v0 = t0; v0 < t1; v0 += kFindBlock) {
+    float x[kFindBlock];
+#pragma unroll
+    for (int u = 0; u < kFindBlock; ++u)
+      x[u] = v0 == t0 ? x0[u] : Elt<DT>::one(srow, v0 + u < t1 ? v0 + u : t1 - 1);
+#pragma unroll
+    for (int u = 0; u < kFindBlock; ++u)
+      if (v0 + u < t1) mine += R.w(x[u], v0 + u);
+  }
   // prefix over the thread sums: a wave scan, then the earlier waves'
   // totals added in wave order
   const int lane = lane_id(), wave = tid / kWave;
@@ -573,17 +603,25 @@ __global__ __launch_bounds__(kThreads) void residual_find_kernel(
     return;
   }
   if (tid != tsel) return;
-  // the selected thread walks its own range in index order
+  // the selected thread walks its own range in index order (the first
+  // block from the registers loaded above)
   int y = -1;
   float acc = found ? excl : 0.f;
   int64_t lastv = -1;
-  for (int64_t v = t0; v < t1; ++v) {
-    const float wv = R.w(Elt<DT>::one(srow, v), v);
-    if (wv > 0.f) lastv = v;
-    acc += wv;
-    if (found && acc > s_target) {
-      y = (int)v;
-      break;
+  for (int64_t v0 = t0; v0 < t1 && y < 0; v0 += kFindBlock) {
+    float x[kFindBlock];
+#pragma unroll
+    for (int u = 0; u < kFindBlock; ++u)
+      x[u] = v0 == t0 ? x0[u] : Elt<DT>::one(srow, v0 + u < t1 ? v0 + u : t1 - 1);
+#pragma unroll
+    for (int u = 0; u < kFindBlock; ++u) {
+      const int64_t v = v0 + u;
+      if (v < t1 && y < 0) {
+        const float wv = R.w(x[u], v);
+        if (wv > 0.f) lastv = v;
+        acc += wv;
+        if (found && acc > s_target) y = (int)v;
+      }
     }
   }
   if (y < 0) y = (int)lastv;
