@@ -165,10 +165,6 @@ def roofline_of(w, tag, avg_us):
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_b32_blk16_v151936_conv.txt")
-TAG_NAMES = {"conv_gemm": "gemm_kernel<64", "conv_epilogue": "conv_epilogue_kernel",
-             "topk_chunk": "topk_chunk_kernel", "project_gemm": "gemm_kernel<128",
-             "argmax_part": "argmax_part_kernel"}
-
 
 def source_hash():
     import glob
