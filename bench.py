@@ -28,6 +28,7 @@ METRIC = "draft blocks/s (topk+select+verify) at B=1/8/32, block 8/16; % HBM pea
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
+STRESS = "b64_blk16_v262144_stress"
 KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm",
                "proj_reduce", "pair_epilogue", "path", "argmax_part", "greedy_final",
                "sumexp_part", "reject_decide", "residual_chunk", "residual_find"]
@@ -317,6 +318,21 @@ def main():
             del c2
         sweep[w.name + " (no conv)"] = dict(B=w.B, block=w.block, us_per_cycle=round(ms_nc * 1e3, 2),
                                             blocks_per_s=round(w.B / (ms_nc / 1e3), 1))
+        if w.name != STRESS:
+            # the stress cycle (64 requests, vocabulary 262,144, half greedy and half
+            # rejection verification), with and without its 20 conv sites
+            ws_ = synth.WORKLOADS[STRESS]
+            E4 = None
+            for conv in (True, False):
+                c2, E4 = build_cycle(ws_, dev, E=E4, conv=conv)
+                c2.capture(conv=conv)
+                m2, _ = time_graph(c2, args.steps, args.warmup)
+                sweep[STRESS + ("" if conv else " (no conv)")] = dict(
+                    B=ws_.B, block=ws_.block, path=ws_.path_mode, verify=ws_.verify,
+                    conv_sites=ws_.conv_sites if conv else 0, us_per_cycle=round(m2 * 1e3, 2),
+                    blocks_per_s=round(ws_.B / (m2 / 1e3), 1))
+                del c2
+            del E4
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -200,9 +200,16 @@ def target_logits(w: Workload, drafter: torch.Tensor, true_tok: torch.Tensor, de
       row T gets a uniform argmax.
     correlated: rows t < T are the drafter's logits plus N(0,1) noise;
       row T is 3*N(0,1).
+    mixed: requests 0 .. B/2 - 1 planted_argmax (the greedy-verified half),
+      the rest correlated with the next seed offset (the rejection half).
     """
     kind = kind or w.target
     B, T, V = drafter.shape[0], w.T, w.V
+    if kind == "mixed":
+        h = B // 2
+        return torch.cat([target_logits(w, drafter[:h], true_tok[:h], device, "planted_argmax", seed_offset),
+                          target_logits(w, drafter[h:], true_tok[h:], device, "correlated", seed_offset + 1)],
+                         0)
     g = _gen(w.seed * 1000 + 2 + seed_offset, device)
     if kind == "tiny_agree":
         z = _randn((B, T + 1, V), g, device)

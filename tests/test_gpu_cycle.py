@@ -24,13 +24,7 @@ pytestmark = [pytest.mark.gpu,
 def build(w, with_conv=None, y_dtype=torch.bfloat16):
     """Inputs for workload w on the GPU, and the Cycle that runs them."""
     z, tok, rank = synth.drafter_logits(w, device=DEV)
-    if w.target == "mixed":
-        g = w.B // 2
-        Zg = synth.target_logits(w, z[:g], tok[:g], device=DEV, kind="planted_argmax")
-        Zr = synth.target_logits(w, z[g:], tok[g:], device=DEV, kind="correlated", seed_offset=1)
-        Z = torch.cat([Zg, Zr], 0)
-    else:
-        Z = synth.target_logits(w, z, tok, device=DEV)
+    Z = synth.target_logits(w, z, tok, device=DEV)
     E = synth.embeddings(w, device=DEV)
     wa, wb, wh = synth.selector_weights(w, device=DEV)
     h = synth.context_hidden(w, device=DEV)
