@@ -550,10 +550,12 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
 // One wave per row: merge splits * 16 keys (splits <= 32), each split's 16
 // best-first (empty slots 0).  Two lower bounds on the row's 16th best key:
 // the largest of the splits' 16th keys (that split holds 16 keys at least
-// as large), and with >= 16 splits the 16th largest of their heads (16
-// distinct keys at least as large).  The keys that reach both are few; they
-// are ranked against each other by broadcast LDS compares.  More than 64
-// of them (ties at the cut) falls back to the exact 64-bit search.
+// as large), and the 16th largest among the first ceil(32 / splits) keys of
+// every split (16 distinct keys at least as large).  The keys that reach
+// both are few (at most 22 per row on the synthetic workloads at 2 to 18
+// splits); they are ranked against each other by broadcast LDS compares.
+// More than 64 of them (ties at the cut) falls back to the exact 64-bit
+// search.
 __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ part,
                                                               int64_t rows, int splits, int k,
                                                               int32_t* __restrict__ out_idx,
@@ -578,19 +580,28 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
     if (s < n && (s & 15) == 15 && keys[i] > b1) b1 = keys[i];
   }
   b1 = wave_max_u64(b1);
+  // b2: the 16th largest key among the first j keys of every list, with
+  // j = ceil(32 / splits) (32 to 62 keys, all in one wave): a subset of the
+  // row's keys, so its 16th largest is a lower bound on the row's.  With
+  // the lists sorted best-first it lands close to the row's 16th best.
   uint64_t b2 = 0ull;
-  if (splits >= 16) {
+  {
+    const int j = (32 + splits - 1) / splits;
+    int nsub = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int s = lane + i * kWave;
-      if (s < n && (s & 15) == 0) ssv[wave][s >> 4] = keys[i];
+      const bool in = s < n && (s & 15) < j;
+      const uint64_t m = ballot(in);
+      if (in) ssv[wave][nsub + lanes_below(m)] = keys[i];
+      nsub += __popcll(m);
     }
     __builtin_amdgcn_wave_barrier();
-    const uint64_t hk = lane < splits ? ssv[wave][lane] : 0ull;
+    const uint64_t sk = lane < nsub ? ssv[wave][lane] : 0ull;
     int rk = 0;
-    for (int l = 0; l < splits; ++l) rk += ssv[wave][l] > hk ? 1 : 0;
-    const uint64_t m = ballot(lane < splits && hk != 0ull && rk == 15);
-    if (m) b2 = shfl_u64(hk, __ffsll((unsigned long long)m) - 1);
+    for (int l = 0; l < nsub; ++l) rk += ssv[wave][l] > sk ? 1 : 0;
+    const uint64_t m = ballot(lane < nsub && sk != 0ull && rk == 15);
+    if (m) b2 = shfl_u64(sk, __ffsll((unsigned long long)m) - 1);
     __builtin_amdgcn_wave_barrier();
   }
   const uint64_t bound = b1 > b2 ? b1 : b2;
