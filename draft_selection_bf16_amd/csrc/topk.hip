@@ -645,11 +645,18 @@ __global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __
 
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   (void)k;
-  // about 448 work-groups of eight waves (two per CU keep enough loads in
-  // flight); one per row when there are that many rows, which also needs no
-  // merge.  Chunks stay >= 8192 entries and <= 32 per row (the merge holds
-  // at most 512 keys per row).
-  int64_t want = (448 + rows - 1) / (rows > 0 ? rows : 1);
+  // One work-group of eight waves per row and no merge from 256 rows on (at
+  // 480 rows most CUs scan two rows).  Below that, as many chunks per row as
+  // keep rows * chunks <= 256, one work-group per CU: a CU's share of the
+  // bytes is what bounds the scan, and every chunk adds a fixed cost
+  // (priming, the final selection) and 16 keys to merge.  Measured per
+  // cycle against the earlier target of ~448 work-groups: 224 rows 98.5
+  // against 101.2 us (1 chunk instead of 2), 120 rows 79.7 against 81.3
+  // (2 instead of 4), 56 rows 100.3 against 101.1 (4 instead of 8), 15 rows
+  // 55.8 against 58.6 (17 instead of 18).  Chunks stay >= 8192 entries and
+  // <= 32 per row (the merge holds at most 512 keys per row).
+  constexpr int64_t kCUs = 256;   // MI355X
+  int64_t want = kCUs / (rows > 0 ? rows : 1);
   int64_t max_by_size = vocab / 8192;
   int64_t s = want < max_by_size ? want : max_by_size;
   if (s < 1) s = 1;

@@ -87,18 +87,20 @@ def test_topk_ties_and_signed_zero():
 
 def test_topk_merge_many_survivors_falls_back_exactly():
     """Few rows, so every row is split into 15 chunks and the per-chunk
-    lists are merged.  Each chunk holds the same 16 large values, so every
-    chunk's 16th best has the same value and about 15 x 16 keys reach the
-    merge's lower bound: the exact fallback has to pick the 16 best (equal
-    values: lowest index first)."""
+    lists are merged.  Five chunks each hold 16 distinct large values,
+    interleaved across the five (chunk c gets 10 + (5 i + c) / 16): every
+    chunk's 16th best is small, the first three keys of all 15 lists hold
+    only 15 large ones, so both lower bounds of the merge stay low and 76
+    keys pass them, more than the 64 of the ranked path: the exact fallback
+    has to pick the 16 best."""
     V = 15 * 8192
     g = torch.Generator().manual_seed(21)
     z = torch.randn(2, V, generator=g)
-    top = 10.0 + 0.0625 * torch.arange(16, dtype=torch.float32)   # exact in bf16
-    for c in range(15):
-        pos = c * 8192 + torch.randperm(8192, generator=g)[:16]
-        z[0, pos] = top
-        z[1, pos] = top.flip(0)
+    for row in range(2):
+        for c in range(5):
+            hot = (3 * c + row) % 15
+            pos = hot * 8192 + torch.randperm(8192, generator=g)[:16]
+            z[row, pos] = 10.0 + 0.0625 * (5 * torch.arange(16, dtype=torch.float32) + c)   # exact in bf16
     z = z.to(torch.bfloat16)
     gi, gv = _topk_gpu(dev(z), 16)
     oi, ov = oracle.topk(z.float(), 16)
