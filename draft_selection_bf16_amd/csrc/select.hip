@@ -9,10 +9,11 @@
 // one r-long dot product with B(b).  fp32 throughout.
 //
 // Path (same section; and "DFlash 2 讓 Qwen3.8-27B 快了兩倍", item 2 --
-// Viterbi): one wave per request.  VITERBI keeps delta_t[j] = max_i
-// delta_{t-1}[i] + S_t[i][j] with back-pointers in LDS: lane l owns target
-// rank j = l & 15 and four predecessors i = 4 (l >> 4) + e, and the four
-// lane groups are combined with cross-lane max (value, lowest rank).
+// Viterbi): one work-group per request, whose first wave runs the
+// recursion.  VITERBI keeps delta_t[j] = max_i delta_{t-1}[i] + S_t[i][j]
+// with back-pointers in LDS: lane l owns target rank j = l >> 2 and four
+// predecessors i = 4 (l & 3) + e, and the four lanes of a quad are combined
+// with DPP quad permutations (value, lowest rank).
 // GREEDY follows the best successor; SAMPLE draws c_t from
 // softmax_j(S_t(c_{t-1}, j) / tau) by inverse CDF in rank order with a
 // Philox uniform.  Path sums are float additions.
