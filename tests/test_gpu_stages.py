@@ -135,6 +135,19 @@ def test_topk_launch_shape_of_the_b32_blk16_workload():
     report("topk b32_blk16", recall16=round(float(r16), 4))
 
 
+@pytest.mark.parametrize("name", ["b1_blk16_v151936", "b8_blk8_v151936_sampled", "b8_blk16_v151936",
+                                  "b32_blk8_v151936"])
+def test_topk_small_batch_launch_shapes(name):
+    """The drafter logits of the other batch x block points (15, 56, 120 and
+    224 rows of 151,936: 17, 4, 2 and 1 chunks per row, then the merge where
+    there is more than one), all rows compared."""
+    w = synth.WORKLOADS[name]
+    z, _, _ = synth.drafter_logits(w, device=DEV)
+    gi, gv = _topk_gpu(z, 16)
+    oi, ov = oracle.topk(z.cpu(), 16)
+    assert np.array_equal(gi, oi) and np.array_equal(gv, ov)
+
+
 def test_topk_gumbel_v262144_rows():
     w = synth.scaled(synth.WORKLOADS["b64_blk16_v262144_stress"], B=2)
     z, _, _ = synth.drafter_logits(w, device=DEV)
