@@ -234,6 +234,8 @@ __global__ __launch_bounds__(64) void greedy_final_kernel(const uint64_t* __rest
                                                           int32_t* __restrict__ accept_len,
                                                           int32_t* __restrict__ out_tok) {
   const int b = blockIdx.x, lane = threadIdx.x;
+  // the drafted token of this lane's position, requested with the keys
+  const int32_t pt = path_tok[(int64_t)b * T + (lane < T ? lane : 0)];
   int y = -1;
   if (lane <= T) {
     const uint64_t* p = part + ((int64_t)b * (T + 1) + lane) * splits;
@@ -242,13 +244,13 @@ __global__ __launch_bounds__(64) void greedy_final_kernel(const uint64_t* __rest
     for (int s = 0; s < splits; ++s) k = p[s] > k ? p[s] : k;
     y = k ? (int)key_index(k) : -1;
   }
-  bool miss = lane < T && path_tok[(int64_t)b * T + lane] != y;
+  bool miss = lane < T && pt != y;
   uint64_t mm = ballot(miss);
   int n = mm ? __ffsll((unsigned long long)mm) - 1 : T;
   int yn = __shfl(y, n);
   if (lane == 0) accept_len[b] = n;
   if (lane <= T) {
-    int v = lane < n ? path_tok[(int64_t)b * T + lane] : lane == n ? yn : -1;
+    int v = lane < n ? pt : lane == n ? yn : -1;
     out_tok[(int64_t)b * (T + 1) + lane] = v;
   }
 }
@@ -357,6 +359,10 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok, DecRec* __restrict__ dec) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const uint64_t seed = seed_dev[0];
+  // this lane's drafted token and its rank, requested with the row partials
+  const int lt = lane < T ? lane : 0;
+  const int32_t x = path_tok[(int64_t)b * T + lt];
+  const int rk = path_rank[(int64_t)b * T + lt];
   uint64_t k = 0ull;
   float s = 0.f;
   if (lane <= T) {
@@ -366,8 +372,6 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
   }
   bool reject = false;
   if (lane < T) {
-    const int32_t x = path_tok[(int64_t)b * T + lane];
-    const int rk = path_rank[(int64_t)b * T + lane];
     const float qx = (rk >= 0 && rk < K) ? q[((int64_t)b * T + lane) * K + rk] : 0.f;
     float px = 0.f;
     if (x >= 0 && x < vocab) {
@@ -396,7 +400,7 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
     dec[b] = d;
   }
   if (lane <= T && lane != n)
-    out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? path_tok[(int64_t)b * T + lane] : -1;
+    out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? x : -1;
 }
 
 // residual weight of entry v of the resampled row
