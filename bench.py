@@ -10,8 +10,11 @@ against the target's logits.  Default workload: 32 requests, block 16
 Prints one JSON line.  value = draft blocks per second (requests x cycles /
 s) for the whole step; per-kernel times come from HIP events recorded on the
 launch stream by the library's timing hook; the roofline object describes the
-kernel with the largest time per step; cpu_baseline times the CPU oracle on a
-bounded sample of the same workload.
+kernel with the largest time per step; hbm_frac is the cycle's algorithmic
+HBM bytes (logits, target logits, gathered embedding rows, context rows,
+selector weights and, with the conv sites, their x, x_prev, W and y) per
+second against the 8 TB/s peak, for the step and every sweep point;
+cpu_baseline times the CPU oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -127,6 +130,23 @@ def profile_kernels(cyc, steps):
             out[tag] = dict(launches_per_step=len(ms) / steps, avg_us=1e3 * sum(ms) / len(ms),
                             us_per_step=1e3 * sum(ms) / steps)
     return out
+
+
+def cycle_bytes(w, conv, esz=2):
+    """Algorithmic HBM bytes of one cycle: the drafter and target logits, the
+    gathered embedding rows of the candidates and last tokens, the context
+    rows and the three selector weights, and, with the conv sites, each
+    site's x, x_prev, W and y."""
+    B, T, K, V, d, r = w.B, w.T, w.K, w.V, w.d, w.r
+    by = B * T * V * esz + B * (T + 1) * V * esz + (B * T * K + B + B * T) * d * 2 + 3 * r * d * 2
+    if conv and w.conv_sites:
+        L, G2 = w.block, 2 * (d // 16)
+        by += w.conv_sites * (2 * B * L * d * 2 + B * d * 2 + G2 * d * 2)
+    return by
+
+
+def hbm_frac(w, conv, us):
+    return round(cycle_bytes(w, conv) / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
 
 
 def algorithmic(w, tag, esz=2):
@@ -314,10 +334,12 @@ def main():
             c2.capture(conv=False)
             m2, _ = time_graph(c2, args.steps, args.warmup)
             sweep[name] = dict(B=ws_.B, block=ws_.block, path=ws_.path_mode, verify=ws_.verify,
-                               us_per_cycle=round(m2 * 1e3, 2), blocks_per_s=round(ws_.B / (m2 / 1e3), 1))
+                               us_per_cycle=round(m2 * 1e3, 2), blocks_per_s=round(ws_.B / (m2 / 1e3), 1),
+                               hbm_frac=hbm_frac(ws_, False, m2 * 1e3))
             del c2
         sweep[w.name + " (no conv)"] = dict(B=w.B, block=w.block, us_per_cycle=round(ms_nc * 1e3, 2),
-                                            blocks_per_s=round(w.B / (ms_nc / 1e3), 1))
+                                            blocks_per_s=round(w.B / (ms_nc / 1e3), 1),
+                                            hbm_frac=hbm_frac(w, False, ms_nc * 1e3))
         if w.name != STRESS:
             # the stress cycle (64 requests, vocabulary 262,144, half greedy and half
             # rejection verification), with and without its 20 conv sites
@@ -330,7 +352,7 @@ def main():
                 sweep[STRESS + ("" if conv else " (no conv)")] = dict(
                     B=ws_.B, block=ws_.block, path=ws_.path_mode, verify=ws_.verify,
                     conv_sites=ws_.conv_sites if conv else 0, us_per_cycle=round(m2 * 1e3, 2),
-                    blocks_per_s=round(ws_.B / (m2 / 1e3), 1))
+                    blocks_per_s=round(ws_.B / (m2 / 1e3), 1), hbm_frac=hbm_frac(ws_, conv, m2 * 1e3))
                 del c2
             del E4
 
@@ -358,6 +380,8 @@ def main():
                    "step": "20 x dynconv2 + topk + pair_scores + path + verify, one HIP graph"},
         "tokens_scored_per_s": round(w.B * w.T * w.K / (ms / 1e3), 1),
         "value_without_conv": round(w.B / (ms_nc / 1e3), 1),
+        "hbm_frac": hbm_frac(w, True, ms * 1e3),
+        "hbm_frac_without_conv": hbm_frac(w, False, ms_nc * 1e3),
         "replay_ms": spread,
         "roofline": roof,
         "cpu_baseline": cpu,
