@@ -467,7 +467,8 @@ def _conv_gpu(x, xp, wt, base, y_dtype):
 
 
 @pytest.mark.parametrize("B,L,d,base,prev", [(1, 4, 64, True, True), (2, 16, 256, False, True),
-                                             (3, 5, 320, True, False), (32, 16, 5120, False, True)])
+                                             (3, 5, 320, True, False), (32, 16, 5120, False, True),
+                                             (65, 16, 1024, True, True)])
 def test_dynconv2_matches_oracle(B, L, d, base, prev):
     w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=L, d=d, conv_base=base)
     x, xp, wt, bs = synth.conv_site(w, 0)
