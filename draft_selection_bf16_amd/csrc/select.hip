@@ -211,7 +211,6 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
   }
   __syncthreads();
   const float* S = sS;
-  const int j = lane & 15;
   float total = 0.f;
 
   if (mode == 0) {  // VITERBI
