@@ -46,7 +46,7 @@ int dflash2_profile_start(const char* kernel, int max_launches) {
     hipEvent_t a, b;
     if (hipEventCreate(&a) != hipSuccess) return DF2_ERR_HIP;
     if (hipEventCreate(&b) != hipSuccess) {
-      hipEventDestroy(a);
+      (void)hipEventDestroy(a);
       return DF2_ERR_HIP;
     }
     P.start.push_back(a);
