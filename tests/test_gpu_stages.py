@@ -353,7 +353,8 @@ def _verify_greedy_gpu(Z, path_tok):
                                                ("ragged", 5, 7, 10007, torch.bfloat16),
                                                ("b32_blk16", 32, 15, 151936, torch.bfloat16),
                                                ("fp16", 3, 5, 5003, torch.float16),
-                                               ("t63", 2, 63, 3001, torch.bfloat16)])
+                                               ("t63", 2, 63, 3001, torch.bfloat16),
+                                               ("b1_blk8", 1, 7, 151936, torch.bfloat16)])
 def test_verify_greedy_exact(name, B, T, V, dtype):
     w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=T + 1, V=V)
     d_dev = DEV if V > 100000 else "cpu"
@@ -409,7 +410,8 @@ def _reject_case(B, T, V, tau, seed, sampled=True, dtype=torch.bfloat16):
 
 
 @pytest.mark.parametrize("B,T,V,tau,sampled", [(8, 7, 151936, 1.0, True), (16, 15, 20000, 0.7, True),
-                                               (16, 15, 20000, 1.0, False), (4, 3, 1000, 1.5, True)])
+                                               (16, 15, 20000, 1.0, False), (4, 3, 1000, 1.5, True),
+                                               (1, 7, 151936, 1.0, True)])
 def test_verify_reject_matches_oracle(B, T, V, tau, sampled):
     seed = 2
     Z, pth, idx = _reject_case(B, T, V, tau, seed, sampled)
