@@ -136,6 +136,38 @@ __device__ __forceinline__ bool better(float v1, int i1, float v0, int i0) {
   return v1 > v0 || (v1 == v0 && i1 < i0);
 }
 
+// Reductions over the 16 lanes of a DPP row (every row reduces its own lanes;
+// the caller reads row 0): two quad permutations, then rotations of the row
+// by 4 and 8.  The rotations associate sums differently in different lanes,
+// so callers take the result of one lane.
+template <int C, bool ZF = false>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), C, 0xF, 0xF, ZF));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dppf<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dppf<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dppf<0x124>(v));   // row_ror:4
+  return fmaxf(v, dppf<0x128>(v));   // row_ror:8
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf<0xB1>(v);
+  v += dppf<0x4E>(v);
+  v += dppf<0x124>(v);
+  return v + dppf<0x128>(v);
+}
+// Inclusive prefix sum over the lanes of a row: row_shr by 1, 2, 4, 8 with
+// zero fill (the additions of a Hillis-Steele scan in lane order).
+__device__ __forceinline__ float row16_prefix(float c) {
+  c += dppf<0x111, true>(c);
+  c += dppf<0x112, true>(c);
+  c += dppf<0x114, true>(c);
+  return c + dppf<0x118, true>(c);
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Keep the better of this lane's (value, rank) and that of the lane the DPP
 // quad permutation CTRL names (all lanes active).
 template <int CTRL>
@@ -288,16 +320,14 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
         pick = bi;
         if (w0 && lane < K) q[((int64_t)b * T + t) * K + lane] = lane == pick ? 1.f : 0.f;
       } else {  // SAMPLE
-        float mx = wave_max_f32(v);
+        // max, sum and prefix over the K <= 16 ranks (lanes 0..15, one DPP
+        // row); max and sum are taken from lane 0
+        const float mx = lane_value(row16_max(v), 0);
         float e = (lane < K) ? expf((v - mx) * inv_tau) : 0.f;
-        float z = wave_sum_f32(e);
+        const float z = lane_value(row16_sum(e), 0);
         float p = e / z;
         // inclusive prefix sum in rank order
-        float c = p;
-        for (int m = 1; m < 16; m <<= 1) {
-          float o = __shfl_up(c, m);
-          if (lane >= m) c += o;
-        }
+        float c = row16_prefix(p);
         float u = cycle_uniform(seed, b, t, 0);
         uint64_t over = ballot(lane < K && c > u);
         if (over) {
@@ -308,7 +338,7 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
         }
         if (w0 && lane < K) q[((int64_t)b * T + t) * K + lane] = p;
       }
-      float sv = __shfl(v, pick);
+      float sv = lane_value(v, pick);
       total = (t == 0) ? sv : total + sv;
       if (w0 && lane == 0) chosen[t] = pick;
       prev = pick;
