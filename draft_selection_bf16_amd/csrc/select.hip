@@ -169,9 +169,10 @@ __device__ __forceinline__ float lane_value(float v, int l) {
 }
 
 // Keep the better of this lane's (value, rank) and that of the lane the DPP
-// quad permutation CTRL names (all lanes active).
+// control CTRL names (a quad permutation or a row rotation; all lanes
+// active).
 template <int CTRL>
-__device__ __forceinline__ void quad_better(float& best, int& arg) {
+__device__ __forceinline__ void dpp_better(float& best, int& arg) {
   const float ob = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(best), CTRL, 0xF, 0xF, false));
   const int oa = __builtin_amdgcn_update_dpp(0, arg, CTRL, 0xF, 0xF, false);
   if (better(ob, oa, best, arg)) {
@@ -269,8 +270,8 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
           }
         }
       }
-      quad_better<0xB1>(best, arg);   // lane ^ 1
-      quad_better<0x4E>(best, arg);   // lane ^ 2
+      dpp_better<0xB1>(best, arg);   // lane ^ 1
+      dpp_better<0x4E>(best, arg);   // lane ^ 2
       if (gv == 0) {
         if (w0) psi[t][jv] = (uint8_t)arg;
         sD[wv][t & 1][jv] = jv < K ? best : -INFINITY;
@@ -278,17 +279,15 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
       __builtin_amdgcn_wave_barrier();
     }
     const float delta = sD[wv][(T - 1) & 1][lane & 15];
-    // end argmax over j (lowest rank on ties)
+    // end argmax over j (lowest rank on ties) across the 16 lanes of row 0:
+    // quad permutations, then row rotations (the pair order is total, so
+    // every lane of the row ends with the same best pair)
     float bv = (lane < K) ? delta : -INFINITY;
     int bi = lane < K ? lane : 64;
-    for (int m = 1; m < 16; m <<= 1) {
-      float ov = __shfl_xor(bv, m);
-      int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    dpp_better<0xB1>(bv, bi);
+    dpp_better<0x4E>(bv, bi);
+    dpp_better<0x124>(bv, bi);   // row_ror:4
+    dpp_better<0x128>(bv, bi);   // row_ror:8
     __syncthreads();
     if (w0 && lane == 0) {
       int c = bi;
