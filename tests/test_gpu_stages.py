@@ -272,6 +272,22 @@ def test_pair_scores_mid_with_intermediates(gate):
     report("pair_scores mid", worst_err_over_bound=round(worst, 4))
 
 
+@pytest.mark.parametrize("r,K", [(128, 16), (64, 7)])
+def test_pair_scores_other_ranks(r, K):
+    """Rank 128 (one W tile per half of [W_A; W_B]) and rank 64 with K = 7
+    (W_A and W_B projected as separate problems; ragged K x K lattices)."""
+    w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=2, V=3000, d=384, r=r, K=K)
+    z, _, _ = synth.drafter_logits(w)
+    idx, val = oracle.topk(z, K)
+    E = synth.embeddings(w)
+    wa, wb, wh = synth.selector_weights(w)
+    h, last = synth.context_hidden(w), synth.last_tokens(w)
+    Sg, _ = _pair_gpu(torch.from_numpy(idx), torch.from_numpy(val), last, E, h, wa, wb, wh)
+    So = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh)
+    worst = close(Sg, So)
+    report("pair_scores other ranks", r=r, K=K, worst_err_over_bound=round(worst, 4))
+
+
 def test_pair_scores_out_of_range_tokens_read_zero_rows():
     w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=1, V=512, d=128, r=32)
     E = synth.embeddings(w)
@@ -470,7 +486,8 @@ def _conv_gpu(x, xp, wt, base, y_dtype):
 
 @pytest.mark.parametrize("B,L,d,base,prev", [(1, 4, 64, True, True), (2, 16, 256, False, True),
                                              (3, 5, 320, True, False), (32, 16, 5120, False, True),
-                                             (65, 16, 1024, True, True)])
+                                             (65, 16, 1024, True, True), (2, 4, 8192, True, True),
+                                             (1, 3, 16384, False, True)])
 def test_dynconv2_matches_oracle(B, L, d, base, prev):
     w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=L, d=d, conv_base=base)
     x, xp, wt, bs = synth.conv_site(w, 0)
