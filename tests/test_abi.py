@@ -132,6 +132,23 @@ def test_verify_validation():
     assert L.dflash2_verify_reject(*args, 1.0, *tail[:-2], need - 1, None) == df2.DF2_ERR_WORKSPACE
 
 
+def test_empty_batch_is_a_no_op():
+    """A batch of zero requests is valid everywhere: each entry point checks
+    its sizes and returns DF2_OK before it touches a pointer or the runtime
+    (all data pointers here are NULL)."""
+    L = df2.lib()
+    assert L.dflash2_topk(None, 1, 0, 151936, 16, None, None, None, 0, None) == df2.DF2_OK
+    assert L.dflash2_pair_scores(None, None, None, None, 1, 151936, None, None, None, None, 0, 7, 16, 5120,
+                                 256, 0, None, None, 0, None) == df2.DF2_OK
+    for mode in (0, 1, 2):
+        assert L.dflash2_path_viterbi(None, None, 0, 7, 16, mode, 1.0, None, None, None, None, None,
+                                      None) == df2.DF2_OK
+    assert L.dflash2_dynconv2(None, None, None, None, 0, 16, 5120, 16, None, 1, None, 0, None) == df2.DF2_OK
+    assert L.dflash2_verify_greedy(None, 1, 151936, None, 0, 15, None, None, None, 0, None) == df2.DF2_OK
+    assert L.dflash2_verify_reject(None, 1, 151936, None, None, None, None, 0, 15, 16, 1.0, None, None,
+                                   None, None, 0, None) == df2.DF2_OK
+
+
 def test_philox_validation():
     L = df2.lib()
     assert L.dflash2_philox4x64(FAKE, FAKE, FAKE, -1, FAKE, None) == df2.DF2_ERR_SHAPE

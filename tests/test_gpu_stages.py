@@ -317,7 +317,7 @@ def _path_gpu(S, cand, mode, tau=0.0, seed=0):
 
 @pytest.mark.parametrize("B,T,K,ties", [(1, 3, 4, False), (32, 15, 16, False), (64, 15, 16, True),
                                         (8, 7, 16, True), (5, 1, 16, False), (3, 63, 16, False),
-                                        (7, 9, 5, True)])
+                                        (7, 9, 5, True), (3, 5, 1, False), (4, 6, 2, True)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_path_deterministic_modes_bit_exact(B, T, K, ties, mode):
     S = synth.pair_score_lattice(B, T, K, seed=B * 100 + T, ties=ties)
