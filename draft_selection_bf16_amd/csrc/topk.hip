@@ -299,24 +299,6 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
   const u32x4* vp = (const u32x4*)((const char*)rowp + a0 * esz);
   const int64_t ngroups = (a1 - a0) / VN;   // 16-byte groups
   const int64_t stride = (int64_t)kWaves * kWave;
-  if (ngroups > 0) {
-    // prime the threshold with the 16th best value among this wave's first
-    // 64 groups (NaN never qualifies); those entries are seen again below
-    const int64_t g = (int64_t)wave * kWave + lane;
-    const bool ok = g < ngroups;
-    const u32x4 v = __builtin_nontemporal_load(vp + (ok ? g : 0));
-    uint32_t ord[VN];
-#pragma unroll
-    for (int e = 0; e < VN; ++e) {
-      const float f = Vec<E>::get(v, e);
-      ord[e] = ok && f == f ? ord_of(f) : 0u;
-    }
-    const uint32_t t = value_cut16<VB, VN>(ord);
-    if (t != 0u) {
-      F.thr = fmaxf(F.thr, value_of_ord(t));
-      if (lane == 0) publish(F, wave);
-    }
-  }
   const int ng = (int)ngroups;   // < 2^31: rows hold < 2^32 entries
   // Software-pipelined over two register sets: the loads of the next
   // iteration are issued before this one's groups are tested (no register
@@ -368,7 +350,24 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
   u32x4 va[kUnroll], vb[kUnroll];
   bool oka[kUnroll], okb[kUnroll];
   int g0 = wave * kWave;
-  if (g0 < ng) load(g0, va, oka);
+  if (g0 < ng) {
+    load(g0, va, oka);
+    // prime the threshold with the 16th best value among this wave's first
+    // 64 groups -- the first group of the batch just issued (NaN never
+    // qualifies); only that load is waited for, and the scan sees these
+    // entries again below
+    uint32_t ord[VN];
+#pragma unroll
+    for (int e = 0; e < VN; ++e) {
+      const float f = Vec<E>::get(va[0], e);
+      ord[e] = oka[0] && f == f ? ord_of(f) : 0u;
+    }
+    const uint32_t t = value_cut16<VB, VN>(ord);
+    if (t != 0u) {
+      F.thr = fmaxf(F.thr, value_of_ord(t));
+      if (lane == 0) publish(F, wave);
+    }
+  }
   while (g0 < ng) {   // the same in all lanes
     if (g0 + step < ng) load(g0 + step, vb, okb);
     process(g0, va, oka);
