@@ -191,7 +191,9 @@ def source_hash():
     import glob
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "draft_selection_bf16_amd", "csrc", "*"))):
+    pkg = os.path.join(ROOT, "draft_selection_bf16_amd")
+    # the kernels are their sources plus the compiler flags they are built with
+    for f in sorted(glob.glob(os.path.join(pkg, "csrc", "*"))) + [os.path.join(pkg, "build.py")]:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read())
     return h.hexdigest()
