@@ -15,6 +15,10 @@ HBM bytes (logits, target logits, gathered embedding rows, context rows,
 selector weights and, with the conv sites, their x, x_prev, W and y) per
 second against the 8 TB/s peak, for the step and every sweep point;
 cpu_baseline times the CPU oracle on a bounded sample of the same workload.
+`tables` reports the same cycles with the pair scores read from per-token
+A/B tables built once per weight set (dflash2_selector_tables, timed on its
+own as `build_ms`); the headline value projects the embedding rows every
+cycle.
 """
 from __future__ import annotations
 
@@ -32,7 +36,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 STRESS = "b64_blk16_v262144_stress"
-KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm",
+KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm", "h_gemm",
                "proj_reduce", "pair_epilogue", "path", "argmax_part", "greedy_final",
                "sumexp_part", "reject_decide", "residual_chunk", "residual_find"]
 
@@ -45,6 +49,7 @@ def parse():
     ap.add_argument("--workload", default="b32_blk16_v151936_conv")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batch x block sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-tables", action="store_true", help="skip the per-token table cycles")
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="requests the oracle recomputes (0: all of the batch)")
@@ -58,7 +63,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_cycle(w, dev, E=None, conv=True):
+def build_cycle(w, dev, E=None, conv=True, tables=False):
     import torch
     import synth
     from draft_selection_bf16_amd.cycle import ConvSite, Cycle
@@ -76,7 +81,7 @@ def build_cycle(w, dev, E=None, conv=True):
             sites.append(ConvSite(x, xp, wt, bs, torch.empty(x.shape, dtype=torch.bfloat16, device=dev)))
     cyc = Cycle(logits=z, target=Z, emb=E, h=h, w_a=wa, w_b=wb, w_h=wh, last_tok=last, K=w.K,
                 path_mode=w.path_mode, verify=w.verify, tau=w.tau if w.tau > 0 else 1.0,
-                conv_sites=sites, seed=w.seed)
+                conv_sites=sites, seed=w.seed, tables=tables)
     return cyc, E
 
 
@@ -132,21 +137,77 @@ def profile_kernels(cyc, steps):
     return out
 
 
-def cycle_bytes(w, conv, esz=2):
+def cycle_bytes(w, conv, esz=2, tables=False):
     """Algorithmic HBM bytes of one cycle: the drafter and target logits, the
     gathered embedding rows of the candidates and last tokens, the context
     rows and the three selector weights, and, with the conv sites, each
-    site's x, x_prev, W and y."""
+    site's x, x_prev, W and y.  With per-token tables the candidates' and
+    last tokens' fp32 table rows and W_H replace the embedding rows and the
+    three weights."""
     B, T, K, V, d, r = w.B, w.T, w.K, w.V, w.d, w.r
-    by = B * T * V * esz + B * (T + 1) * V * esz + (B * T * K + B + B * T) * d * 2 + 3 * r * d * 2
+    by = B * T * V * esz + B * (T + 1) * V * esz
+    if tables:
+        by += (B * T * K + B) * 2 * r * 4 + B * T * d * 2 + r * d * 2
+    else:
+        by += (B * T * K + B + B * T) * d * 2 + 3 * r * d * 2
     if conv and w.conv_sites:
         L, G2 = w.block, 2 * (d // 16)
         by += w.conv_sites * (2 * B * L * d * 2 + B * d * 2 + G2 * d * 2)
     return by
 
 
-def hbm_frac(w, conv, us):
-    return round(cycle_bytes(w, conv) / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+def hbm_frac(w, conv, us, tables=False):
+    return round(cycle_bytes(w, conv, tables=tables) / (us * 1e-6) / (HBM_PEAK_GBS * 1e9), 4)
+
+
+def tables_leg(w, E, dev, steps, warmup, with_sweep):
+    """The cycle with per-token A/B tables: the one-off table build, the step
+    with and without the conv sites, per-kernel times and (with the sweep)
+    the two small-batch points."""
+    import torch
+    import draft_selection_bf16_amd as df2
+    out = {}
+    cyc, _ = build_cycle(w, dev, E=E, conv=True, tables=True)
+    wa, wb = cyc.w_a, cyc.w_b
+    tab = torch.empty_like(cyc.tab)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    df2.dflash2_selector_tables(E, wa, wb, tab)
+    a.record()
+    for _ in range(3):
+        df2.dflash2_selector_tables(E, wa, wb, tab)
+    b.record()
+    torch.cuda.synchronize()
+    build_ms = a.elapsed_time(b) / 3
+    out["build_ms"] = round(build_ms, 3)
+    out["build_tflops"] = round(2 * w.V * w.d * 2 * w.r / (build_ms * 1e-3) / 1e12, 1)
+    out["table_bytes"] = w.V * 2 * w.r * 4
+    del tab
+    cyc.capture()
+    ms, _ = time_graph(cyc, steps, warmup)
+    out["ms_per_step"] = round(ms, 5)
+    out["value"] = round(w.B / (ms / 1e3), 1)
+    out["hbm_frac"] = hbm_frac(w, True, ms * 1e3, tables=True)
+    out["kernels"] = {k: round(v["avg_us"], 2) for k, v in profile_kernels(cyc, min(steps, 50)).items()}
+    del cyc
+    cyc_nc, _ = build_cycle(w, dev, E=E, conv=False, tables=True)
+    cyc_nc.capture(conv=False)
+    ms_nc, _ = time_graph(cyc_nc, steps, warmup)
+    del cyc_nc
+    out["us_per_cycle_without_conv"] = round(ms_nc * 1e3, 2)
+    out["value_without_conv"] = round(w.B / (ms_nc / 1e3), 1)
+    out["hbm_frac_without_conv"] = hbm_frac(w, False, ms_nc * 1e3, tables=True)
+    if with_sweep:
+        import synth
+        sw = {}
+        for name in ("b1_blk8_v151936", "b8_blk8_v151936_sampled"):
+            ws_ = synth.WORKLOADS[name]
+            c2, _ = build_cycle(ws_, dev, E=E, conv=False, tables=True)
+            c2.capture(conv=False)
+            m2, _ = time_graph(c2, steps, warmup)
+            sw[name] = dict(us_per_cycle=round(m2 * 1e3, 2), blocks_per_s=round(ws_.B / (m2 / 1e3), 1))
+            del c2
+        out["sweep"] = sw
+    return out
 
 
 def algorithmic(w, tag, esz=2):
@@ -358,6 +419,11 @@ def main():
                 del c2
             del E4
 
+    tabs = None
+    if not args.no_tables:
+        log("per-token tables")
+        tabs = tables_leg(w, E, dev, args.steps, args.warmup, not args.no_sweep)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -389,6 +455,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "sweep": sweep,
+        "tables": tabs,
         "wall_s_timed": round(wall, 3),
     }
     s = json.dumps(line)

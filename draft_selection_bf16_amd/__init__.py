@@ -28,6 +28,7 @@ EXPORTS = [
     "dflash2_abi_version", "dflash2_status_string", "dflash2_last_error", "dflash2_init",
     "dflash2_topk_workspace_bytes", "dflash2_topk",
     "dflash2_pair_scores_workspace_bytes", "dflash2_pair_scores",
+    "dflash2_selector_tables", "dflash2_pair_scores_tab_workspace_bytes", "dflash2_pair_scores_tab",
     "dflash2_path_viterbi",
     "dflash2_dynconv2_workspace_bytes", "dflash2_dynconv2",
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
@@ -63,6 +64,10 @@ def lib():
         L.dflash2_pair_scores_workspace_bytes.argtypes = [I, I, I, I, I]
         L.dflash2_pair_scores_workspace_bytes.restype = SZ
         L.dflash2_pair_scores.argtypes = [P, P, P, P, I, I64, P, P, P, P, I, I, I, I, I, I, P, P, SZ, P]
+        L.dflash2_selector_tables.argtypes = [P, I, I64, I, P, P, I, P, P]
+        L.dflash2_pair_scores_tab_workspace_bytes.argtypes = [I, I, I, I]
+        L.dflash2_pair_scores_tab_workspace_bytes.restype = SZ
+        L.dflash2_pair_scores_tab.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, P, P, SZ, P]
         L.dflash2_path_viterbi.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P]
         L.dflash2_dynconv2_workspace_bytes.argtypes = [I, I, I, I]
         L.dflash2_dynconv2_workspace_bytes.restype = SZ
@@ -76,7 +81,8 @@ def lib():
         L.dflash2_profile_start.restype = I
         L.dflash2_profile_stop.argtypes = [P, I, P]
         L.dflash2_profile_stop.restype = I
-        for name in ("dflash2_topk", "dflash2_pair_scores", "dflash2_path_viterbi",
+        for name in ("dflash2_topk", "dflash2_pair_scores", "dflash2_selector_tables",
+                     "dflash2_pair_scores_tab", "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
@@ -147,6 +153,28 @@ def dflash2_pair_scores(cand_idx, cand_val, last_tok, emb, h, w_a, w_b, w_h, sco
                                      V, _ptr(h), _ptr(w_a), _ptr(w_b), _ptr(w_h), B, T, K, d, r,
                                      int(gate), _ptr(scores), _ptr(ws), _bytes(ws), _stream(stream)),
            "dflash2_pair_scores")
+
+
+def dflash2_selector_tables(emb, w_a, w_b, tab, stream=None):
+    """tab [V, 2r] fp32 <- [E W_A^T | E W_B^T] for every token."""
+    V, d = emb.shape
+    r = w_a.shape[0]
+    _check(lib().dflash2_selector_tables(_ptr(emb), _dt(emb), V, d, _ptr(w_a), _ptr(w_b), r, _ptr(tab),
+                                         _stream(stream)), "dflash2_selector_tables")
+
+
+def dflash2_pair_scores_tab_workspace_bytes(B, T, d, r) -> int:
+    return int(lib().dflash2_pair_scores_tab_workspace_bytes(B, T, d, r))
+
+
+def dflash2_pair_scores_tab(cand_idx, cand_val, last_tok, tab, h, w_h, scores, ws,
+                            gate=DF2_GATE_IDENTITY, stream=None):
+    B, T, K = cand_idx.shape
+    V, r2 = tab.shape
+    d = h.shape[-1]
+    _check(lib().dflash2_pair_scores_tab(_ptr(cand_idx), _ptr(cand_val), _ptr(last_tok), _ptr(tab), V,
+                                         _ptr(h), _ptr(w_h), B, T, K, d, r2 // 2, int(gate), _ptr(scores),
+                                         _ptr(ws), _bytes(ws), _stream(stream)), "dflash2_pair_scores_tab")
 
 
 def dflash2_path_viterbi(scores, cand_idx, mode, path_rank, path_tok, q, path_score=None,

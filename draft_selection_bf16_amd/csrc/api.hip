@@ -238,6 +238,113 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
                     "dflash2_pair_scores (epilogue)");
 }
 
+// ------------------------------------------------------------------ per-token tables
+// A(tok) and B(tok) depend on the token alone, so [A | B] can be computed
+// once for the whole vocabulary: one GEMM E [W_A; W_B]^T with thousands of
+// tiles and no split of the reduction over d.
+int dflash2_selector_tables(const void* emb, int emb_dt, int64_t vocab, int d, const void* w_a,
+                            const void* w_b, int r, float* tab, hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_selector_tables: embedding table must be BF16");
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_selector_tables: d %d is not a positive multiple of 64", d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_selector_tables: r %d not a multiple of 16 in [16, 256]", r);
+  REQUIRE(vocab >= 0 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_selector_tables: vocab %lld", (long long)vocab);
+  REQUIRE((uint64_t)vocab * (uint64_t)d * 2u < (1ull << 32), DF2_ERR_UNSUPPORTED,
+          "dflash2_selector_tables: embedding table of %lld x %d bf16 is 4 GiB or more", (long long)vocab, d);
+  if (vocab == 0) return DF2_OK;
+  REQUIRE(emb && w_a && w_b && tab, DF2_ERR_NULL, "dflash2_selector_tables: null pointer argument");
+  REQUIRE(aligned16(emb) && aligned16(w_a) && aligned16(w_b) && aligned16(tab), DF2_ERR_SHAPE,
+          "dflash2_selector_tables: emb/w_a/w_b/tab must be 16-byte aligned");
+  GemmSeg s[2] = {};
+  s[0].x = (const uint16_t*)emb;
+  s[0].gather = nullptr;
+  s[0].x_rows = vocab;
+  s[0].ldx = d;
+  s[0].M = (int)vocab;
+  s[0].w0 = (const uint16_t*)w_a;
+  s[0].w1 = (const uint16_t*)w_b;
+  s[0].n0 = r;
+  s[0].N = 2 * r;
+  s[0].out = tab;
+  s[0].ldo = 2 * r;
+  s[0].out_kstride = 0;
+  s[0].gate = DF2_GATE_IDENTITY;
+  int nseg = 1;
+  if (r % 128 != 0) {   // W tiles may not straddle W_A / W_B
+    s[1] = s[0];
+    s[0].w1 = s[0].w0;
+    s[0].N = r;
+    s[1].w0 = s[1].w1 = (const uint16_t*)w_b;
+    s[1].N = r;
+    s[1].out = tab + r;
+    nseg = 2;
+  }
+  return hip_status(launch_gemm(s, nseg, d, 1, kProjTiling, "table_gemm", stream), "dflash2_selector_tables");
+}
+
+namespace {
+// Per cycle only H = W_H h is projected: B*T rows, a skinny product whose
+// reduction over d is split so that about one work-group per CU takes part
+// (64 x 128 tiles; slices of >= 4 K-tiles, at most kMaxHSplit), then summed
+// in slice order by the reduce pass.
+constexpr GemmTiling kHTiling{64, 128, 3, 4};
+constexpr int kMaxHSplit = 16;
+int h_split(int B, int T, int d, int r) {
+  const int tiles = ((B * T + kHTiling.bm - 1) / kHTiling.bm) * ((r + kHTiling.bn - 1) / kHTiling.bn);
+  int ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks > d / 64 / 4) ks = d / 64 / 4;
+  if (ks > kMaxHSplit) ks = kMaxHSplit;
+  return ks < 1 ? 1 : ks;
+}
+}  // namespace
+
+size_t dflash2_pair_scores_tab_workspace_bytes(int B, int T, int d, int r) {
+  if (B <= 0 || T <= 0 || r <= 0 || d < 64) return 0;
+  return align256((size_t)h_split(B, T, d, r) * (size_t)B * T * r * sizeof(float));
+}
+
+int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                            const float* tab, int64_t vocab, const void* h, const void* w_h, int B, int T,
+                            int K, int d, int r, int gate, float* scores, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: K %d not in [1, 16]", K);
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: d %d is not a positive multiple of 64", d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: r %d not a multiple of 16 in [16, 256]", r);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: vocab %lld", (long long)vocab);
+  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores_tab: gate %d", gate);
+  if (B == 0) return DF2_OK;
+  REQUIRE(cand_idx && cand_val && last_tok && tab && h && w_h && scores, DF2_ERR_NULL,
+          "dflash2_pair_scores_tab: null pointer argument");
+  REQUIRE(aligned16(tab) && aligned16(h) && aligned16(w_h), DF2_ERR_SHAPE,
+          "dflash2_pair_scores_tab: tab/h/w_h must be 16-byte aligned");
+  const int split = h_split(B, T, d, r);
+  const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
+  REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_pair_scores_tab: workspace %zu < %zu bytes",
+          ws_bytes, need);
+  float* hg = (float*)ws;
+  const int64_t h_k = (int64_t)B * T * r;
+  GemmSeg s = {};
+  s.x = (const uint16_t*)h;
+  s.gather = nullptr;
+  s.x_rows = (int64_t)B * T;
+  s.ldx = d;
+  s.M = B * T;
+  s.w0 = (const uint16_t*)w_h;
+  s.w1 = (const uint16_t*)w_h;
+  s.n0 = r;
+  s.N = r;
+  s.out = hg;
+  s.ldo = r;
+  s.out_kstride = h_k;
+  s.gate = DF2_GATE_IDENTITY;
+  hipError_t e = launch_gemm(&s, 1, d, split, kHTiling, "h_gemm", stream);
+  if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores_tab (projection)");
+  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, hg, split, h_k, gate, cand_val,
+                                             B, T, K, r, scores, stream),
+                    "dflash2_pair_scores_tab (epilogue)");
+}
+
 // ------------------------------------------------------------------ path
 int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
                          float temperature, const uint64_t* seed_dev, int32_t* path_rank,

@@ -6,7 +6,10 @@
 // one work-group per (request, position); the predecessor rows A(a) (the
 // candidates of position t-1, or the last verified token at t = 0) are
 // scaled by the gate H_t once in LDS, then each of the K x K threads takes
-// one r-long dot product with B(b).  fp32 throughout.
+// one r-long dot product with B(b).  fp32 throughout.  A and B are functions
+// of the token alone (same section: every token gets its own compact
+// vectors), so their rows come either from this cycle's projection of the
+// gathered embedding rows or from a per-token table built once.
 //
 // Path (same section; and "DFlash 2 讓 Qwen3.8-27B 快了兩倍", item 2 --
 // Viterbi): one work-group per request, whose first wave runs the
@@ -59,11 +62,20 @@ __global__ __launch_bounds__(64) void slice_reduce_kernel(float* __restrict__ p0
   *(f32x4*)q = acc;
 }
 
+// TAB = false: ab holds the projected [A | B] row of every candidate
+// (B*T*K rows of 2r floats) and a_last the A row of each request's last
+// token.  TAB = true: ab is the per-token table [vocab, 2r] and rows are
+// addressed by token id (cand_idx, last_tok); ids outside [0, vocab) read
+// zeros, as the projection does for them.
+template <bool TAB>
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
                                                             const float* __restrict__ h_part,
                                                             int gate,
                                                             const float* __restrict__ cand_val,
+                                                            const int32_t* __restrict__ cand_idx,
+                                                            const int32_t* __restrict__ last_tok,
+                                                            int64_t vocab,
                                                             int T, int K, int r,
                                                             float* __restrict__ scores) {
   // rows padded to kLd floats: 16-byte aligned, and 16 rows at one column
@@ -89,12 +101,23 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     gq[u] = e % r4;
     ga[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (gi[u] < npred) {
-      const float* src = t == 0 ? a_last + (int64_t)b * r
-                                : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
-      ga[u] = *(const f32x4*)(src + 4 * gq[u]);
+    if (TAB) {
+      if (gi[u] < npred) {
+        const int64_t id = t == 0 ? last_tok[b] : cand_idx[(int64_t)(bt - 1) * K + gi[u]];
+        if (id >= 0 && id < vocab) ga[u] = *(const f32x4*)(ab + id * (2 * r) + 4 * gq[u]);
+      }
+      if (gi[u] < K) {
+        const int64_t id = cand_idx[(int64_t)bt * K + gi[u]];
+        if (id >= 0 && id < vocab) gb[u] = *(const f32x4*)(ab + id * (2 * r) + r + 4 * gq[u]);
+      }
+    } else {
+      if (gi[u] < npred) {
+        const float* src = t == 0 ? a_last + (int64_t)b * r
+                                  : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
+        ga[u] = *(const f32x4*)(src + 4 * gq[u]);
+      }
+      if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
     }
-    if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -372,8 +395,25 @@ hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
                    ab, n0, ab_k, a_last, n1, alast_k, h, n2, h_k, split));
   }
   ProfileScope ps("pair_epilogue", stream);
-  DF2_TRY(launch(pair_epilogue_kernel, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, gate, cand_val,
-                 T, K, r, scores));
+  DF2_TRY(launch(pair_epilogue_kernel<false>, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, gate,
+                 cand_val, (const int32_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, T, K, r, scores));
+  return hipGetLastError();
+}
+
+hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32_t* cand_idx,
+                                    const int32_t* last_tok, float* h, int split, int64_t h_k, int gate,
+                                    const float* cand_val, int B, int T, int K, int r, float* scores,
+                                    hipStream_t stream) {
+  if (B * T == 0) return hipSuccess;
+  if (split > 1) {
+    const int64_t n = (int64_t)B * T * r / 4;
+    ProfileScope pr("proj_reduce", stream);
+    DF2_TRY(launch(slice_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, pr,
+                   h, n, h_k, h, (int64_t)0, h_k, h, (int64_t)0, h_k, split));
+  }
+  ProfileScope ps("pair_epilogue", stream);
+  DF2_TRY(launch(pair_epilogue_kernel<true>, dim3(B * T), dim3(256), 0, stream, ps, tab, (const float*)nullptr,
+                 h, gate, cand_val, cand_idx, last_tok, vocab, T, K, r, scores));
   return hipGetLastError();
 }
 

@@ -12,7 +12,9 @@ library; their outputs (block logits, hidden states, target logits) are
 inputs here.
 
 All output and scratch buffers are allocated once, before any capture, so a
-captured cycle allocates nothing.  The sampling seed lives in device memory
+captured cycle allocates nothing.  With `tables=True` the per-token A/B
+table [V, 2r] is built once at construction (dflash2_selector_tables) and
+each cycle scores pairs from it (dflash2_pair_scores_tab).  The sampling seed lives in device memory
 (`seed`), so a replay can run with a fresh seed written between replays.
 """
 from __future__ import annotations
@@ -24,7 +26,8 @@ import torch
 
 from . import (DF2_GATE_IDENTITY, DF2_PATH_GREEDY, DF2_PATH_SAMPLE, DF2_PATH_VITERBI,
                dflash2_dynconv2, dflash2_dynconv2_workspace_bytes, dflash2_init,
-               dflash2_pair_scores, dflash2_pair_scores_workspace_bytes, dflash2_path_viterbi,
+               dflash2_pair_scores, dflash2_pair_scores_tab, dflash2_pair_scores_tab_workspace_bytes,
+               dflash2_pair_scores_workspace_bytes, dflash2_path_viterbi, dflash2_selector_tables,
                dflash2_topk, dflash2_topk_workspace_bytes, dflash2_verify_greedy,
                dflash2_verify_reject, dflash2_verify_workspace_bytes)
 
@@ -50,13 +53,15 @@ class Cycle:
     """Static-buffer cycle for fixed shapes.
 
     verify: "greedy" | "reject" | "mixed" (first `greedy_rows` requests greedy,
-    the rest rejection sampling).
+    the rest rejection sampling).  tables: score pairs from per-token A/B
+    tables built once here, instead of projecting the candidates' embedding
+    rows every cycle.
     """
 
     def __init__(self, *, logits, target, emb, h, w_a, w_b, w_h, last_tok, K: int,
                  path_mode: str, verify: str, tau: float = 1.0, gate: int = DF2_GATE_IDENTITY,
                  conv_sites: Optional[List[ConvSite]] = None, greedy_rows: Optional[int] = None,
-                 seed: int = 0):
+                 seed: int = 0, tables: bool = False):
         dflash2_init()
         dev = logits.device
         self.B, self.T, self.V = logits.shape
@@ -80,7 +85,13 @@ class Cycle:
         self.out_tok = torch.empty((B, T + 1), **i32)
         self.seed = torch.full((1,), int(seed), dtype=torch.int64, device=dev)
         self.ws_topk = _ws(dflash2_topk_workspace_bytes(B * T, V, K), dev)
-        self.ws_pair = _ws(dflash2_pair_scores_workspace_bytes(B, T, K, self.d, self.r), dev)
+        self.tab = None
+        if tables:
+            self.tab = torch.empty((V, 2 * self.r), **f32)
+            dflash2_selector_tables(emb, w_a, w_b, self.tab)
+            self.ws_pair = _ws(dflash2_pair_scores_tab_workspace_bytes(B, T, self.d, self.r), dev)
+        else:
+            self.ws_pair = _ws(dflash2_pair_scores_workspace_bytes(B, T, K, self.d, self.r), dev)
         self.ws_verify = _ws(dflash2_verify_workspace_bytes(B, T, V), dev)
         conv_bytes = 0
         for s in self.conv_sites:
@@ -98,6 +109,10 @@ class Cycle:
         dflash2_topk(self.logits, self.K, self.cand_idx, self.cand_val, self.ws_topk)
 
     def run_pair_scores(self):
+        if self.tab is not None:
+            dflash2_pair_scores_tab(self.cand_idx, self.cand_val, self.last_tok, self.tab, self.h, self.w_h,
+                                    self.scores, self.ws_pair, gate=self.gate)
+            return
         dflash2_pair_scores(self.cand_idx, self.cand_val, self.last_tok, self.emb, self.h, self.w_a,
                             self.w_b, self.w_h, self.scores, self.ws_pair, gate=self.gate)
 

@@ -10,6 +10,8 @@
  *                          sublayer)
  *   dflash2_topk           keep the K best candidates of every draft position
  *   dflash2_pair_scores    score every adjacent candidate pair
+ *   dflash2_selector_tables  per-token A/B tables, once per weight set
+ *   dflash2_pair_scores_tab  the pair scores with A/B read from those tables
  *   dflash2_path_viterbi   pick one path through the K x K lattices
  *   dflash2_verify_greedy  accept the longest prefix the target agrees with
  *   dflash2_verify_reject  speculative rejection sampling with a residual draw
@@ -123,6 +125,33 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
                         const void* emb, int emb_dt, int64_t vocab, const void* h, const void* w_a,
                         const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
                         int gate, float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Per-token selector tables.  [KDP] "A lightweight path selector": A and B
+ * give every token its own compact rank-r vectors, so they depend on the
+ * token alone and can be computed once per weight set:
+ *   tab[v] = [ W_A E[v] | W_B E[v] ]      for every v in [0, vocab)
+ *   emb  [vocab, d] bf16 (emb_dt = DF2_BF16), w_a, w_b [r, d] bf16
+ *   tab  [vocab, 2r] float, caller-owned (vocab * 2r * 4 bytes, 16-byte
+ *        aligned): A in columns 0..r-1, B in columns r..2r-1.
+ * Same limits and arithmetic as dflash2_pair_scores (fp32 accumulation of
+ * bf16 products; the rows equal that call's A and B up to summation order).
+ * No workspace.  vocab = 0 is a no-op.
+ *
+ * dflash2_pair_scores_tab computes the same scores as dflash2_pair_scores
+ * with A and B read from such a table: per call only H = gate(W_H h_t) is
+ * projected (ws: dflash2_pair_scores_tab_workspace_bytes, H's partial
+ * products over d).  cand_idx, cand_val, last_tok, h, w_h, scores, gate
+ * and the limits are those of dflash2_pair_scores; tab [vocab, 2r] float as
+ * above.  Token ids outside [0, vocab) read zero A and B rows.
+ * ------------------------------------------------------------------------ */
+int dflash2_selector_tables(const void* emb, int emb_dt, int64_t vocab, int d, const void* w_a,
+                            const void* w_b, int r, float* tab, hipStream_t stream);
+size_t dflash2_pair_scores_tab_workspace_bytes(int B, int T, int d, int r);
+int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                            const float* tab, int64_t vocab, const void* h, const void* w_h, int B, int T,
+                            int K, int d, int r, int gate, float* scores, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Path through the lattice.

@@ -7,7 +7,9 @@ raw 16-bit patterns.  Every function returns fresh numpy outputs.
 
 Parity status per function (details in the C source):
   topk, project, pair_scores, path, verify_greedy, verify_reject, dynconv2,
-  philox -- all pinned by the CPU tests in tests/test_oracle_*.py.
+  philox -- all pinned by the CPU tests in tests/test_oracle_*.py;
+  selector_tables, pair_scores_tab (numpy, below) -- pinned by
+  tests/test_oracle_tables.py.
 """
 from __future__ import annotations
 
@@ -166,6 +168,55 @@ def pair_scores(cand_idx, cand_val, last_tok, emb, h, w_a, w_b, w_h, gate: int =
     if intermediates:
         return S, dict(a_last=outs[0], a_cand=outs[1], b_cand=outs[2], h=outs[3])
     return S
+
+
+def selector_tables(emb, w_a, w_b, rows=None) -> np.ndarray:
+    """Per-token rows of the selector: "DFlash 2: Keep Drafting Parallel",
+    section "A lightweight path selector" gives every token its own compact
+    rank-r vectors A(tok) and B(tok), read as A(v) = W_A E[v] and
+    B(v) = W_B E[v].  Returns [A(v) | B(v)] in float64 for the token ids
+    `rows` (default: every token), one row per id.  emb: torch bf16 [V, d];
+    w_a, w_b: bf16 [r, d]."""
+    import torch
+    V = emb.shape[0]
+    ids = torch.arange(V) if rows is None else torch.as_tensor(np.asarray(rows, np.int64))
+    sub = emb[ids]
+    return np.concatenate([project(sub, w_a), project(sub, w_b)], axis=1)
+
+
+def pair_scores_tab(cand_idx, cand_val, last_tok, tab, h, w_h, gate: int = GATE_IDENTITY) -> np.ndarray:
+    """Pair scores with A and B read from a per-token table: same section,
+    equation S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>, where row v of
+    tab [V, 2r] is [A(v) | B(v)] and ids outside [0, V) read zero rows.  At
+    t = 0 the only predecessor is the last verified token (row a = 0, rows
+    a >= 1 are -inf); for t >= 1 a ranges over the candidates of t - 1.
+    H = gate(W_H h_t) by project().  Sums in float64, rounded once to
+    float32."""
+    ci = np.asarray(host(cand_idx)[0], np.int64)
+    U = np.asarray(host(cand_val)[0], np.float64)
+    lt = np.asarray(host(last_tok)[0], np.int64)
+    tb = np.asarray(host(tab)[0], np.float64)
+    V, r2 = tb.shape
+    r = r2 // 2
+    B, T, K = ci.shape
+    d = h.shape[-1]
+    H = project(h.reshape(B * T, d), w_h, gate).reshape(B, T, r)
+
+    def rows(ids):
+        out = np.zeros(ids.shape + (r2,))
+        ok = (ids >= 0) & (ids < V)
+        out[ok] = tb[ids[ok]]
+        return out
+    cand_rows = rows(ci)
+    A_c, B_c = cand_rows[..., :r], cand_rows[..., r:]
+    A_last = rows(lt)[:, :r]
+    S = np.full((B, T, K, K), -np.inf)
+    for b in range(B):
+        for t in range(T):
+            pred = A_last[b][None, :] if t == 0 else A_c[b, t - 1]     # [P, r]
+            bigram = (pred * H[b, t][None, :]) @ B_c[b, t].T          # [P, K]
+            S[b, t, :pred.shape[0], :] = U[b, t][None, :] + bigram
+    return S.astype(np.float32)
 
 
 def _bids(b_ids, B):

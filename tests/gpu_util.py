@@ -64,6 +64,18 @@ def conv_error_bound(x, x_prev, w, base=None, group: int = 16) -> np.ndarray:
     return dc0 * np.abs(xf) + dc1 * np.abs(xm1) + 5 * U32 * (t0 + t1)
 
 
+def gemm_error_bound(x, w) -> np.ndarray:
+    """Element-wise bound on |fp32 (x w^T) - exact| for bf16 x [n, d] and w
+    [m, d]: every product of two bf16 values is exact in fp32, so a sum of d
+    of them, in any order or blocking, is within gamma_d * sum_i |x_i w_i|,
+    gamma_d = d u / (1 - d u) (Higham, Accuracy and Stability of Numerical
+    Algorithms, Thm. 3.1)."""
+    xf = np.asarray(x.float().numpy() if hasattr(x, "float") else x, np.float64)
+    wf = np.asarray(w.float().numpy() if hasattr(w, "float") else w, np.float64)
+    d = xf.shape[-1]
+    return d * U32 / (1 - d * U32) * (np.abs(xf) @ np.abs(wf).T)
+
+
 def conv_close(g, o, bound) -> float:
     """fp32 conv output within the arithmetic bound of conv_error_bound."""
     g = np.asarray(g, np.float64)

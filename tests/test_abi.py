@@ -75,6 +75,40 @@ def test_pair_scores_validation():
     assert L.dflash2_pair_scores(*args(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
 
 
+def test_selector_tables_validation():
+    L = df2.lib()
+    args = lambda **kw: [kw.get("emb", FAKE), kw.get("edt", 1), kw.get("V", 151936), kw.get("d", 5120), FAKE,
+                         FAKE, kw.get("r", 256), kw.get("tab", FAKE), None]
+    assert L.dflash2_selector_tables(*args(edt=0)) == df2.DF2_ERR_DTYPE
+    assert L.dflash2_selector_tables(*args(d=100)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_selector_tables(*args(r=8)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_selector_tables(*args(r=272)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_selector_tables(*args(V=-1)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_selector_tables(*args(V=1 << 20, d=4096)) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_selector_tables(*args(tab=None)) == df2.DF2_ERR_NULL
+    assert L.dflash2_selector_tables(*args(tab=C.c_void_p(0x100004))) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_selector_tables(None, 1, 0, 5120, None, None, 256, None, None) == df2.DF2_OK
+
+
+def test_pair_scores_tab_validation():
+    L = df2.lib()
+    need = df2.dflash2_pair_scores_tab_workspace_bytes(32, 16, 5120, 256)
+    assert need > 0
+    assert need < df2.dflash2_pair_scores_workspace_bytes(32, 16, 16, 5120, 256)
+    args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, kw.get("tab", FAKE), 151936, FAKE, FAKE,
+                         kw.get("B", 32), kw.get("T", 16), kw.get("K", 16), kw.get("d", 5120),
+                         kw.get("r", 256), kw.get("gate", 0), FAKE, FAKE, kw.get("ws", need), None]
+    assert L.dflash2_pair_scores_tab(*args(T=0)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(T=64)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(K=17)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(d=96)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(r=20)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(gate=2)) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_pair_scores_tab(*args(tab=None)) == df2.DF2_ERR_NULL
+    assert L.dflash2_pair_scores_tab(*args(tab=C.c_void_p(0x100008))) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab(*args(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+
+
 def test_path_validation():
     L = df2.lib()
     assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
@@ -143,6 +177,8 @@ def test_empty_batch_is_a_no_op():
     for mode in (0, 1, 2):
         assert L.dflash2_path_viterbi(None, None, 0, 7, 16, mode, 1.0, None, None, None, None, None,
                                       None) == df2.DF2_OK
+    assert L.dflash2_pair_scores_tab(None, None, None, None, 151936, None, None, 0, 7, 16, 5120, 256, 0, None,
+                                     None, 0, None) == df2.DF2_OK
     assert L.dflash2_dynconv2(None, None, None, None, 0, 16, 5120, 16, None, 1, None, 0, None) == df2.DF2_OK
     assert L.dflash2_verify_greedy(None, 1, 151936, None, 0, 15, None, None, None, 0, None) == df2.DF2_OK
     assert L.dflash2_verify_reject(None, 1, 151936, None, None, None, None, 0, 15, 16, 1.0, None, None,

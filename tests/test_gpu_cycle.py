@@ -21,7 +21,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def build(w, with_conv=None, y_dtype=torch.bfloat16):
+def build(w, with_conv=None, y_dtype=torch.bfloat16, tables=False):
     """Inputs for workload w on the GPU, and the Cycle that runs them."""
     z, tok, rank = synth.drafter_logits(w, device=DEV)
     Z = synth.target_logits(w, z, tok, device=DEV)
@@ -37,7 +37,7 @@ def build(w, with_conv=None, y_dtype=torch.bfloat16):
     path_mode = "viterbi" if w.path_mode == "both" else w.path_mode
     cyc = Cycle(logits=z, target=Z, emb=E, h=h, w_a=wa, w_b=wb, w_h=wh, last_tok=last, K=w.K,
                 path_mode=path_mode, verify=w.verify, tau=w.tau if w.tau > 0 else 1.0,
-                conv_sites=sites, seed=w.seed)
+                conv_sites=sites, seed=w.seed, tables=tables)
     return cyc, dict(tok=tok, rank=rank)
 
 
@@ -165,6 +165,26 @@ def test_cycle_b32_blk16_conv_full_size():
     cyc, _ = build(w)
     cyc.run()
     check_cycle(cyc, w, [0, 13, 31], w.name, check_conv_sites=(0, 7, 19))
+
+
+def test_cycle_b32_blk16_tables_graph():
+    """The batch-32 / block-16 cycle with pair scores read from per-token
+    tables (built once), captured as a graph and replayed: the same checks
+    against the oracle's own cycle, which projects the embedding rows."""
+    w = synth.WORKLOADS["b32_blk16_v151936_conv"]
+    print(f"[case] {w.name} tables graph", flush=True)
+    cyc, _ = build(w, with_conv=0, tables=True)
+    cyc.capture(conv=False)
+    for _ in range(3):
+        cyc.replay()
+    check_cycle(cyc, w, [0, 13, 31], w.name + " tables")
+
+
+def test_cycle_b8_blk8_sampled_tables():
+    w = synth.WORKLOADS["b8_blk8_v151936_sampled"]
+    cyc, _ = build(w, tables=True)
+    cyc.run()
+    check_cycle(cyc, w, list(range(8)), w.name + " tables")
 
 
 def test_graph_replay_equals_eager_and_is_deterministic():
