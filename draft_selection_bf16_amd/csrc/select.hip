@@ -64,9 +64,12 @@ __global__ __launch_bounds__(64) void slice_reduce_kernel(float* __restrict__ p0
 
 // TAB = false: ab holds the projected [A | B] row of every candidate
 // (B*T*K rows of 2r floats) and a_last the A row of each request's last
-// token.  TAB = true: ab is the per-token table [vocab, 2r] and rows are
-// addressed by token id (cand_idx, last_tok); ids outside [0, vocab) read
-// zeros, as the projection does for them.
+// token; H is already summed over its slices.  TAB = true: ab is the
+// per-token table [vocab, 2r] and rows are addressed by token id (cand_idx,
+// last_tok); ids outside [0, vocab) read zeros, as the projection does for
+// them.  H arrives as hsplit slices of partial products (h_k floats apart):
+// the first r/4 threads request them before the id-dependent table loads,
+// add them in slice order and gate the sum into LDS.
 template <bool TAB>
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
                                                             const float* __restrict__ cand_val,
                                                             const int32_t* __restrict__ cand_idx,
                                                             const int32_t* __restrict__ last_tok,
-                                                            int64_t vocab,
+                                                            int64_t vocab, int hsplit, int64_t h_k,
                                                             int T, int K, int r,
                                                             float* __restrict__ scores) {
   // rows padded to kLd floats: 16-byte aligned, and 16 rows at one column
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
   constexpr int kLd = kMaxR + 4;
   __shared__ __attribute__((aligned(16))) float sG[16 * kLd];   // A(pred) * H_t
   __shared__ __attribute__((aligned(16))) float sB[16 * kLd];   // B(cand)
+  __shared__ __attribute__((aligned(16))) float sH[TAB ? kMaxR : 4];   // gated H_t (TAB)
   const int bt = blockIdx.x, b = bt / T, t = bt % T;
   const int tid = threadIdx.x;
   const int npred = t == 0 ? 1 : K;
@@ -91,6 +95,14 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
   // U_t(b) of this thread's output, requested before the staging loads
   const int oi = tid / 16, oj = tid % 16;
   const float u_j = (oi < K && oj < K) ? cand_val[(int64_t)bt * K + oj] : 0.f;
+  // TAB: the first block of H slices, requested before the table loads
+  const bool hthr = TAB && tid < r4;
+  const float* hp = Hp + 4 * (hthr ? tid : 0);
+  f32x4 hv[8];
+  if (hthr) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) hv[u] = *(const f32x4*)(hp + (int64_t)(u < hsplit ? u : 0) * h_k);
+  }
   // each thread stages up to 4 float4 of G and 4 of B (16 rows x 64 float4)
   f32x4 ga[4], gb[4];
   int gi[4], gq[4];
@@ -119,15 +131,39 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
       if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
     }
   }
+  if (TAB) {
+    if (hthr) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (u < hsplit) acc += hv[u];
+      for (int s0 = 8; s0 < hsplit; s0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) hv[u] = *(const f32x4*)(hp + (int64_t)(s0 + u < hsplit ? s0 + u : 0) * h_k);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < hsplit) acc += hv[u];
+      }
+      if (gate == 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = 1.0f / (1.0f + expf(-acc[e]));
+      *(f32x4*)&sH[4 * tid] = acc;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if (gi[u] < 16) {
       f32x4 h = f32x4{0.f, 0.f, 0.f, 0.f};
       if (gi[u] < npred) {
-        h = *(const f32x4*)(Hp + 4 * gq[u]);
-        if (gate == 1)
+        if (TAB) {
+          h = *(const f32x4*)&sH[4 * gq[u]];
+        } else {
+          h = *(const f32x4*)(Hp + 4 * gq[u]);
+          if (gate == 1)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) h[e] = 1.0f / (1.0f + expf(-h[e]));
+            for (int e = 0; e < 4; ++e) h[e] = 1.0f / (1.0f + expf(-h[e]));
+        }
       }
       *(f32x4*)&sG[gi[u] * kLd + 4 * gq[u]] = ga[u] * h;
       *(f32x4*)&sB[gi[u] * kLd + 4 * gq[u]] = gb[u];
@@ -396,7 +432,8 @@ hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
   }
   ProfileScope ps("pair_epilogue", stream);
   DF2_TRY(launch(pair_epilogue_kernel<false>, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, gate,
-                 cand_val, (const int32_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, T, K, r, scores));
+                 cand_val, (const int32_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, 1, (int64_t)0, T, K, r,
+                 scores));
   return hipGetLastError();
 }
 
@@ -405,15 +442,9 @@ hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32
                                     const float* cand_val, int B, int T, int K, int r, float* scores,
                                     hipStream_t stream) {
   if (B * T == 0) return hipSuccess;
-  if (split > 1) {
-    const int64_t n = (int64_t)B * T * r / 4;
-    ProfileScope pr("proj_reduce", stream);
-    DF2_TRY(launch(slice_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, pr,
-                   h, n, h_k, h, (int64_t)0, h_k, h, (int64_t)0, h_k, split));
-  }
   ProfileScope ps("pair_epilogue", stream);
   DF2_TRY(launch(pair_epilogue_kernel<true>, dim3(B * T), dim3(256), 0, stream, ps, tab, (const float*)nullptr,
-                 h, gate, cand_val, cand_idx, last_tok, vocab, T, K, r, scores));
+                 h, gate, cand_val, cand_idx, last_tok, vocab, split, h_k, T, K, r, scores));
   return hipGetLastError();
 }
 
