@@ -113,16 +113,33 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     gq[u] = e % r4;
     ga[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     gb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (TAB) {
-      if (gi[u] < npred) {
-        const int64_t id = t == 0 ? last_tok[b] : cand_idx[(int64_t)(bt - 1) * K + gi[u]];
-        if (id >= 0 && id < vocab) ga[u] = *(const f32x4*)(ab + id * (2 * r) + 4 * gq[u]);
-      }
-      if (gi[u] < K) {
-        const int64_t id = cand_idx[(int64_t)bt * K + gi[u]];
-        if (id >= 0 && id < vocab) gb[u] = *(const f32x4*)(ab + id * (2 * r) + r + 4 * gq[u]);
-      }
-    } else {
+  }
+  if (TAB) {
+    // every id, then every table row, requested unconditionally (clamped
+    // indices; rows that do not count are loaded from row 0 and dropped), so
+    // each round has one wait
+    const int32_t* pbase = t == 0 ? last_tok + b : cand_idx + (int64_t)(bt - 1) * K;
+    const int32_t* cbase = cand_idx + (int64_t)bt * K;
+    int32_t pid[4], cid[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gc = gi[u] < K ? gi[u] : K - 1;
+      pid[u] = pbase[t == 0 ? 0 : gc];
+      cid[u] = cbase[gc];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool okp = gi[u] < npred && pid[u] >= 0 && pid[u] < vocab;
+      const bool okc = gi[u] < K && cid[u] >= 0 && cid[u] < vocab;
+      const f32x4 va = *(const f32x4*)(ab + (int64_t)(okp ? pid[u] : 0) * (2 * r) + 4 * gq[u]);
+      const f32x4 vb = *(const f32x4*)(ab + (int64_t)(okc ? cid[u] : 0) * (2 * r) + r + 4 * gq[u]);
+      if (okp) ga[u] = va;
+      if (okc) gb[u] = vb;
+    }
+  }
+  if (!TAB) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
       if (gi[u] < npred) {
         const float* src = t == 0 ? a_last + (int64_t)b * r
                                   : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
