@@ -29,6 +29,7 @@ EXPORTS = [
     "dflash2_topk_workspace_bytes", "dflash2_topk",
     "dflash2_pair_scores_workspace_bytes", "dflash2_pair_scores",
     "dflash2_selector_tables", "dflash2_pair_scores_tab_workspace_bytes", "dflash2_pair_scores_tab",
+    "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
     "dflash2_path_viterbi",
     "dflash2_dynconv2_workspace_bytes", "dflash2_dynconv2",
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
@@ -68,6 +69,8 @@ def lib():
         L.dflash2_pair_scores_tab_workspace_bytes.argtypes = [I, I, I, I]
         L.dflash2_pair_scores_tab_workspace_bytes.restype = SZ
         L.dflash2_pair_scores_tab.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, P, P, SZ, P]
+        L.dflash2_h_projection.argtypes = [P, P, I, I, I, I, P, SZ, P]
+        L.dflash2_pair_scores_tab_from_h.argtypes = [P, P, P, P, I64, I, I, I, I, I, I, P, P, SZ, P]
         L.dflash2_path_viterbi.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P]
         L.dflash2_dynconv2_workspace_bytes.argtypes = [I, I, I, I]
         L.dflash2_dynconv2_workspace_bytes.restype = SZ
@@ -82,7 +85,8 @@ def lib():
         L.dflash2_profile_stop.argtypes = [P, I, P]
         L.dflash2_profile_stop.restype = I
         for name in ("dflash2_topk", "dflash2_pair_scores", "dflash2_selector_tables",
-                     "dflash2_pair_scores_tab", "dflash2_path_viterbi",
+                     "dflash2_pair_scores_tab", "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
+                     "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
@@ -175,6 +179,22 @@ def dflash2_pair_scores_tab(cand_idx, cand_val, last_tok, tab, h, w_h, scores, w
     _check(lib().dflash2_pair_scores_tab(_ptr(cand_idx), _ptr(cand_val), _ptr(last_tok), _ptr(tab), V,
                                          _ptr(h), _ptr(w_h), B, T, K, d, r2 // 2, int(gate), _ptr(scores),
                                          _ptr(ws), _bytes(ws), _stream(stream)), "dflash2_pair_scores_tab")
+
+
+def dflash2_h_projection(h, w_h, ws, stream=None):
+    """H's partial products for dflash2_pair_scores_tab_from_h (h [B, T, d])."""
+    B, T, d = h.shape
+    _check(lib().dflash2_h_projection(_ptr(h), _ptr(w_h), B, T, d, w_h.shape[0], _ptr(ws), _bytes(ws),
+                                      _stream(stream)), "dflash2_h_projection")
+
+
+def dflash2_pair_scores_tab_from_h(cand_idx, cand_val, last_tok, tab, d, scores, ws,
+                                   gate=DF2_GATE_IDENTITY, stream=None):
+    B, T, K = cand_idx.shape
+    V, r2 = tab.shape
+    _check(lib().dflash2_pair_scores_tab_from_h(_ptr(cand_idx), _ptr(cand_val), _ptr(last_tok), _ptr(tab), V,
+                                                B, T, K, int(d), r2 // 2, int(gate), _ptr(scores), _ptr(ws),
+                                                _bytes(ws), _stream(stream)), "dflash2_pair_scores_tab_from_h")
 
 
 def dflash2_path_viterbi(scores, cand_idx, mode, path_rank, path_tok, q, path_score=None,

@@ -302,28 +302,20 @@ size_t dflash2_pair_scores_tab_workspace_bytes(int B, int T, int d, int r) {
   return align256((size_t)h_split(B, T, d, r) * (size_t)B * T * r * sizeof(float));
 }
 
-int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
-                            const float* tab, int64_t vocab, const void* h, const void* w_h, int B, int T,
-                            int K, int d, int r, int gate, float* scores, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
-  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: B %d", B);
-  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: T %d not in [1, %d]", T, kMaxT);
-  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: K %d not in [1, 16]", K);
-  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: d %d is not a positive multiple of 64", d);
-  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: r %d not a multiple of 16 in [16, 256]", r);
-  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores_tab: vocab %lld", (long long)vocab);
-  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores_tab: gate %d", gate);
-  if (B == 0) return DF2_OK;
-  REQUIRE(cand_idx && cand_val && last_tok && tab && h && w_h && scores, DF2_ERR_NULL,
-          "dflash2_pair_scores_tab: null pointer argument");
-  REQUIRE(aligned16(tab) && aligned16(h) && aligned16(w_h), DF2_ERR_SHAPE,
-          "dflash2_pair_scores_tab: tab/h/w_h must be 16-byte aligned");
-  const int split = h_split(B, T, d, r);
-  const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
-  REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_pair_scores_tab: workspace %zu < %zu bytes",
-          ws_bytes, need);
-  float* hg = (float*)ws;
-  const int64_t h_k = (int64_t)B * T * r;
+namespace {
+int check_tab_shapes(const char* fn, int B, int T, int K, int d, int r, int64_t vocab, int gate) {
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "%s: B %d", fn, B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "%s: T %d not in [1, %d]", fn, T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "%s: K %d not in [1, 16]", fn, K);
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "%s: d %d is not a positive multiple of 64", fn, d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "%s: r %d not a multiple of 16 in [16, 256]", fn, r);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "%s: vocab %lld", fn, (long long)vocab);
+  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "%s: gate %d", fn, gate);
+  return DF2_OK;
+}
+
+// H's split-K partial products (ungated) into ws.
+hipError_t project_h(const void* h, const void* w_h, int B, int T, int d, int r, float* hg, hipStream_t stream) {
   GemmSeg s = {};
   s.x = (const uint16_t*)h;
   s.gather = nullptr;
@@ -336,12 +328,57 @@ int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, cons
   s.N = r;
   s.out = hg;
   s.ldo = r;
-  s.out_kstride = h_k;
+  s.out_kstride = (int64_t)B * T * r;
   s.gate = DF2_GATE_IDENTITY;
-  hipError_t e = launch_gemm(&s, 1, d, split, kHTiling, "h_gemm", stream);
+  return launch_gemm(&s, 1, d, h_split(B, T, d, r), kHTiling, "h_gemm", stream);
+}
+}  // namespace
+
+int dflash2_h_projection(const void* h, const void* w_h, int B, int T, int d, int r, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  if (int st = check_tab_shapes("dflash2_h_projection", B, T, 1, d, r, 1, DF2_GATE_IDENTITY)) return st;
+  if (B == 0) return DF2_OK;
+  REQUIRE(h && w_h, DF2_ERR_NULL, "dflash2_h_projection: null pointer argument");
+  REQUIRE(aligned16(h) && aligned16(w_h), DF2_ERR_SHAPE, "dflash2_h_projection: h/w_h must be 16-byte aligned");
+  const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
+  REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_h_projection: workspace %zu < %zu bytes",
+          ws_bytes, need);
+  return hip_status(project_h(h, w_h, B, T, d, r, (float*)ws, stream), "dflash2_h_projection");
+}
+
+int dflash2_pair_scores_tab_from_h(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                                   const float* tab, int64_t vocab, int B, int T, int K, int d, int r, int gate,
+                                   float* scores, const void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (int st = check_tab_shapes("dflash2_pair_scores_tab_from_h", B, T, K, d, r, vocab, gate)) return st;
+  if (B == 0) return DF2_OK;
+  REQUIRE(cand_idx && cand_val && last_tok && tab && scores, DF2_ERR_NULL,
+          "dflash2_pair_scores_tab_from_h: null pointer argument");
+  REQUIRE(aligned16(tab), DF2_ERR_SHAPE, "dflash2_pair_scores_tab_from_h: tab must be 16-byte aligned");
+  const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
+  REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_pair_scores_tab_from_h: workspace %zu < %zu bytes",
+          ws_bytes, need);
+  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, (float*)ws, h_split(B, T, d, r),
+                                             (int64_t)B * T * r, gate, cand_val, B, T, K, r, scores, stream),
+                    "dflash2_pair_scores_tab_from_h");
+}
+
+int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                            const float* tab, int64_t vocab, const void* h, const void* w_h, int B, int T,
+                            int K, int d, int r, int gate, float* scores, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (int st = check_tab_shapes("dflash2_pair_scores_tab", B, T, K, d, r, vocab, gate)) return st;
+  if (B == 0) return DF2_OK;
+  REQUIRE(cand_idx && cand_val && last_tok && tab && h && w_h && scores, DF2_ERR_NULL,
+          "dflash2_pair_scores_tab: null pointer argument");
+  REQUIRE(aligned16(tab) && aligned16(h) && aligned16(w_h), DF2_ERR_SHAPE,
+          "dflash2_pair_scores_tab: tab/h/w_h must be 16-byte aligned");
+  const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
+  REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_pair_scores_tab: workspace %zu < %zu bytes",
+          ws_bytes, need);
+  hipError_t e = project_h(h, w_h, B, T, d, r, (float*)ws, stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores_tab (projection)");
-  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, hg, split, h_k, gate, cand_val,
-                                             B, T, K, r, scores, stream),
+  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, (float*)ws, h_split(B, T, d, r),
+                                             (int64_t)B * T * r, gate, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores_tab (epilogue)");
 }
 

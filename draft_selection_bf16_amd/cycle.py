@@ -14,7 +14,10 @@ inputs here.
 All output and scratch buffers are allocated once, before any capture, so a
 captured cycle allocates nothing.  With `tables=True` the per-token A/B
 table [V, 2r] is built once at construction (dflash2_selector_tables) and
-each cycle scores pairs from it (dflash2_pair_scores_tab).  The sampling seed lives in device memory
+each cycle scores pairs from it (dflash2_pair_scores_tab), on one stream:
+running H = W_H h_t on a second stream beside top-K measured slower (its
+work-groups take CU slots from top-K's rows, and the join costs time in
+the replayed graph).  The sampling seed lives in device memory
 (`seed`), so a replay can run with a fresh seed written between replays.
 """
 from __future__ import annotations

@@ -12,6 +12,8 @@
  *   dflash2_pair_scores    score every adjacent candidate pair
  *   dflash2_selector_tables  per-token A/B tables, once per weight set
  *   dflash2_pair_scores_tab  the pair scores with A/B read from those tables
+ *                            (or in two halves: dflash2_h_projection, then
+ *                            dflash2_pair_scores_tab_from_h)
  *   dflash2_path_viterbi   pick one path through the K x K lattices
  *   dflash2_verify_greedy  accept the longest prefix the target agrees with
  *   dflash2_verify_reject  speculative rejection sampling with a residual draw
@@ -144,10 +146,23 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
  * products over d).  cand_idx, cand_val, last_tok, h, w_h, scores, gate
  * and the limits are those of dflash2_pair_scores; tab [vocab, 2r] float as
  * above.  Token ids outside [0, vocab) read zero A and B rows.
+ *
+ * The same call in two halves, so that H (which depends on the drafter's
+ * hidden states alone, not on the candidates) can run on another stream
+ * while the candidates are selected: dflash2_h_projection writes H's
+ * partial products into ws (same size), and dflash2_pair_scores_tab_from_h
+ * reads them from ws to finish the scores.  The caller orders the two
+ * (same stream, or an event) and passes the same B, T, d, r to both;
+ * ws must not be reused in between.
  * ------------------------------------------------------------------------ */
 int dflash2_selector_tables(const void* emb, int emb_dt, int64_t vocab, int d, const void* w_a,
                             const void* w_b, int r, float* tab, hipStream_t stream);
 size_t dflash2_pair_scores_tab_workspace_bytes(int B, int T, int d, int r);
+int dflash2_h_projection(const void* h, const void* w_h, int B, int T, int d, int r, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+int dflash2_pair_scores_tab_from_h(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                                   const float* tab, int64_t vocab, int B, int T, int K, int d, int r, int gate,
+                                   float* scores, const void* ws, size_t ws_bytes, hipStream_t stream);
 int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
                             const float* tab, int64_t vocab, const void* h, const void* w_h, int B, int T,
                             int K, int d, int r, int gate, float* scores, void* ws, size_t ws_bytes,

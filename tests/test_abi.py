@@ -109,6 +109,22 @@ def test_pair_scores_tab_validation():
     assert L.dflash2_pair_scores_tab(*args(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
 
 
+def test_h_projection_and_from_h_validation():
+    L = df2.lib()
+    need = df2.dflash2_pair_scores_tab_workspace_bytes(32, 16, 5120, 256)
+    assert L.dflash2_h_projection(FAKE, FAKE, 32, 16, 100, 256, FAKE, need, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_h_projection(FAKE, FAKE, 32, 0, 5120, 256, FAKE, need, None) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_h_projection(None, FAKE, 32, 16, 5120, 256, FAKE, need, None) == df2.DF2_ERR_NULL
+    assert L.dflash2_h_projection(FAKE, FAKE, 32, 16, 5120, 256, FAKE, need - 1, None) == df2.DF2_ERR_WORKSPACE
+    assert L.dflash2_h_projection(None, None, 0, 16, 5120, 256, None, 0, None) == df2.DF2_OK
+    args = lambda **kw: [FAKE, FAKE, FAKE, kw.get("tab", FAKE), 151936, 32, 16, kw.get("K", 16), 5120, 256,
+                         kw.get("gate", 0), FAKE, FAKE, kw.get("ws", need), None]
+    assert L.dflash2_pair_scores_tab_from_h(*args(K=0)) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_pair_scores_tab_from_h(*args(gate=3)) == df2.DF2_ERR_UNSUPPORTED
+    assert L.dflash2_pair_scores_tab_from_h(*args(tab=None)) == df2.DF2_ERR_NULL
+    assert L.dflash2_pair_scores_tab_from_h(*args(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+
+
 def test_path_validation():
     L = df2.lib()
     assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \

@@ -86,6 +86,32 @@ def test_pair_scores_tab_shapes(B, block, r, K):
     report("pair_scores_tab shapes", B=B, T=w.T, r=r, K=K, worst_err_over_bound=round(worst, 4))
 
 
+def test_pair_scores_tab_in_two_halves_on_two_streams():
+    """dflash2_h_projection on a side stream, joined by an event, then
+    dflash2_pair_scores_tab_from_h: the same kernels as the one call, so the
+    same bits, and the oracle's scores."""
+    w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=4, V=4096, d=512)
+    idx, val, last, E, h, wa, wb, wh = _inputs(w)
+    tab = _tables_gpu(E, wa, wb)
+    one = _scores_tab_gpu(idx, val, last, tab, h, wh, gate=1)
+    B, T, K = idx.shape
+    hd, whd = dev(h), dev(wh)
+    wsp = ws(df2.dflash2_pair_scores_tab_workspace_bytes(B, T, w.d, w.r))
+    S = torch.empty((B, T, K, K), dtype=torch.float32, device=DEV)
+    args = [dev(idx), dev(val), dev(last)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        df2.dflash2_h_projection(hd, whd, wsp)
+    torch.cuda.current_stream().wait_stream(side)
+    df2.dflash2_pair_scores_tab_from_h(*args, tab, w.d, S, wsp, gate=1)
+    torch.cuda.synchronize()
+    two = S.cpu().numpy()
+    assert np.array_equal(one, two)
+    worst = close(two, oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, gate=1))
+    report("pair_scores_tab two halves", worst_err_over_bound=round(worst, 4))
+
+
 def test_pair_scores_tab_out_of_range_ids_read_zero_rows():
     w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=2, V=600, d=128, r=32, K=4)
     idx, val, last, E, h, wa, wb, wh = _inputs(w)
