@@ -163,7 +163,7 @@ def hbm_frac(w, conv, us, tables=False):
 def tables_leg(w, E, dev, steps, warmup, with_sweep):
     """The cycle with per-token A/B tables: the one-off table build, the step
     with and without the conv sites, per-kernel times and (with the sweep)
-    the two small-batch points."""
+    the other batch x block points."""
     import torch
     import draft_selection_bf16_amd as df2
     out = {}
@@ -199,7 +199,8 @@ def tables_leg(w, E, dev, steps, warmup, with_sweep):
     if with_sweep:
         import synth
         sw = {}
-        for name in ("b1_blk8_v151936", "b8_blk8_v151936_sampled"):
+        for name in ("b1_blk8_v151936", "b8_blk8_v151936_sampled", "b32_blk8_v151936",
+                     "b1_blk16_v151936", "b8_blk16_v151936"):
             ws_ = synth.WORKLOADS[name]
             c2, _ = build_cycle(ws_, dev, E=E, conv=False, tables=True)
             c2.capture(conv=False)
