@@ -357,7 +357,7 @@ int dflash2_pair_scores_tab_from_h(const int32_t* cand_idx, const float* cand_va
   const size_t need = dflash2_pair_scores_tab_workspace_bytes(B, T, d, r);
   REQUIRE(ws && ws_bytes >= need, DF2_ERR_WORKSPACE, "dflash2_pair_scores_tab_from_h: workspace %zu < %zu bytes",
           ws_bytes, need);
-  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, (float*)ws, h_split(B, T, d, r),
+  return hip_status(launch_pair_epilogue_tab(tab, vocab, cand_idx, last_tok, (const float*)ws, h_split(B, T, d, r),
                                              (int64_t)B * T * r, gate, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores_tab_from_h");
 }

@@ -455,7 +455,7 @@ hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
 }
 
 hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32_t* cand_idx,
-                                    const int32_t* last_tok, float* h, int split, int64_t h_k, int gate,
+                                    const int32_t* last_tok, const float* h, int split, int64_t h_k, int gate,
                                     const float* cand_val, int B, int T, int K, int r, float* scores,
                                     hipStream_t stream) {
   if (B * T == 0) return hipSuccess;

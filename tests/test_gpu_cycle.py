@@ -180,6 +180,20 @@ def test_cycle_b32_blk16_tables_graph():
     check_cycle(cyc, w, [0, 13, 31], w.name + " tables")
 
 
+def test_stress_shape_tables_graph():
+    """64 requests, block 16, vocabulary 262,144 (a 537 MB table), greedy
+    verification for requests 0-31 and rejection sampling for 32-63, pair
+    scores from per-token tables, captured and replayed."""
+    w = synth.WORKLOADS["b64_blk16_v262144_stress"]
+    print(f"[case] {w.name} tables graph", flush=True)
+    cyc, _ = build(w, with_conv=0, tables=True)
+    cyc.set_seed(4_000_000)
+    cyc.capture(conv=False)
+    for _ in range(3):
+        cyc.replay()
+    check_cycle(cyc, w, [0, 31, 32, 63], w.name + " tables")
+
+
 def test_cycle_b8_blk8_sampled_tables():
     w = synth.WORKLOADS["b8_blk8_v151936_sampled"]
     cyc, _ = build(w, tables=True)
