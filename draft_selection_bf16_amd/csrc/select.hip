@@ -187,6 +187,36 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     }
   }
   __syncthreads();
+  // Dot products, register-blocked: wave w takes the float4 columns
+  // [w r4/4, (w+1) r4/4) of the rows and lane (bi, bj) the 2 x 2 outputs
+  // (2bi..2bi+1, 2bj..2bj+1), so every LDS read feeds two products; the
+  // waves' partial sums meet in LDS and are added in wave order.
+  __shared__ float sP[4][256];
+  {
+    const int w = tid >> 6, lane = tid & 63;
+    const int i0 = 2 * (lane >> 3), j0 = 2 * (lane & 7);
+    const int qn = r4 / 4, qa = w * qn;
+    const f32x4* g0 = (const f32x4*)&sG[i0 * kLd] + qa;
+    const f32x4* g1 = (const f32x4*)&sG[(i0 + 1) * kLd] + qa;
+    const f32x4* b0 = (const f32x4*)&sB[j0 * kLd] + qa;
+    const f32x4* b1 = (const f32x4*)&sB[(j0 + 1) * kLd] + qa;
+    float a00 = 0.f, a01 = 0.f, a10 = 0.f, a11 = 0.f;
+    for (int q = 0; q < qn; ++q) {
+      const f32x4 x0 = g0[q], x1 = g1[q], y0 = b0[q], y1 = b1[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a00 = fmaf(x0[e], y0[e], a00);
+        a01 = fmaf(x0[e], y1[e], a01);
+        a10 = fmaf(x1[e], y0[e], a10);
+        a11 = fmaf(x1[e], y1[e], a11);
+      }
+    }
+    sP[w][i0 * 16 + j0] = a00;
+    sP[w][i0 * 16 + j0 + 1] = a01;
+    sP[w][(i0 + 1) * 16 + j0] = a10;
+    sP[w][(i0 + 1) * 16 + j0 + 1] = a11;
+  }
+  __syncthreads();
   const int i = oi, j = oj;
   if (i >= K || j >= K) return;
   float* out = scores + ((int64_t)bt * K + i) * K + j;
@@ -194,17 +224,8 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
     *out = -INFINITY;
     return;
   }
-  const f32x4* gr = (const f32x4*)&sG[i * kLd];
-  const f32x4* br = (const f32x4*)&sB[j * kLd];
-  float acc = 0.f;
-  for (int q = 0; q < r4; ++q) {
-    f32x4 x = gr[q], y = br[q];
-    acc = fmaf(x[0], y[0], acc);
-    acc = fmaf(x[1], y[1], acc);
-    acc = fmaf(x[2], y[2], acc);
-    acc = fmaf(x[3], y[3], acc);
-  }
-  *out = u_j + acc;
+  const int o = i * 16 + j;
+  *out = u_j + (((sP[0][o] + sP[1][o]) + sP[2][o]) + sP[3][o]);
 }
 
 // (value, rank) comparison: larger value, then lower rank
