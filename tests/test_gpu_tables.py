@@ -76,9 +76,11 @@ def test_pair_scores_tab_mid(gate):
     report("pair_scores_tab mid", gate=gate, worst_err_over_bound=round(max(worst, worst2), 4))
 
 
-@pytest.mark.parametrize("B,block,r,K", [(2, 8, 64, 7), (1, 8, 256, 16), (5, 4, 128, 16)])
+@pytest.mark.parametrize("B,block,r,K", [(2, 8, 64, 7), (1, 8, 256, 16), (5, 4, 128, 16), (3, 2, 256, 1),
+                                         (2, 3, 16, 2)])
 def test_pair_scores_tab_shapes(B, block, r, K):
-    """Ragged K x K lattices (K = 7), one request, short blocks, ranks 64 and 128."""
+    """Ragged K x K lattices (K = 7), one request, short blocks, ranks 64 and
+    128; one draft position with one candidate; rank 16 with two."""
     w = synth.scaled(synth.WORKLOADS["b1_blk8_v151936"], B=B, block=block, V=3000, d=384, r=r, K=K)
     idx, val, last, E, h, wa, wb, wh = _inputs(w)
     Sg = _scores_tab_gpu(idx, val, last, _tables_gpu(E, wa, wb), h, wh)
