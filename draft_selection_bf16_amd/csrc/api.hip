@@ -117,14 +117,25 @@ constexpr GemmTiling kProjTiling{128, 128, 3, 8};
 // in a fixed order by a reduce pass spread over many work-groups before the
 // pair epilogue, which gates H after the sum.
 constexpr int kMaxProjSplit = 8;
+// Below 1,024 candidate rows the projection uses 64 x 128 tiles (4 waves)
+// and up to 16 slices: more, smaller work-groups read less each (batch 1 /
+// block 8: 47.9 -> 45.8 us per cycle; batch 8 / block 8 sampled 96.5 ->
+// 93.8; at 1,920 rows, batch 8 / block 16, the 128 x 128 tiles stay ahead).
+constexpr int kSmallProjRows = 1024;
+constexpr GemmTiling kProjTilingSmall{64, 128, 3, 4};
+const GemmTiling& proj_tiling(int B, int T, int K) {
+  return B * T * K < kSmallProjRows ? kProjTilingSmall : kProjTiling;
+}
 int proj_split(int B, int T, int K, int d, int r) {
-  const int bm = kProjTiling.bm, bn = kProjTiling.bn;
+  const GemmTiling& tl0 = proj_tiling(B, T, K);
+  const int bm = tl0.bm, bn = tl0.bn;
+  const int maxs = B * T * K < kSmallProjRows ? 16 : kMaxProjSplit;
   auto tl = [&](int m, int n) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   const int mc = B * T * K;
   const int tiles = (r % bn == 0 ? tl(mc, 2 * r) : 2 * tl(mc, r)) + tl(B, r) + tl(B * T, r);
   int ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks > d / 64 / 4) ks = d / 64 / 4;
-  if (ks > kMaxProjSplit) ks = kMaxProjSplit;
+  if (ks > maxs) ks = maxs;
   return ks < 1 ? 1 : ks;
 }
 struct PairWs {
@@ -231,7 +242,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
     s[3].out = ab + r;
     nseg = 4;
   }
-  hipError_t e = launch_gemm(s, nseg, d, pw.split, kProjTiling, "project_gemm", stream);
+  hipError_t e = launch_gemm(s, nseg, d, pw.split, proj_tiling(B, T, K), "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, pw.split, (int64_t)pw.ab_k, (int64_t)pw.alast_k,
                                          (int64_t)pw.h_k, gate, cand_val, B, T, K, r, scores, stream),
