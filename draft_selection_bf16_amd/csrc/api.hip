@@ -117,19 +117,11 @@ constexpr GemmTiling kProjTiling{128, 128, 3, 8};
 // in a fixed order by a reduce pass spread over many work-groups before the
 // pair epilogue, which gates H after the sum.
 constexpr int kMaxProjSplit = 8;
-// Below 1,024 candidate rows the projection uses 64 x 128 tiles (4 waves)
-// and up to 16 slices: more, smaller work-groups read less each (batch 1 /
-// block 8: 47.9 -> 45.8 us per cycle; batch 8 / block 8 sampled 96.5 ->
-// 93.8; at 1,920 rows, batch 8 / block 16, the 128 x 128 tiles stay ahead).
-constexpr int kSmallProjRows = 1024;
+constexpr int kMaxProjSplitSmall = 16;
 constexpr GemmTiling kProjTilingSmall{64, 128, 3, 4};
-const GemmTiling& proj_tiling(int B, int T, int K) {
-  return B * T * K < kSmallProjRows ? kProjTilingSmall : kProjTiling;
-}
-int proj_split(int B, int T, int K, int d, int r) {
-  const GemmTiling& tl0 = proj_tiling(B, T, K);
-  const int bm = tl0.bm, bn = tl0.bn;
-  const int maxs = B * T * K < kSmallProjRows ? 16 : kMaxProjSplit;
+constexpr int kSmallProjRows = 1024;
+int split_for(const GemmTiling& t, int maxs, int B, int T, int K, int d, int r) {
+  const int bm = t.bm, bn = t.bn;
   auto tl = [&](int m, int n) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
   const int mc = B * T * K;
   const int tiles = (r % bn == 0 ? tl(mc, 2 * r) : 2 * tl(mc, r)) + tl(B, r) + tl(B * T, r);
@@ -137,6 +129,24 @@ int proj_split(int B, int T, int K, int d, int r) {
   if (ks > d / 64 / 4) ks = d / 64 / 4;
   if (ks > maxs) ks = maxs;
   return ks < 1 ? 1 : ks;
+}
+// 64 x 128 tiles (4 waves, up to 16 slices) below 1,024 candidate rows, and
+// wherever they need no K split while 128 x 128 tiles would (no reduce
+// pass); 128 x 128 otherwise.  Per cycle: batch 1 / block 8 47.9 -> 45.8 us,
+// batch 8 / block 8 sampled 96.5 -> 93.8, batch 32 / block 8 (3,584 rows,
+// no split instead of two slices) 94.4 -> 91.5; at batch 8 / block 16 both
+// split and the 128 x 128 tiles stay ahead (76.7 against 78.4).
+bool proj_small(int B, int T, int K, int d, int r) {
+  if (B * T * K < kSmallProjRows) return true;
+  return split_for(kProjTilingSmall, kMaxProjSplitSmall, B, T, K, d, r) == 1 &&
+         split_for(kProjTiling, kMaxProjSplit, B, T, K, d, r) > 1;
+}
+const GemmTiling& proj_tiling(int B, int T, int K, int d, int r) {
+  return proj_small(B, T, K, d, r) ? kProjTilingSmall : kProjTiling;
+}
+int proj_split(int B, int T, int K, int d, int r) {
+  return proj_small(B, T, K, d, r) ? split_for(kProjTilingSmall, kMaxProjSplitSmall, B, T, K, d, r)
+                                   : split_for(kProjTiling, kMaxProjSplit, B, T, K, d, r);
 }
 struct PairWs {
   int split;
@@ -242,7 +252,7 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
     s[3].out = ab + r;
     nseg = 4;
   }
-  hipError_t e = launch_gemm(s, nseg, d, pw.split, proj_tiling(B, T, K), "project_gemm", stream);
+  hipError_t e = launch_gemm(s, nseg, d, pw.split, proj_tiling(B, T, K, d, r), "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, pw.split, (int64_t)pw.ab_k, (int64_t)pw.alast_k,
                                          (int64_t)pw.h_k, gate, cand_val, B, T, K, r, scores, stream),
