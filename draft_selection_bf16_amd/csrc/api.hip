@@ -305,8 +305,8 @@ int dflash2_selector_tables(const void* emb, int emb_dt, int64_t vocab, int d, c
 namespace {
 // Per cycle only H = W_H h is projected: B*T rows, a skinny product whose
 // reduction over d is split so that about one work-group per CU takes part
-// (64 x 128 tiles; slices of >= 4 K-tiles, at most kMaxHSplit), then summed
-// in slice order by the reduce pass.
+// (64 x 128 tiles; slices of >= 4 K-tiles, at most kMaxHSplit); the
+// table-mode pair epilogue sums the slices in slice order itself.
 constexpr GemmTiling kHTiling{64, 128, 3, 4};
 constexpr int kMaxHSplit = 16;
 int h_split(int B, int T, int d, int r) {

@@ -5,11 +5,13 @@
 // path selector", equation S_t(a,b) = U_t(b) + <A(a) (.) H(h_t), B(b)>):
 // one work-group per (request, position); the predecessor rows A(a) (the
 // candidates of position t-1, or the last verified token at t = 0) are
-// scaled by the gate H_t once in LDS, then each of the K x K threads takes
-// one r-long dot product with B(b).  fp32 throughout.  A and B are functions
-// of the token alone (same section: every token gets its own compact
-// vectors), so their rows come either from this cycle's projection of the
-// gathered embedding rows or from a per-token table built once.
+// scaled by the gate H_t once in LDS, then the K x K dot products with B(b)
+// are taken register-blocked (each lane a 2 x 2 block of outputs over a
+// quarter of r; the quarters added in a fixed order).  fp32 throughout.
+// A and B are functions of the token alone (same section: every token gets
+// its own compact vectors), so their rows come either from this cycle's
+// projection of the gathered embedding rows or from a per-token table
+// built once.
 //
 // Path (same section; and "DFlash 2 讓 Qwen3.8-27B 快了兩倍", item 2 --
 // Viterbi): one work-group per request, whose first wave runs the
@@ -136,8 +138,7 @@ __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restr
       if (okp) ga[u] = va;
       if (okc) gb[u] = vb;
     }
-  }
-  if (!TAB) {
+  } else {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (gi[u] < npred) {
