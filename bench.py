@@ -338,7 +338,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no "
-              f"multi-GPU form in this build", file=sys.stderr)
+              f"multi-GPU form (every request is independent: shard the batch, one process per GPU)", file=sys.stderr)
         sys.exit(2)
     log("importing torch")
     import torch
