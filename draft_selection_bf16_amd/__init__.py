@@ -71,14 +71,14 @@ def lib():
         L.dflash2_pair_scores_tab.argtypes = [P, P, P, P, I64, P, P, I, I, I, I, I, I, P, P, SZ, P]
         L.dflash2_h_projection.argtypes = [P, P, I, I, I, I, P, SZ, P]
         L.dflash2_pair_scores_tab_from_h.argtypes = [P, P, P, P, I64, I, I, I, I, I, I, P, P, SZ, P]
-        L.dflash2_path_viterbi.argtypes = [P, P, I, I, I, I, F, P, P, P, P, P, P]
+        L.dflash2_path_viterbi.argtypes = [P, P, I, I, I, I, F, P, I, P, P, P, P, P]
         L.dflash2_dynconv2_workspace_bytes.argtypes = [I, I, I, I]
         L.dflash2_dynconv2_workspace_bytes.restype = SZ
         L.dflash2_dynconv2.argtypes = [P, P, P, P, I, I, I, I, P, I, P, SZ, P]
         L.dflash2_verify_workspace_bytes.argtypes = [I, I, I64]
         L.dflash2_verify_workspace_bytes.restype = SZ
         L.dflash2_verify_greedy.argtypes = [P, I, I64, P, I, I, P, P, P, SZ, P]
-        L.dflash2_verify_reject.argtypes = [P, I, I64, P, P, P, P, I, I, I, F, P, P, P, P, SZ, P]
+        L.dflash2_verify_reject.argtypes = [P, I, I64, P, P, P, P, I, I, I, F, P, I, P, P, P, SZ, P]
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
         L.dflash2_profile_start.argtypes = [C.c_char_p, I]
         L.dflash2_profile_start.restype = I
@@ -198,10 +198,11 @@ def dflash2_pair_scores_tab_from_h(cand_idx, cand_val, last_tok, tab, d, scores,
 
 
 def dflash2_path_viterbi(scores, cand_idx, mode, path_rank, path_tok, q, path_score=None,
-                         temperature=0.0, seed_dev=None, stream=None):
+                         temperature=0.0, seed_dev=None, b0=0, stream=None):
+    """b0: index of scores[0]'s request in the batch the seed covers."""
     B, T, K, _ = scores.shape
     _check(lib().dflash2_path_viterbi(_ptr(scores), _ptr(cand_idx), B, T, K, int(mode),
-                                      float(temperature), _ptr(seed_dev), _ptr(path_rank),
+                                      float(temperature), _ptr(seed_dev), int(b0), _ptr(path_rank),
                                       _ptr(path_tok), _ptr(q), _ptr(path_score), _stream(stream)),
            "dflash2_path_viterbi")
 
@@ -229,12 +230,13 @@ def dflash2_verify_greedy(target, path_tok, accept_len, out_tok, ws, stream=None
 
 
 def dflash2_verify_reject(target, path_tok, path_rank, cand_idx, q, temperature, seed_dev,
-                          accept_len, out_tok, ws, stream=None):
+                          accept_len, out_tok, ws, b0=0, stream=None):
+    """b0: index of target[0]'s request in the batch the seed covers."""
     B, T1, V = target.shape
     K = cand_idx.shape[-1]
     _check(lib().dflash2_verify_reject(_ptr(target), _dt(target), V, _ptr(path_tok), _ptr(path_rank),
                                        _ptr(cand_idx), _ptr(q), B, T1 - 1, K, float(temperature),
-                                       _ptr(seed_dev), _ptr(accept_len), _ptr(out_tok), _ptr(ws),
+                                       _ptr(seed_dev), int(b0), _ptr(accept_len), _ptr(out_tok), _ptr(ws),
                                        _bytes(ws), _stream(stream)), "dflash2_verify_reject")
 
 

@@ -405,7 +405,7 @@ int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, cons
 
 // ------------------------------------------------------------------ path
 int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
-                         float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                         float temperature, const uint64_t* seed_dev, int b0, int32_t* path_rank,
                          int32_t* path_tok, float* q, float* path_score, hipStream_t stream) {
   REQUIRE(mode == DF2_PATH_VITERBI || mode == DF2_PATH_GREEDY || mode == DF2_PATH_SAMPLE,
           DF2_ERR_UNSUPPORTED, "dflash2_path_viterbi: mode %d", mode);
@@ -414,11 +414,13 @@ int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, in
   REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_path_viterbi: B %d", B);
   REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_path_viterbi: T %d not in [1, %d]", T, kMaxT);
   REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_path_viterbi: K %d not in [1, 16]", K);
+  REQUIRE(b0 >= 0 && (int64_t)b0 + B <= ((int64_t)1 << 31) - 1, DF2_ERR_SHAPE,
+          "dflash2_path_viterbi: b0 %d (with B %d) outside [0, 2^31 - 1]", b0, B);
   if (B == 0) return DF2_OK;
   REQUIRE(scores && cand_idx && path_rank && path_tok && q, DF2_ERR_NULL,
           "dflash2_path_viterbi: null pointer argument");
   REQUIRE(mode != DF2_PATH_SAMPLE || seed_dev, DF2_ERR_NULL, "dflash2_path_viterbi: sampling needs seed_dev");
-  return hip_status(launch_path(scores, cand_idx, B, T, K, mode, temperature, seed_dev, path_rank,
+  return hip_status(launch_path(scores, cand_idx, B, T, K, mode, temperature, seed_dev, b0, path_rank,
                                 path_tok, q, path_score, stream),
                     "dflash2_path_viterbi");
 }
@@ -476,7 +478,7 @@ int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, cons
 
 int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
                           const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
-                          int T, int K, float temperature, const uint64_t* seed_dev,
+                          int T, int K, float temperature, const uint64_t* seed_dev, int b0,
                           int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
                           hipStream_t stream) {
   int st = check_dt(dt, "dflash2_verify_reject");
@@ -487,6 +489,8 @@ int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, cons
   REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_verify_reject: B %d", B);
   REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_reject: T %d not in [1, %d]", T, kMaxT);
   REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_verify_reject: K %d not in [1, 16]", K);
+  REQUIRE(b0 >= 0 && (int64_t)b0 + B <= ((int64_t)1 << 31) - 1, DF2_ERR_SHAPE,
+          "dflash2_verify_reject: b0 %d (with B %d) outside [0, 2^31 - 1]", b0, B);
   if (B == 0) return DF2_OK;
   REQUIRE(target_logits && path_tok && path_rank && cand_idx && q && seed_dev && accept_len && out_tok,
           DF2_ERR_NULL, "dflash2_verify_reject: null pointer argument");
@@ -495,7 +499,7 @@ int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, cons
   REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_verify_reject: workspace %zu < %zu bytes",
           ws_bytes, plan.ws_bytes);
   return hip_status(launch_verify_reject(target_logits, dt, vocab, path_tok, path_rank, cand_idx, q, B, T,
-                                         K, temperature, seed_dev, accept_len, out_tok, ws, plan, stream),
+                                         K, temperature, seed_dev, b0, accept_len, out_tok, ws, plan, stream),
                     "dflash2_verify_reject");
 }
 

@@ -111,7 +111,7 @@ hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32
 
 // ---- path ------------------------------------------------------------------
 hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
-                       float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                       float temperature, const uint64_t* seed_dev, int b0, int32_t* path_rank,
                        int32_t* path_tok, float* q, float* path_score, hipStream_t stream);
 
 // ---- verification ------------------------------------------------------------
@@ -131,7 +131,7 @@ hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int3
                                 const VerifyPlan& plan, hipStream_t stream);
 hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
                                 const int32_t* path_rank, const int32_t* cand_idx, const float* q,
-                                int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                                int B, int T, int K, float temperature, const uint64_t* seed_dev, int b0,
                                 int32_t* accept_len, int32_t* out_tok, void* ws,
                                 const VerifyPlan& plan, hipStream_t stream);
 

@@ -292,7 +292,7 @@ constexpr int kPathLoads = 4;   // 16-byte lattice loads in flight per thread
 __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restrict__ scores,
                                                   const int32_t* __restrict__ cand_idx, int T,
                                                   int K, int mode, float inv_tau,
-                                                  const uint64_t* __restrict__ seed_dev,
+                                                  const uint64_t* __restrict__ seed_dev, int b0,
                                                   int32_t* __restrict__ path_rank,
                                                   int32_t* __restrict__ path_tok,
                                                   float* __restrict__ q, float* __restrict__ path_score) {
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kPathThreads) void path_kernel(const float* __restr
         float p = e / z;
         // inclusive prefix sum in rank order
         float c = row16_prefix(p);
-        float u = cycle_uniform(seed, b, t, 0);
+        float u = cycle_uniform(seed, b0 + b, t, 0);
         uint64_t over = ballot(lane < K && c > u);
         if (over) {
           pick = __ffsll((unsigned long long)over) - 1;
@@ -490,13 +490,13 @@ hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32
 }
 
 hipError_t launch_path(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
-                       float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                       float temperature, const uint64_t* seed_dev, int b0, int32_t* path_rank,
                        int32_t* path_tok, float* q, float* path_score, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   float inv_tau = mode == 2 ? 1.0f / temperature : 0.f;
   ProfileScope ps("path", stream);
   DF2_TRY(launch(path_kernel, dim3(B), dim3(kPathThreads), 0, stream, ps, scores, cand_idx, T, K, mode, inv_tau, seed_dev,
-                                                path_rank, path_tok, q, path_score));
+                                                b0, path_rank, path_tok, q, path_score));
   return hipGetLastError();
 }
 

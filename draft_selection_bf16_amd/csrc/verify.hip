@@ -355,7 +355,7 @@ template <int DT>
 __global__ __launch_bounds__(64) void reject_decide_kernel(
     const void* __restrict__ z, int64_t vocab, const RowPart* __restrict__ part, int splits, int T,
     int K, float c, const int32_t* __restrict__ path_tok, const int32_t* __restrict__ path_rank,
-    const float* __restrict__ q, const uint64_t* __restrict__ seed_dev,
+    const float* __restrict__ q, const uint64_t* __restrict__ seed_dev, int b0,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok, DecRec* __restrict__ dec) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const uint64_t seed = seed_dev[0];
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
       float zx = Elt<DT>::one(rowp, x);
       px = exp2f((zx - key_value(k)) * c) / s;
     }
-    const float u1 = cycle_uniform(seed, b, lane, 1);
+    const float u1 = cycle_uniform(seed, b0 + b, lane, 1);
     const bool accept = qx <= 0.f || u1 < px / qx;
     reject = !accept;
   }
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
     d.argmax = knn ? (int)key_index(knn) : 0;
     d.m = key_value(knn);
     d.s = sn;
-    d.u2 = cycle_uniform(seed, b, n, 2);
+    d.u2 = cycle_uniform(seed, b0 + b, n, 2);
     d.pad = 0.f;
     dec[b] = d;
   }
@@ -696,7 +696,7 @@ hipError_t launch_verify_greedy(const void* z, int dt, int64_t vocab, const int3
 template <int DT>
 static hipError_t reject_launch(const void* z, int64_t vocab, const int32_t* path_tok,
                           const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
-                          int T, int K, float c, const uint64_t* seed_dev, int32_t* accept_len,
+                          int T, int K, float c, const uint64_t* seed_dev, int b0, int32_t* accept_len,
                           int32_t* out_tok, void* ws, const VerifyPlan& plan, hipStream_t stream) {
   const int64_t rows = (int64_t)B * (T + 1);
   RowPart* part = (RowPart*)((char*)ws + plan.off_part);
@@ -710,7 +710,7 @@ static hipError_t reject_launch(const void* z, int64_t vocab, const int32_t* pat
   {
     ProfileScope ps("reject_decide", stream);
     DF2_TRY(launch(reject_decide_kernel<DT>, dim3(B), dim3(64), 0, stream, ps, z, vocab, part, plan.splits, T, K, c,
-                                                              path_tok, path_rank, q, seed_dev,
+                                                              path_tok, path_rank, q, seed_dev, b0,
                                                               accept_len, out_tok, dec));
   }
   {
@@ -726,18 +726,18 @@ static hipError_t reject_launch(const void* z, int64_t vocab, const int32_t* pat
 
 hipError_t launch_verify_reject(const void* z, int dt, int64_t vocab, const int32_t* path_tok,
                                 const int32_t* path_rank, const int32_t* cand_idx, const float* q,
-                                int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                                int B, int T, int K, float temperature, const uint64_t* seed_dev, int b0,
                                 int32_t* accept_len, int32_t* out_tok, void* ws,
                                 const VerifyPlan& plan, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   const float c = kLog2e / temperature;
   if (dt == 0)
-    return reject_launch<0>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+    return reject_launch<0>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, b0, accept_len,
                             out_tok, ws, plan, stream);
   if (dt == 1)
-    return reject_launch<1>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+    return reject_launch<1>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, b0, accept_len,
                             out_tok, ws, plan, stream);
-  return reject_launch<2>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, accept_len,
+  return reject_launch<2>(z, vocab, path_tok, path_rank, cand_idx, q, B, T, K, c, seed_dev, b0, accept_len,
                           out_tok, ws, plan, stream);
 }
 

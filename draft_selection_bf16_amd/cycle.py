@@ -138,7 +138,7 @@ class Cycle:
             if g < self.B:
                 dflash2_verify_reject(self.target[g:], self.path_tok[g:], self.path_rank[g:],
                                       self.cand_idx[g:], self.q[g:], self.tau, self.seed,
-                                      self.accept_len[g:], self.out_tok[g:], self.ws_verify)
+                                      self.accept_len[g:], self.out_tok[g:], self.ws_verify, b0=g)
         else:
             raise ValueError(self.verify)
 

@@ -73,7 +73,7 @@ typedef enum { DF2_PATH_VITERBI = 0, DF2_PATH_GREEDY = 1, DF2_PATH_SAMPLE = 2 } 
 
 typedef enum { DF2_GATE_IDENTITY = 0, DF2_GATE_SIGMOID = 1 } df2_gate;
 
-#define DFLASH2_ABI_VERSION 1
+#define DFLASH2_ABI_VERSION 2
 
 int dflash2_abi_version(void);
 /* Static text for a status code (host). */
@@ -177,11 +177,16 @@ int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, cons
  *   DF2_PATH_SAMPLE  [KDP] same section: the sampled path draws from the
  *                    same scores; c_t ~ softmax_j(S_t(c_{t-1}, j) / tau),
  *                    inverse CDF in candidate-rank order with Philox4x64-10
- *                    key (seed, 0), counter (t, b, 0, 0), word 0.
+ *                    key (seed, 0), counter (t, b0 + b, 0, 0), word 0.
  * Path sums are float additions; argmax ties go to the lowest rank.
  *
  *   scores     [B, T, K, K] float     cand_idx [B, T, K] int32
  *   seed_dev   [1] uint64 (device; read by SAMPLE only, may be NULL else)
+ *   b0         index of this call's first request in the batch the seed
+ *              covers: request b of the call draws the counter of request
+ *              b0 + b, so a batch split over several calls draws the same
+ *              uniforms as one call over the whole batch (0 <= b0,
+ *              b0 + B < 2^31; else DF2_ERR_SHAPE)
  *   path_rank  [B, T] int32  chosen candidate rank per position
  *   path_tok   [B, T] int32  chosen token id
  *   q          [B, T, K] float  the proposal the step drew from (one-hot for
@@ -190,7 +195,7 @@ int dflash2_pair_scores_tab(const int32_t* cand_idx, const float* cand_val, cons
  * SAMPLE needs temperature > 0 (else DF2_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 int dflash2_path_viterbi(const float* scores, const int32_t* cand_idx, int B, int T, int K, int mode,
-                         float temperature, const uint64_t* seed_dev, int32_t* path_rank,
+                         float temperature, const uint64_t* seed_dev, int b0, int32_t* path_rank,
                          int32_t* path_tok, float* q, float* path_score, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -233,23 +238,27 @@ int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, cons
  * Speculative rejection sampling.  [KDP] "A lightweight path selector":
  * rejection sampling restores the exact target distribution; [WC]
  * "輸出完全一致".  With p_t = softmax(Z_t / tau):
- *   accept draft t iff u1 < p_t(x_t) / q_t(x_t)        (word 1 at (t, b))
+ *   accept draft t iff u1 < p_t(x_t) / q_t(x_t)        (word 1 at (t, b0+b))
  *   at the first rejection draw from max(0, p_t - q~_t) (q~ = q on the
  *   candidates of position t, 0 elsewhere) by index-order inverse CDF with
- *   u2 (word 2 at (t, b)); if every draft is accepted, draw the bonus token
- *   from p_T with word 2 at (T, b).
- * Uniforms: Philox4x64-10, key (seed, 0), counter (t, b, 0, 0); a word w
- * maps to (2 * (w >> 41) + 1) * 2^-24.  q_t(x_t) <= 0 accepts.
+ *   u2 (word 2 at (t, b0+b)); if every draft is accepted, draw the bonus
+ *   token from p_T with word 2 at (T, b0+b).
+ * Uniforms: Philox4x64-10, key (seed, 0), counter (t, b0 + b, 0, 0); a
+ * word w maps to (2 * (w >> 41) + 1) * 2^-24.  q_t(x_t) <= 0 accepts.
  *
  *   target_logits [B, T+1, vocab]; path_tok, path_rank [B, T] int32;
  *   cand_idx [B, T, K] int32; q [B, T, K] float (from dflash2_path_viterbi)
  *   seed_dev [1] uint64 (device)
+ *   b0       index of this call's first request in the batch the seed
+ *            covers (as in dflash2_path_viterbi): a sub-range of a batch
+ *            (pointers offset by b0 requests, B requests) draws the same
+ *            uniforms as the whole batch in one call
  *   accept_len [B], out_tok [B, T+1] as in dflash2_verify_greedy
  * Needs temperature > 0 (else DF2_ERR_UNSUPPORTED).  Probabilities fp32.
  * ------------------------------------------------------------------------ */
 int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
                           const int32_t* path_rank, const int32_t* cand_idx, const float* q, int B,
-                          int T, int K, float temperature, const uint64_t* seed_dev,
+                          int T, int K, float temperature, const uint64_t* seed_dev, int b0,
                           int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
                           hipStream_t stream);
 

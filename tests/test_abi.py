@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_strings():
-    assert df2.dflash2_abi_version() == 1
+    assert df2.dflash2_abi_version() == 2
     assert df2.dflash2_status_string(0) == "ok"
     assert df2.dflash2_status_string(4) == "workspace too small"
 
@@ -127,18 +127,17 @@ def test_h_projection_and_from_h_validation():
 
 def test_path_validation():
     L = df2.lib()
-    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 3, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
+    f = L.dflash2_path_viterbi
+    assert f(FAKE, FAKE, 2, 7, 16, 3, 1.0, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 2, 7, 16, 2, 0.0, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, 2, 7, 16, 2, float("inf"), FAKE, 0, FAKE, FAKE, FAKE, FAKE, None) == \
         df2.DF2_ERR_UNSUPPORTED
-    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, 0.0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == \
-        df2.DF2_ERR_UNSUPPORTED
-    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, float("inf"), FAKE, FAKE, FAKE, FAKE, FAKE,
-                                  None) == df2.DF2_ERR_UNSUPPORTED
-    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 16, 2, 1.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
-        df2.DF2_ERR_NULL
-    assert L.dflash2_path_viterbi(FAKE, FAKE, 2, 7, 0, 0, 1.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
-        df2.DF2_ERR_SHAPE
-    assert L.dflash2_path_viterbi(None, FAKE, 2, 7, 16, 0, 0.0, None, FAKE, FAKE, FAKE, FAKE, None) == \
-        df2.DF2_ERR_NULL
+    assert f(FAKE, FAKE, 2, 7, 16, 2, 1.0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_NULL
+    assert f(FAKE, FAKE, 2, 7, 0, 0, 1.0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_SHAPE
+    assert f(None, FAKE, 2, 7, 16, 0, 0.0, None, 0, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_NULL
+    # the request offset of the Philox counters: b0 >= 0 and b0 + B < 2^31
+    assert f(FAKE, FAKE, 2, 7, 16, 2, 1.0, FAKE, -1, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_SHAPE
+    assert f(FAKE, FAKE, 2, 7, 16, 2, 1.0, FAKE, 2**31 - 2, FAKE, FAKE, FAKE, FAKE, None) == df2.DF2_ERR_SHAPE
 
 
 def test_conv_validation():
@@ -174,12 +173,14 @@ def test_verify_validation():
     assert L.dflash2_verify_greedy(FAKE, 1, 151936, FAKE, 32, 15, FAKE, FAKE, FAKE, need - 1, None) == \
         df2.DF2_ERR_WORKSPACE
     args = [FAKE, 1, 151936, FAKE, FAKE, FAKE, FAKE, 32, 15, 16]
-    tail = [FAKE, FAKE, FAKE, FAKE, need, None]
+    tail = [FAKE, 0, FAKE, FAKE, FAKE, need, None]
     assert L.dflash2_verify_reject(*args, 0.0, *tail) == df2.DF2_ERR_UNSUPPORTED
     assert L.dflash2_verify_reject(*args, -1.0, *tail) == df2.DF2_ERR_UNSUPPORTED
     assert L.dflash2_verify_reject(*args, 1.0, None, *tail[1:]) == df2.DF2_ERR_NULL
     assert L.dflash2_verify_reject(*args[:-1], 0, 1.0, *tail) == df2.DF2_ERR_SHAPE
     assert L.dflash2_verify_reject(*args, 1.0, *tail[:-2], need - 1, None) == df2.DF2_ERR_WORKSPACE
+    assert L.dflash2_verify_reject(*args, 1.0, FAKE, -3, *tail[2:]) == df2.DF2_ERR_SHAPE
+    assert L.dflash2_verify_reject(*args, 1.0, FAKE, 2**31 - 32, *tail[2:]) == df2.DF2_ERR_SHAPE
 
 
 def test_empty_batch_is_a_no_op():
@@ -191,13 +192,13 @@ def test_empty_batch_is_a_no_op():
     assert L.dflash2_pair_scores(None, None, None, None, 1, 151936, None, None, None, None, 0, 7, 16, 5120,
                                  256, 0, None, None, 0, None) == df2.DF2_OK
     for mode in (0, 1, 2):
-        assert L.dflash2_path_viterbi(None, None, 0, 7, 16, mode, 1.0, None, None, None, None, None,
+        assert L.dflash2_path_viterbi(None, None, 0, 7, 16, mode, 1.0, None, 0, None, None, None, None,
                                       None) == df2.DF2_OK
     assert L.dflash2_pair_scores_tab(None, None, None, None, 151936, None, None, 0, 7, 16, 5120, 256, 0, None,
                                      None, 0, None) == df2.DF2_OK
     assert L.dflash2_dynconv2(None, None, None, None, 0, 16, 5120, 16, None, 1, None, 0, None) == df2.DF2_OK
     assert L.dflash2_verify_greedy(None, 1, 151936, None, 0, 15, None, None, None, 0, None) == df2.DF2_OK
-    assert L.dflash2_verify_reject(None, 1, 151936, None, None, None, None, 0, 15, 16, 1.0, None, None,
+    assert L.dflash2_verify_reject(None, 1, 151936, None, None, None, None, 0, 15, 16, 1.0, None, 0, None,
                                    None, None, 0, None) == df2.DF2_OK
 
 

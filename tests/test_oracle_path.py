@@ -166,3 +166,16 @@ def test_sample_requires_positive_temperature(orc):
     S = synth.pair_score_lattice(1, 2, 4, seed=1).numpy()
     with pytest.raises(orc.OracleError):
         orc.path(S, np.zeros((1, 2, 4), np.int32), orc.PATH_SAMPLE, temperature=0.0)
+
+
+def test_sample_sub_ranges_equal_one_call(orc):
+    """Sampled paths draw uniforms keyed by the request's batch index: two
+    sub-range calls with their batch indices equal one call."""
+    S = synth.pair_score_lattice(20, 6, 16, seed=8, spread=1.0).numpy()
+    idx = np.broadcast_to(np.arange(16, dtype=np.int32), (20, 6, 16)).copy()
+    full = orc.path(S, idx, orc.PATH_SAMPLE, temperature=1.0, seed=3)
+    lo = orc.path(S[:8], idx[:8], orc.PATH_SAMPLE, temperature=1.0, seed=3, b_ids=np.arange(8))
+    hi = orc.path(S[8:], idx[8:], orc.PATH_SAMPLE, temperature=1.0, seed=3, b_ids=np.arange(8, 20))
+    np.testing.assert_array_equal(np.concatenate([lo["rank"], hi["rank"]]), full["rank"])
+    wrong = orc.path(S[8:], idx[8:], orc.PATH_SAMPLE, temperature=1.0, seed=3)
+    assert not np.array_equal(wrong["rank"], full["rank"][8:])

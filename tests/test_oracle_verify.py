@@ -143,3 +143,24 @@ def test_reject_requires_positive_temperature(orc):
         orc.verify_reject(Z, np.zeros((1, 1), np.int32), np.zeros((1, 1), np.int32),
                           np.zeros((1, 1, 4), np.int32), np.full((1, 1, 4), 0.25, np.float32),
                           0.0, seed=1)
+
+
+def test_reject_sub_ranges_equal_one_call(orc):
+    """The uniforms are keyed by the request's index in the whole batch, so
+    verifying a batch as two sub-ranges (with their batch indices) gives
+    exactly the result of one call over the batch, and a sub-range called
+    with the wrong indices (counted from 0) draws different uniforms."""
+    rng = np.random.default_rng(4)
+    B, T, V, K = 24, 5, 50, 4
+    Z = (rng.normal(size=(B, T + 1, V)) * 2).astype(np.float32)
+    idx = np.stack([rng.choice(V, size=(T, K), replace=False) for _ in range(B)]).astype(np.int32)
+    rank = rng.integers(0, K, size=(B, T)).astype(np.int32)
+    tok = np.take_along_axis(idx, rank[..., None], -1)[..., 0].astype(np.int32)
+    q = rng.dirichlet(np.ones(K), size=(B, T)).astype(np.float32)
+    full = orc.verify_reject(Z, tok, rank, idx, q, 1.0, 11)
+    parts = [orc.verify_reject(Z[a:b], tok[a:b], rank[a:b], idx[a:b], q[a:b], 1.0, 11, b_ids=np.arange(a, b))
+             for a, b in ((0, 9), (9, B))]
+    np.testing.assert_array_equal(np.concatenate([p["accept_len"] for p in parts]), full["accept_len"])
+    np.testing.assert_array_equal(np.concatenate([p["out_tok"] for p in parts]), full["out_tok"])
+    wrong = orc.verify_reject(Z[9:], tok[9:], rank[9:], idx[9:], q[9:], 1.0, 11)
+    assert not np.array_equal(wrong["out_tok"], full["out_tok"][9:])
