@@ -132,7 +132,9 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   const bool from_w0 = n0 < sn0;
   const uint16_t* wbase = from_w0 ? w0 + (int64_t)n0 * K : w1 + (int64_t)(n0 - sn0) * K;
   const int wrows = (from_w0 ? (sn0 < N ? sn0 : N) : N) - n0;
-  const uint32_t xbytes = (uint32_t)(x_rows * ldx * 2);
+  // in 64 bits: rows x ldx x 2 exceeds INT_MAX for tables over 2 GiB (the
+  // launcher keeps it under 2^32 - 2K - 16)
+  const uint32_t xbytes = (uint32_t)((uint64_t)(uint32_t)x_rows * (uint64_t)(uint32_t)ldx * 2u);
   const uint32_t wbytes = (uint32_t)((int64_t)wrows * K * 2);
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)sx, 0, (int)xbytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, (int)wbytes, kBufferWord3);
