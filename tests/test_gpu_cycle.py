@@ -3,11 +3,13 @@ captured as a HIP graph.
 
 Stages are chained on both sides (GPU: conv -> top-K -> pair scores -> path
 -> verify; oracle: the same from the same inputs).  The oracle recomputes a
-sample of requests one by one.  Top-K, greedy verification and conv are
-compared exactly / within tolerance; the path is compared exactly except for
-decisions that the score parity cannot decide: a decision whose oracle
-margin is below max(1e-6, 2 T max|dS| / max(1, |best|)) may flip, and is
-reported (dS = GPU minus oracle pair score)."""
+sample of requests one by one.  Top-K and greedy verification are compared
+exactly, conv outputs within 1e-3 of their terms' magnitudes; the path is
+compared exactly except where the decision that flipped is one the score
+parity cannot decide (tests/path_compare.py: its oracle margin is under
+1e-6 plus the allowance the score difference gives for that decision);
+such flips are counted, bounded and reported, and the verification of
+those requests is checked against the oracle run on the GPU's path."""
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,9 @@ import torch
 import oracle
 import synth
 from draft_selection_bf16_amd.cycle import ConvSite, Cycle
-from gpu_util import DEV, NEAR_TIE, bf16_ulp_close, close, conv_error_bound, report
+from gpu_util import (DEV, NEAR_TIE, bf16_ulp_close, close, conv_close, conv_error_bound, conv_rel_close,
+                      conv_rel_close_bf16, conv_term_scale, report)
+from path_compare import compare_path
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -60,25 +64,6 @@ def oracle_cycle(cyc, rows, w, seed):
     return dict(idx=idx, val=val, S=S)
 
 
-def compare_path(g_rank, o_path, S_g, S_o, T):
-    """Exact unless the first differing decision is numerically undecided."""
-    fin = np.isfinite(S_o)
-    dS = float(np.max(np.abs(S_g[fin] - S_o[fin]))) if fin.any() else 0.0
-    allow = max(NEAR_TIE, 2 * T * dS)
-    undecided, bad = 0, 0
-    for b in range(g_rank.shape[0]):
-        if np.array_equal(g_rank[b], o_path["rank"][b]):
-            continue
-        t = int(np.flatnonzero(g_rank[b] != o_path["rank"][b])[-1])
-        m = float(np.min(o_path["margin"][b]))
-        if m < allow:
-            undecided += 1
-        else:
-            bad += 1
-    near = int((o_path["margin"] < NEAR_TIE).sum())
-    return dict(max_dS=dS, undecided_flips=undecided, bad=bad, near_ties=near)
-
-
 def check_cycle(cyc, w, rows, label, check_conv_sites=(0,)):
     torch.cuda.synchronize()
     o = oracle_cycle(cyc, rows, w, w.seed)
@@ -89,17 +74,26 @@ def check_cycle(cyc, w, rows, label, check_conv_sites=(0,)):
     Sg = cyc.scores[rows].cpu().numpy()
     worst = close(Sg, o["S"])
     mode = {0: oracle.PATH_VITERBI, 1: oracle.PATH_GREEDY, 2: oracle.PATH_SAMPLE}[cyc.path_mode]
-    op = oracle.path(o["S"], o["idx"], mode, temperature=cyc.tau, seed=int(cyc.seed.item()),
-                     b_ids=np.array(rows))
+    seed = int(cyc.seed.item())
+    g_rows = np.array(rows)
+    op = oracle.path(o["S"], o["idx"], mode, temperature=cyc.tau, seed=seed, b_ids=g_rows)
     g_rank = cyc.path_rank[rows].cpu().numpy()
-    cmp = compare_path(g_rank, op, Sg, o["S"], w.T)
+    cmp = compare_path(g_rank, op, Sg, o["S"], mode, cyc.tau, w.T)
     assert cmp["bad"] == 0, cmp
-    # verification from the oracle's own path
+    # a flip is rare: at most one checked request in eight may take one
+    assert cmp["undecided_flips"] <= max(1, len(rows) // 8), cmp
+    # verification: rows whose path equals the oracle's are compared with the
+    # oracle's own chain; rows with an excused flip with the oracle's
+    # verification run on the GPU's path (and the GPU's proposal q)
     same = np.array([np.array_equal(g_rank[i], op["rank"][i]) for i in range(len(rows))])
+    g_tok = cyc.path_tok[rows].cpu().numpy()
+    g_q = cyc.q[rows].cpu().numpy()
+    v_tok = np.where(same[:, None], op["tok"], g_tok)
+    v_rank = np.where(same[:, None], op["rank"], g_rank)
+    v_q = np.where(same[:, None, None], op["q"], g_q)
     Z = cyc.target[rows].cpu()
     ga = cyc.accept_len[rows].cpu().numpy()
     go = cyc.out_tok[rows].cpu().numpy()
-    g_rows = np.array(rows)
     greedy = np.ones(len(rows), bool)
     if cyc.verify == "reject":
         greedy[:] = False
@@ -107,33 +101,37 @@ def check_cycle(cyc, w, rows, label, check_conv_sites=(0,)):
         greedy = g_rows < cyc.greedy_rows
     near_v = 0
     if greedy.any():
-        ov = oracle.verify_greedy(Z[greedy], op["tok"][greedy])
-        s = same[greedy]
-        assert np.array_equal(ga[greedy][s], ov["accept_len"][s])
-        assert np.array_equal(go[greedy][s], ov["out_tok"][s])
+        ov = oracle.verify_greedy(Z[greedy], v_tok[greedy])
+        assert np.array_equal(ga[greedy], ov["accept_len"])
+        assert np.array_equal(go[greedy], ov["out_tok"])
     if (~greedy).any():
         sel = ~greedy
-        # counters use the request's index within the verify call (the
-        # reject half starts at greedy_rows in mixed mode)
-        off = cyc.greedy_rows if cyc.verify == "mixed" else 0
-        ov = oracle.verify_reject(Z[sel], op["tok"][sel], op["rank"][sel], o["idx"][sel], op["q"][sel],
-                                  cyc.tau, int(cyc.seed.item()), b_ids=g_rows[sel] - off)
+        # Philox counters are keyed by the request's index in the whole batch
+        ov = oracle.verify_reject(Z[sel], v_tok[sel], v_rank[sel], o["idx"][sel], v_q[sel],
+                                  cyc.tau, seed, b_ids=g_rows[sel])
         for i in range(int(sel.sum())):
-            if not same[sel][i]:
-                continue
             if ga[sel][i] == ov["accept_len"][i] and np.array_equal(go[sel][i], ov["out_tok"][i]):
                 continue
             ma = ov["margin_accept"][i]
             assert (np.nanmin(ma[: ov["accept_len"][i] + 1]) < NEAR_TIE or
                     ov["margin_sample"][i] < NEAR_TIE), ("reject mismatch", i)
             near_v += 1
+    worst_conv = 0.0
     for s in check_conv_sites:
         if s >= len(cyc.conv_sites):
             continue
         site = cyc.conv_sites[s]
         args = (site.x[rows].cpu(), site.x_prev[rows].cpu(), site.w.cpu(),
                 None if site.base is None else site.base.cpu())
-        bf16_ulp_close(site.y[rows], oracle.dynconv2(*args), conv_error_bound(*args))
+        yo = oracle.dynconv2(*args)
+        if site.y.dtype == torch.bfloat16:
+            conv_rel_close_bf16(site.y[rows], yo, conv_term_scale(*args))
+            bf16_ulp_close(site.y[rows], yo, conv_error_bound(*args))
+        else:
+            yg = site.y[rows].cpu().numpy()
+            worst_conv = max(worst_conv, conv_rel_close(yg, yo, conv_term_scale(*args)))
+            conv_close(yg, yo, conv_error_bound(*args))
+    cmp.pop("excused_rows")
     report(label, rows=len(rows), S_worst=round(worst, 4), mean_accept=float(ga.mean()),
            reject_near_ties=near_v, **cmp)
 
@@ -254,18 +252,27 @@ def test_stress_b64_blk16_v262144_graph_1000_replays():
     cyc.set_seed(4_000_000)
     cyc.replay()
     check_cycle(cyc, w, rows, w.name + " cycle 0", check_conv_sites=(0, 19))
-    o = oracle_cycle(cyc, list(range(32, 64)), w, 0)
+    half = list(range(32, 64))
+    o = oracle_cycle(cyc, half, w, 0)
     op = oracle.path(o["S"], o["idx"], oracle.PATH_VITERBI)
     g_rank = cyc.path_rank[32:].cpu().numpy()
+    cmp = compare_path(g_rank, op, cyc.scores[32:].cpu().numpy(), o["S"], oracle.PATH_VITERBI, cyc.tau, w.T)
+    assert cmp["bad"] == 0 and cmp["undecided_flips"] <= 4, cmp
+    # requests whose path flipped on an undecided decision are verified
+    # against the oracle run on the GPU's own path
     same = np.array([np.array_equal(g_rank[i], op["rank"][i]) for i in range(32)])
+    v_tok = np.where(same[:, None], op["tok"], cyc.path_tok[32:].cpu().numpy())
+    v_rank = np.where(same[:, None], op["rank"], g_rank)
+    v_q = np.where(same[:, None, None], op["q"], cyc.q[32:].cpu().numpy())
     Z = cyc.target[32:].cpu()
     near = 0
     for c in sorted(checks):
         acc, out = results[c]
-        ov = oracle.verify_reject(Z, op["tok"], op["rank"], o["idx"], op["q"], cyc.tau, 4_000_000 + c)
+        # the reject half's Philox counters carry the requests' batch indices
+        ov = oracle.verify_reject(Z, v_tok, v_rank, o["idx"], v_q, cyc.tau, 4_000_000 + c, b_ids=np.array(half))
         ga, go = acc[32:].cpu().numpy(), out[32:].cpu().numpy()
         for i in range(32):
-            if not same[i] or (ga[i] == ov["accept_len"][i] and np.array_equal(go[i], ov["out_tok"][i])):
+            if ga[i] == ov["accept_len"][i] and np.array_equal(go[i], ov["out_tok"][i]):
                 continue
             ma = ov["margin_accept"][i]
             assert np.nanmin(ma[: ov["accept_len"][i] + 1]) < NEAR_TIE or \
@@ -273,4 +280,5 @@ def test_stress_b64_blk16_v262144_graph_1000_replays():
             near += 1
         # the greedy half does not depend on the seed
         assert torch.equal(acc[:32], results[0][0][:32])
-    report("stress 1000 replays", checked_cycles=len(checks), reject_near_ties=near)
+    report("stress 1000 replays", checked_cycles=len(checks), reject_near_ties=near,
+           undecided_flips=cmp["undecided_flips"])

@@ -5,8 +5,10 @@ sizes, sampled rows at the full vocabulary), the scores against
 oracle.pair_scores_tab on an oracle-built table, and end to end (GPU tables,
 then GPU scores) against the oracle's pair scores from the embeddings.
 Scores within 1e-3 relative (rms floor), as for the projection path; table
-rows within the forward error bound of an fp32 sum of exact bf16 products
-(gpu_util.gemm_error_bound)."""
+rows within 1e-3 relative, each magnitude floored at 1 % of the rms entry
+(an entry is a sum of d products and may cancel), and within the forward
+error bound of an fp32 sum of exact bf16 products (gpu_util.gemm_error_bound)
+as well."""
 import numpy as np
 import pytest
 import torch
@@ -58,8 +60,11 @@ def test_selector_tables_all_rows(r):
     wa, wb, _ = synth.selector_weights(w)
     tab = _tables_gpu(E, wa, wb)
     torch.cuda.synchronize()
-    worst = conv_close(tab.cpu().numpy(), oracle.selector_tables(E, wa, wb), _table_bound(E, wa, wb))
-    report("selector_tables", V=w.V, d=w.d, r=r, worst_err_over_bound=round(worst, 4))
+    tg, to = tab.cpu().numpy(), oracle.selector_tables(E, wa, wb)
+    worst = close(tg, to, floor=1e-2)
+    worst_b = conv_close(tg, to, _table_bound(E, wa, wb))
+    report("selector_tables", V=w.V, d=w.d, r=r, worst_err_over_1e3=round(worst, 4),
+           worst_err_over_sum_bound=round(worst_b, 4))
 
 
 @pytest.mark.parametrize("gate", [0, 1])
@@ -150,6 +155,8 @@ def test_pair_scores_tab_full_size():
     rng = np.random.default_rng(78)
     rows = np.r_[0, 1, 127, 128, w.V - 128, w.V - 1, rng.integers(0, w.V, 58)]
     Er = Ec[torch.from_numpy(rows)]
-    worst_t = conv_close(tab[torch.from_numpy(rows).to(DEV)].cpu().numpy(),
-                         oracle.selector_tables(Ec, wac, wbc, rows=rows), _table_bound(Er, wac, wbc))
+    tg = tab[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    to = oracle.selector_tables(Ec, wac, wbc, rows=rows)
+    worst_t = close(tg, to, floor=1e-2)
+    conv_close(tg, to, _table_bound(Er, wac, wbc))
     report("pair_scores_tab full", worst_err_over_bound=round(worst, 4), table_rows=round(worst_t, 4))
