@@ -33,6 +33,7 @@ EXPORTS = [
     "dflash2_path_viterbi",
     "dflash2_dynconv2_workspace_bytes", "dflash2_dynconv2",
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
+    "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_noalloc_max_bytes",
     "dflash2_philox4x64", "dflash2_profile_start", "dflash2_profile_stop",
 ]
 
@@ -79,6 +80,8 @@ def lib():
         L.dflash2_verify_workspace_bytes.restype = SZ
         L.dflash2_verify_greedy.argtypes = [P, I, I64, P, I, I, P, P, P, SZ, P]
         L.dflash2_verify_reject.argtypes = [P, I, I64, P, P, P, P, I, I, I, F, P, I, P, P, P, SZ, P]
+        L.dflash2_verify_greedy_noalloc.argtypes = [P, I, I64, P, I, I, P, P, P]
+        L.dflash2_verify_greedy_noalloc_max_bytes.restype = SZ
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
         L.dflash2_profile_start.argtypes = [C.c_char_p, I]
         L.dflash2_profile_start.restype = I
@@ -88,6 +91,7 @@ def lib():
                      "dflash2_pair_scores_tab", "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
                      "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
+                     "dflash2_verify_greedy_noalloc",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
         _lib = L
@@ -227,6 +231,19 @@ def dflash2_verify_greedy(target, path_tok, accept_len, out_tok, ws, stream=None
     _check(lib().dflash2_verify_greedy(_ptr(target), _dt(target), V, _ptr(path_tok), B, T1 - 1,
                                        _ptr(accept_len), _ptr(out_tok), _ptr(ws), _bytes(ws),
                                        _stream(stream)), "dflash2_verify_greedy")
+
+
+def dflash2_verify_greedy_noalloc_max_bytes() -> int:
+    return int(lib().dflash2_verify_greedy_noalloc_max_bytes())
+
+
+def dflash2_verify_greedy_noalloc(target, path_tok, accept_len, out_tok, stream=None):
+    """dflash2_verify_greedy with the library's fixed device scratch instead
+    of a workspace (for callers that cannot allocate)."""
+    B, T1, V = target.shape
+    _check(lib().dflash2_verify_greedy_noalloc(_ptr(target), _dt(target), V, _ptr(path_tok), B, T1 - 1,
+                                               _ptr(accept_len), _ptr(out_tok), _stream(stream)),
+           "dflash2_verify_greedy_noalloc")
 
 
 def dflash2_verify_reject(target, path_tok, path_rank, cand_idx, q, temperature, seed_dev,

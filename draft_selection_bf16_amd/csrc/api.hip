@@ -5,6 +5,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "dflash2.h"
 #include "df2_internal.h"
 
@@ -51,6 +54,44 @@ constexpr int kMaxB = 1 << 20;
 
 }  // namespace
 
+// Scratch of dflash2_verify_greedy_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends.  Host code never passes this name
+// to a kernel (on the host it is only a stand-in for the symbol); it uses
+// the device address that scratch_address() resolves for each device.
+constexpr size_t kScratchBytes = (size_t)1 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_address(void** out, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DF2_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, fn);
+      if (!p) return fail(DF2_ERR_HIP, "%s: no device address for the scratch array", fn);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return DF2_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int dflash2_abi_version(void) { return DFLASH2_ABI_VERSION; }
@@ -77,6 +118,8 @@ int dflash2_init(void) {
   hipDeviceProp_t prop;
   e = hipGetDeviceProperties(&prop, dev);
   if (e != hipSuccess) return hip_status(e, "dflash2_init");
+  void* scratch_dev = nullptr;
+  if (int st = scratch_address(&scratch_dev, "dflash2_init")) return st;
   g_err[0] = 0;
   return DF2_OK;
 }
@@ -474,6 +517,34 @@ int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, cons
   return hip_status(launch_verify_greedy(target_logits, dt, vocab, path_tok, B, T, accept_len, out_tok,
                                          ws, plan, stream),
                     "dflash2_verify_greedy");
+}
+
+size_t dflash2_verify_greedy_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int dflash2_verify_greedy_noalloc(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                                  int B, int T, int32_t* accept_len, int32_t* out_tok, hipStream_t stream) {
+  int st = check_dt(dt, "dflash2_verify_greedy_noalloc");
+  if (st) return st;
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_verify_greedy_noalloc: vocab %lld",
+          (long long)vocab);
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_verify_greedy_noalloc: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_greedy_noalloc: T %d not in [1, %d]", T, kMaxT);
+  if (B == 0) return DF2_OK;
+  REQUIRE(target_logits && path_tok && accept_len && out_tok, DF2_ERR_NULL,
+          "dflash2_verify_greedy_noalloc: null pointer argument");
+  REQUIRE(((uintptr_t)target_logits % elem_size(dt)) == 0, DF2_ERR_SHAPE,
+          "dflash2_verify_greedy_noalloc: misaligned logits");
+  VerifyPlan plan = verify_plan(B, T, vocab);
+  REQUIRE(plan.ws_bytes <= kScratchBytes, DF2_ERR_WORKSPACE,
+          "dflash2_verify_greedy_noalloc: this size needs %zu bytes of scratch, more than the fixed %zu "
+          "(use dflash2_verify_greedy with a workspace)", plan.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (int st2 = scratch_address(&ws, "dflash2_verify_greedy_noalloc")) return st2;
+  // the kernels write every partial result before they read it: nothing
+  // in the scratch has to start at zero
+  return hip_status(launch_verify_greedy(target_logits, dt, vocab, path_tok, B, T, accept_len, out_tok,
+                                         ws, plan, stream),
+                    "dflash2_verify_greedy_noalloc");
 }
 
 int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,

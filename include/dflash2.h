@@ -235,6 +235,27 @@ int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, cons
                           size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Greedy verification that allocates nothing, for callers that cannot
+ * allocate device memory or hand over a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, results and errors as dflash2_verify_greedy, without
+ * (ws, ws_bytes): its scratch is a fixed device array of
+ * dflash2_verify_greedy_noalloc_max_bytes() bytes (1 MiB), one per GPU,
+ * held until the process ends.  A size whose
+ * dflash2_verify_workspace_bytes(B, T, vocab) exceeds that returns
+ * DF2_ERR_WORKSPACE before anything is launched (batch 64 x block 16 at
+ * vocab 262,144 needs 34 KB; up to about 2,300 requests of block 16 fit).  The array's address is looked up once per
+ * device, by dflash2_init or by the first call on that device; call
+ * dflash2_init on each device before capturing a graph.  Every call on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing
+ * in the array needs to start at zero; it keeps the last call's contents.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_verify_greedy_noalloc_max_bytes(void);
+int dflash2_verify_greedy_noalloc(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
+                                  int B, int T, int32_t* accept_len, int32_t* out_tok, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Speculative rejection sampling.  [KDP] "A lightweight path selector":
  * rejection sampling restores the exact target distribution; [WC]
  * "輸出完全一致".  With p_t = softmax(Z_t / tau):

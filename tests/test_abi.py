@@ -183,6 +183,23 @@ def test_verify_validation():
     assert L.dflash2_verify_reject(*args, 1.0, FAKE, 2**31 - 32, *tail[2:]) == df2.DF2_ERR_SHAPE
 
 
+def test_verify_greedy_noalloc_validation():
+    """The allocation-free greedy verification checks its arguments, and
+    rejects a size whose scratch exceeds its fixed array, before it looks up
+    the array or launches anything."""
+    L = df2.lib()
+    f = L.dflash2_verify_greedy_noalloc
+    assert df2.dflash2_verify_greedy_noalloc_max_bytes() == 1 << 20
+    assert f(FAKE, 5, 151936, FAKE, 32, 15, FAKE, FAKE, None) == df2.DF2_ERR_DTYPE
+    assert f(FAKE, 1, 151936, FAKE, 32, 64, FAKE, FAKE, None) == df2.DF2_ERR_SHAPE
+    assert f(FAKE, 1, 151936, None, 32, 15, FAKE, FAKE, None) == df2.DF2_ERR_NULL
+    assert f(C.c_void_p(0x100001), 1, 151936, FAKE, 32, 15, FAKE, FAKE, None) == df2.DF2_ERR_SHAPE
+    assert df2.dflash2_verify_workspace_bytes(4096, 15, 151936) > (1 << 20)
+    assert f(FAKE, 1, 151936, FAKE, 4096, 15, FAKE, FAKE, None) == df2.DF2_ERR_WORKSPACE
+    assert "scratch" in _last()
+    assert f(None, 1, 151936, None, 0, 15, None, None, None) == df2.DF2_OK
+
+
 def test_empty_batch_is_a_no_op():
     """A batch of zero requests is valid everywhere: each entry point checks
     its sizes and returns DF2_OK before it touches a pointer or the runtime
