@@ -7,7 +7,7 @@ raw 16-bit patterns.  Every function returns fresh numpy outputs.
 
 Parity status per function (details in the C source):
   topk, project, pair_scores, path, verify_greedy, verify_reject, dynconv2,
-  philox -- all pinned by the CPU tests in tests/test_oracle_*.py;
+  lm_head_topk, philox -- all pinned by the CPU tests in tests/test_oracle_*.py;
   selector_tables, pair_scores_tab (numpy, below) -- pinned by
   tests/test_oracle_tables.py.
 """
@@ -58,8 +58,10 @@ def _declare(L):
     L.oracle_verify_reject.argtypes = [P, C.c_int, I64, P, P, P, P, C.c_int, C.c_int, C.c_int,
                                        F64, U64, P, P, P, P, P, P]
     L.oracle_dynconv2.argtypes = [P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P]
+    L.oracle_lm_head_topk.argtypes = [P, P, I64, I64, C.c_int, C.c_int, P, P]
     for f in ("oracle_topk", "oracle_project", "oracle_pair_scores", "oracle_path",
-              "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2"):
+              "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2",
+              "oracle_lm_head_topk"):
         getattr(L, f).restype = C.c_int
 
 
@@ -124,6 +126,22 @@ def topk(logits, k: int):
     idx = np.zeros(a.shape[:-1] + (k,), dtype=np.int32)
     val = np.zeros(a.shape[:-1] + (k,), dtype=np.float32)
     _check(lib().oracle_topk(_ptr(a), dt, rows, V, k, _ptr(idx), _ptr(val)), "oracle_topk")
+    return idx, val
+
+
+def lm_head_topk(h, emb, k: int):
+    """Drafter logits z = h E^T (float64) through the shared LM head, then
+    the k best per row.  h [rows, d] bf16, emb [V, d] bf16 ->
+    (idx int32 [rows, k], val float64 [rows, k])."""
+    ha, hdt = host(h)
+    ea, edt = host(emb)
+    assert hdt == BF16 and edt == BF16
+    rows, d = ha.shape
+    V = ea.shape[0]
+    idx = np.zeros((rows, k), np.int32)
+    val = np.zeros((rows, k), np.float64)
+    _check(lib().oracle_lm_head_topk(_ptr(ha), _ptr(ea), rows, V, d, k, _ptr(idx), _ptr(val)),
+           "oracle_lm_head_topk")
     return idx, val
 
 

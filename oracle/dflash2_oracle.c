@@ -196,6 +196,67 @@ int oracle_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
 }
 
 /* ------------------------------------------------------------------ */
+/* Drafter logits through the LM head shared with the target, then the  */
+/* K best per row.  "大模型推理，加速王者：DFlash" (m.163.com), paragraph */
+/* before the three-step pipeline: the drafter reuses the target's      */
+/* embedding and LM head; [WC] "坑 2"-"坑 4": the selector takes its      */
+/* top-k candidates from that dense lm_head.  For each row r (a draft   */
+/* position's final hidden state h[r], bf16) and every token v:         */
+/*   z[r][v] = sum_k h[r][k] * E[v][k]        (double, E bf16 [V, d])     */
+/* then the K best by (z descending, v ascending), as oracle_topk orders */
+/* a row.  out_val receives the selected logits in double.               */
+/* Pinned by: one-hot embedding rows (each logit is one entry of h,     */
+/* known by inspection, down to the last of the d coordinates); a        */
+/* permutation of E's rows permutes the indices; scaling h by a power of */
+/* two scales the logits exactly; agreement with oracle_topk where the   */
+/* logits are exact in float.                                            */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+  double v;
+  int32_t i;
+} dvi_pair;
+
+static int by_dvalue_desc_index_asc(const void* pa, const void* pb) {
+  const dvi_pair* a = (const dvi_pair*)pa;
+  const dvi_pair* b = (const dvi_pair*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  return (a->i > b->i) - (a->i < b->i);
+}
+
+int oracle_lm_head_topk(const uint16_t* h, const uint16_t* emb, int64_t rows, int64_t vocab, int d,
+                        int k, int32_t* out_idx, double* out_val) {
+  if (k < 1 || k > vocab || d < 1) return 3;
+  dvi_pair* z = (dvi_pair*)malloc(sizeof(dvi_pair) * (size_t)vocab);
+  double* hr = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!z || !hr) {
+    free(z);
+    free(hr);
+    return 1;
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int q = 0; q < d; ++q) hr[q] = (double)bf16_value(h[r * d + q]);
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < vocab; ++v) {
+      const uint16_t* e = emb + v * d;
+      double acc = 0.0;
+      for (int q = 0; q < d; ++q) acc += hr[q] * (double)bf16_value(e[q]);
+      z[v].v = acc;
+      z[v].i = (int32_t)v;
+    }
+    qsort(z, (size_t)vocab, sizeof(dvi_pair), by_dvalue_desc_index_asc);
+    for (int j = 0; j < k; ++j) {
+      out_idx[r * k + j] = z[j].i;
+      out_val[r * k + j] = z[j].v;
+    }
+  }
+  free(z);
+  free(hr);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Rank-r projections.  [KDP] "A lightweight path selector": A and B     */
 /* give each token a compact 256-dimensional embedding and H(h_t) gates  */
 /* their match from the position's hidden state.  Reading: A(tok) =     */
