@@ -27,6 +27,7 @@ DF2_GATE_IDENTITY, DF2_GATE_SIGMOID = 0, 1
 EXPORTS = [
     "dflash2_abi_version", "dflash2_status_string", "dflash2_last_error", "dflash2_init",
     "dflash2_topk_workspace_bytes", "dflash2_topk",
+    "dflash2_lm_head_topk_workspace_bytes", "dflash2_lm_head_topk",
     "dflash2_pair_scores_workspace_bytes", "dflash2_pair_scores",
     "dflash2_selector_tables", "dflash2_pair_scores_tab_workspace_bytes", "dflash2_pair_scores_tab",
     "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
@@ -63,6 +64,9 @@ def lib():
         L.dflash2_topk_workspace_bytes.argtypes = [I64, I64, I]
         L.dflash2_topk_workspace_bytes.restype = SZ
         L.dflash2_topk.argtypes = [P, I, I64, I64, I, P, P, P, SZ, P]
+        L.dflash2_lm_head_topk_workspace_bytes.argtypes = [I, I64, I, I]
+        L.dflash2_lm_head_topk_workspace_bytes.restype = SZ
+        L.dflash2_lm_head_topk.argtypes = [P, P, I, I64, I, I, I, P, P, P, SZ, P]
         L.dflash2_pair_scores_workspace_bytes.argtypes = [I, I, I, I, I]
         L.dflash2_pair_scores_workspace_bytes.restype = SZ
         L.dflash2_pair_scores.argtypes = [P, P, P, P, I, I64, P, P, P, P, I, I, I, I, I, I, P, P, SZ, P]
@@ -87,7 +91,7 @@ def lib():
         L.dflash2_profile_start.restype = I
         L.dflash2_profile_stop.argtypes = [P, I, P]
         L.dflash2_profile_stop.restype = I
-        for name in ("dflash2_topk", "dflash2_pair_scores", "dflash2_selector_tables",
+        for name in ("dflash2_topk", "dflash2_lm_head_topk", "dflash2_pair_scores", "dflash2_selector_tables",
                      "dflash2_pair_scores_tab", "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
                      "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
@@ -146,6 +150,21 @@ def dflash2_topk(logits, k, out_idx, out_val, ws=None, stream=None):
     rows = logits.numel() // V if V else 0
     _check(lib().dflash2_topk(_ptr(logits), _dt(logits), rows, V, int(k), _ptr(out_idx), _ptr(out_val),
                               _ptr(ws), _bytes(ws), _stream(stream)), "dflash2_topk")
+
+
+def dflash2_lm_head_topk_workspace_bytes(rows: int, vocab: int, d: int, k: int) -> int:
+    return int(lib().dflash2_lm_head_topk_workspace_bytes(rows, vocab, d, k))
+
+
+def dflash2_lm_head_topk(h, emb, k, out_idx, out_val, ws, stream=None):
+    """h [..., d] bf16, emb [V, d] bf16 -> the k best tokens of h E^T per row
+    (out_idx int32 [..., k], out_val fp32 [..., k])."""
+    d = h.shape[-1]
+    rows = h.numel() // d if d else 0
+    V = emb.shape[0]
+    _check(lib().dflash2_lm_head_topk(_ptr(h), _ptr(emb), _dt(emb), V, rows, d, int(k), _ptr(out_idx),
+                                      _ptr(out_val), _ptr(ws), _bytes(ws), _stream(stream)),
+           "dflash2_lm_head_topk")
 
 
 def dflash2_pair_scores_workspace_bytes(B, T, K, d, r) -> int:

@@ -147,6 +147,31 @@ int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
                     "dflash2_topk");
 }
 
+// ------------------------------------------------------------------ LM head + top-K
+size_t dflash2_lm_head_topk_workspace_bytes(int rows, int64_t vocab, int d, int k) {
+  if (rows <= 0 || vocab <= 0 || d <= 0) return 0;
+  (void)k;
+  return lmhead_plan(rows, vocab, d).ws_bytes;
+}
+
+int dflash2_lm_head_topk(const void* h, const void* emb, int emb_dt, int64_t vocab, int rows, int d, int k,
+                         int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_lm_head_topk: the LM head must be BF16");
+  REQUIRE(rows >= 0 && rows <= kMaxB, DF2_ERR_SHAPE, "dflash2_lm_head_topk: rows %d", rows);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_lm_head_topk: vocab %lld", (long long)vocab);
+  REQUIRE(d >= 64 && d % 64 == 0 && d <= 65536, DF2_ERR_SHAPE,
+          "dflash2_lm_head_topk: d %d is not a multiple of 64 in [64, 65536]", d);
+  REQUIRE(k >= 1 && k <= 16 && k <= vocab, DF2_ERR_SHAPE, "dflash2_lm_head_topk: k %d not in [1, min(16, vocab)]", k);
+  if (rows == 0) return DF2_OK;
+  REQUIRE(h && emb && out_idx && out_val, DF2_ERR_NULL, "dflash2_lm_head_topk: null pointer argument");
+  REQUIRE(aligned16(h) && aligned16(emb), DF2_ERR_SHAPE, "dflash2_lm_head_topk: h/emb must be 16-byte aligned");
+  LmHeadPlan plan = lmhead_plan(rows, vocab, d);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_lm_head_topk: workspace %zu < %zu bytes",
+          ws_bytes, plan.ws_bytes);
+  return hip_status(launch_lmhead_topk(h, emb, vocab, rows, d, k, out_idx, out_val, ws, plan, stream),
+                    "dflash2_lm_head_topk");
+}
+
 // ------------------------------------------------------------------ pair scores
 namespace {
 // projection tiling: 128-row tiles, one work-group per CU, 8 waves (two per

@@ -146,6 +146,19 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
                            int B, int L, int d, int group, void* y, int y_dt, void* ws,
                            const ConvPlan& plan, hipStream_t stream);
 
+// ---- drafter LM head fused with the top-K ----------------------------------
+struct LmHeadPlan {
+  int mblocks;      // 128-row blocks of h
+  int nblocks;      // 128-token blocks of the vocabulary
+  int nranges;      // token ranges (work-groups per row block)
+  int xcd_groups;   // nranges % 8 == 0: a range's row blocks run on one XCD
+  size_t ws_bytes;  // per-range best-16 keys [M, nranges, 16]
+};
+LmHeadPlan lmhead_plan(int M, int64_t vocab, int d);
+hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int M, int d, int k,
+                              int32_t* out_idx, float* out_val, void* ws, const LmHeadPlan& plan,
+                              hipStream_t stream);
+
 // ---- Philox words -----------------------------------------------------------
 hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,
                          uint64_t* out, hipStream_t stream);

@@ -20,6 +20,7 @@
 // of register copies.
 #include "df2_device.h"
 #include "df2_internal.h"
+#include "mfma_tile.h"
 
 namespace df2 {
 
@@ -30,7 +31,7 @@ extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
 namespace gemm {
 
-constexpr int BK = 64;
+using mfma::BK;
 constexpr int kXcds = 8;
 
 constexpr int kMaxSeg = 4;
@@ -52,33 +53,11 @@ __device__ __forceinline__ float apply_gate(float z, int gate) {
 
 // The K-tiles are copied by direct buffer-to-LDS loads (no register
 // staging) into S LDS stages, S - 1 of them in flight while the MFMAs of the
-// current one run; one barrier per K-tile.
-//
-// LDS stage = X tile [BM][64] then W tile [BN][64], rows of 128 bytes.  One
-// load instruction of a wave fills 1 KB = 8 rows: lane i writes the 16-byte
-// slot (row i / 8, slot i % 8) and fetches the chunk slot ^ swz(row) of that
-// row, so the 16-byte chunks of a row are stored in swizzled order.  With
-// chunk c of row r stored at c ^ (r mod 8), the MFMA fragment reads (16
-// consecutive rows, one chunk each) are free of bank conflicts: 4 LDS cycles
-// per 16-byte read of a wave, measured with the bank-conflict counter (an
-// extra ^ (r / 8 mod 2) term doubles it to 8).  Rows outside the problem get
-// an out-of-range lane offset: the hardware writes zeros for them.
-
-__device__ __forceinline__ int swz(int r) { return r & 7; }
-
-// One direct buffer-to-LDS load of 16 bytes per lane (a plain device
-// function: called from the kernel template directly, the builtin keeps the
-// host-side launch stub from being emitted).
-typedef __attribute__((address_space(3))) void lds_void;
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// of this wave are outstanding (expcnt and lgkmcnt left unconstrained)
-__host__ __device__ constexpr int vmcnt_imm(int n) {
-  return (n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14);
-}
+// current one run; one barrier per K-tile.  The stage layout, the chunk
+// swizzle and the load helper are in mfma_tile.h.
+using mfma::load_lds16;
+using mfma::swz;
+using mfma::vmcnt_imm;
 
 // The tile of work-group `bid` of a grid of `nb` (the body of the GEMM
 // kernel; NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8)).

@@ -1,0 +1,358 @@
+// lmhead.hip -- drafter logits through the shared LM head, fused with the
+// per-row top-K, so that the logits never reach memory.
+//
+// The drafter reuses the target's embedding and LM head ("大模型推理，加速王者：
+// DFlash", paragraph before the three-step pipeline), and the selector takes
+// its top-k candidates from that dense head ("DFlash 2 讓 Qwen3.8-27B 快了兩倍",
+// 坑 2-4; the K = 16 kept per draft position: "DFlash 2: Keep Drafting
+// Parallel", sections "The right tokens are already there" and "A
+// lightweight path selector").  For rows r (draft positions, h [M, d]) and
+// tokens v (E [V, d]):  z[r, v] = <h_r, E_v>  (bf16 products, fp32 sums),
+// then the K best per row by (value desc, index asc).
+//
+// Two launches:
+//  1. lmhead_topk_kernel: the product on the matrix cores, 128 x 128 tiles
+//     (rows of h x tokens), K-tiles of 64 staged through 4 LDS stages by
+//     direct buffer-to-LDS loads (mfma_tile.h), 8 waves.  A work-group owns
+//     one 128-row block and a contiguous range of 128-token blocks; after
+//     each token block the fp32 tile goes through LDS, and thread (row, q)
+//     folds columns q, q + 4, ... of its row into a running best-16 list
+//     held in registers (a sorted insertion, taken only by the few values
+//     at or above the row's current threshold, found with one fp32 compare
+//     each).  At the end the four lists of a row are ranked against
+//     each other and the row's 16 best keys of the range are written out.
+//     The work-groups that share a token range (one per row block) run on
+//     one XCD, one after the other in dispatch order, so that the token
+//     block is fetched from memory once for all of them.
+//  2. lmhead_merge_kernel: one work-group per row merges the ranges' lists:
+//     the largest of the lists' 16th keys bounds the row's 16th best from
+//     below (that list holds 16 keys at least as large), and the keys that
+//     reach it are ranked against each other.
+// Keys are the 64-bit (value, index) codes of df2_device.h: the result is
+// the same whatever the order in which tokens are seen.
+#include "df2_device.h"
+#include "df2_internal.h"
+#include "mfma_tile.h"
+
+namespace df2 {
+
+extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+
+namespace {
+
+using mfma::BK;
+using mfma::load_lds16;
+using mfma::swz;
+using mfma::vmcnt_imm;
+
+constexpr int kBM = 128, kBN = 128, kS = 4, kNW = 8;   // tile, LDS stages, waves
+constexpr int kThreads = kNW * 64;
+constexpr int kWcol = kNW / 2;                          // waves along the tokens
+constexpr int kWM = kBM / 2, kWN = kBN / kWcol;         // 64 x 32 per wave
+constexpr int kFM = kWM / 16, kFN = kWN / 16;           // 4 x 2 blocks of 16 x 16
+constexpr int kALD = kBM / (8 * kNW), kBLD = kBN / (8 * kNW);   // loads per wave per stage
+constexpr int kLPW = kALD + kBLD;
+constexpr int kStage = (kBM + kBN) * BK * 2;             // bytes
+constexpr int kLds = kS * kStage;                        // 128 KB
+constexpr int kOld = kBN + 4;                            // padded row of the fp32 tile
+constexpr int kQ = kThreads / kBM;                       // threads per row (4)
+constexpr int kMaxRanges = 256;
+static_assert(kBM * kOld * 4 <= kLds, "fp32 tile fits the stages");
+static_assert(kBM * kQ * 16 * 8 <= kLds, "the rows' lists fit the stages");
+static_assert(kQ == 4 && kBN % kQ == 0, "four threads per row");
+
+// Insert key x into the list l[0] > l[1] > ... > l[15] (0 = empty) when it
+// is larger than l[15]: every entry moves down one place past x.
+__device__ __forceinline__ void insert16(uint64_t (&l)[16], uint64_t x) {
+#pragma unroll
+  for (int i = 15; i > 0; --i) {
+    const uint64_t up = l[i - 1];
+    l[i] = x > up ? up : (x > l[i] ? x : l[i]);
+  }
+  l[0] = x > l[0] ? x : l[0];
+}
+
+// grid: mblocks * nranges work-groups of kThreads; dynamic LDS kLds.
+// part[(row * nranges + range) * 16 + i]: the i-th best key of the range.
+__global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
+    const uint16_t* __restrict__ h, int M, const uint16_t* __restrict__ emb, int64_t vocab, int K,
+    int mblocks, int nranges, int nblocks, int xcd_groups, uint64_t* __restrict__ part) {
+  const int bid = blockIdx.x;
+  int mb, nr;
+  if (xcd_groups) {   // nranges % 8 == 0: the row blocks of a token range share an XCD
+    const int x = bid % 8, q = bid / 8;
+    mb = q % mblocks;
+    nr = (q / mblocks) * 8 + x;
+  } else {
+    mb = bid % mblocks;
+    nr = bid / mblocks;
+  }
+  const int nb0 = (int)((int64_t)nr * nblocks / nranges), nb1 = (int)((int64_t)(nr + 1) * nblocks / nranges);
+  const int m0 = mb * kBM;
+  const int wave = wave_id(), lane = lane_id();
+  const int wm = wave / kWcol, wn = wave % kWcol;
+  const int nkt = K / BK;
+  const int sub = lane >> 3, slot = lane & 7;
+  const int fr = lane & 15, fq = lane >> 4;
+  // h rows: one buffer resource for the row block (rows past M read zeros)
+  const int hrows = M - m0 < kBM ? M - m0 : kBM;
+  const __amdgpu_buffer_rsrc_t hres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(h + (int64_t)m0 * K), 0, hrows * K * 2, kBufferWord3);
+  const uint32_t kOut = 0xFFFFFFF0u - (uint32_t)K * 2u;   // beyond every buffer for the whole K walk
+  uint32_t xo[kALD], wo[kBLD];
+#pragma unroll
+  for (int a = 0; a < kALD; ++a) {
+    const int row = 8 * (wave + kNW * a) + sub;
+    xo[a] = row < hrows ? (uint32_t)((row * K + ((slot ^ swz(row)) * 8)) * 2) : kOut;
+  }
+  // fragment byte offsets inside a stage (rows fixed per lane, chunk 4 s + fq)
+  int ao[kFM][2], bo[kFN][2];
+#pragma unroll
+  for (int i = 0; i < kFM; ++i) {
+    const int r = wm * kWM + i * 16 + fr;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) ao[i][s2] = r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
+  }
+#pragma unroll
+  for (int j = 0; j < kFN; ++j) {
+    const int r = wn * kWN + j * 16 + fr;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) bo[j][s2] = kBM * 128 + r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
+  }
+  // the running best-16 of this thread: row tid / 4, columns tid % 4 + 4 j
+  const int my_row = threadIdx.x / kQ, my_q = threadIdx.x % kQ;
+  uint64_t best[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) best[i] = 0ull;
+  float* tile = (float*)dyn_lds;
+
+  for (int nb = nb0; nb < nb1; ++nb) {
+    const int64_t n0 = (int64_t)nb * kBN;
+    const int wrows = vocab - n0 < kBN ? (int)(vocab - n0) : kBN;
+    const __amdgpu_buffer_rsrc_t eres =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(emb + n0 * K), 0, wrows * K * 2, kBufferWord3);
+#pragma unroll
+    for (int b = 0; b < kBLD; ++b) {
+      const int row = 8 * (wave + kNW * b) + sub;
+      wo[b] = row < wrows ? (uint32_t)((row * K + ((slot ^ swz(row)) * 8)) * 2) : kOut;
+    }
+    auto issue = [&](int t) {
+      const bool in = t < nkt;
+      uint8_t* sb = dyn_lds + (t % kS) * kStage;
+      const int so = __builtin_amdgcn_readfirstlane(in ? t * BK * 2 : 0);
+      const uint32_t dx = in ? 0u : kOut;   // past the end: reads nothing
+#pragma unroll
+      for (int a = 0; a < kALD; ++a) load_lds16(hres, sb + (wave + kNW * a) * 8 * 128, xo[a] | dx, so);
+#pragma unroll
+      for (int b = 0; b < kBLD; ++b)
+        load_lds16(eres, sb + kBM * 128 + (wave + kNW * b) * 8 * 128, wo[b] | dx, so);
+    };
+    f32x4 acc[kFM][kFN];
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < kS - 1; ++t) issue(t);
+    for (int t = 0; t < nkt; ++t) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kS - 2) * kLPW));
+      __builtin_amdgcn_s_barrier();
+      issue(t + kS - 1);
+      const uint8_t* st = dyn_lds + (t % kS) * kStage;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        bf16x8 a[kFM], b[kFN];
+#pragma unroll
+        for (int i = 0; i < kFM; ++i) a[i] = *(const bf16x8*)(st + ao[i][s2]);
+#pragma unroll
+        for (int j = 0; j < kFN; ++j) b[j] = *(const bf16x8*)(st + bo[j][s2]);
+#pragma unroll
+        for (int i = 0; i < kFM; ++i)
+#pragma unroll
+          for (int j = 0; j < kFN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+    // the fp32 tile through LDS (lane holds column lane & 15, rows
+    // 4 (lane >> 4) + e of each 16 x 16 block), then each thread folds its
+    // columns of its row into its list
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();   // every wave is done with the stages
+#pragma unroll
+    for (int i = 0; i < kFM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          tile[(wm * kWM + i * 16 + fq * 4 + e) * kOld + wn * kWN + j * 16 + fr] = acc[i][j][e];
+    __syncthreads();
+    // The row's threshold: the largest of its four threads' 16th keys (the
+    // row has 16 keys at least that large, so no key at or below it can be
+    // among its 16 best).  One fp32 compare per value against the
+    // threshold's value marks the few that may pass; only those are made
+    // into keys and inserted (the wave runs the insertion loop as often as
+    // its busiest lane needs, not once per value).
+    const float* trow = tile + my_row * kOld;
+    const int ncols = wrows;   // columns past the vocabulary are not tokens
+    uint64_t thr = best[15];
+    {
+      const uint64_t o1 = shfl_xor_u64(thr, 1);
+      thr = o1 > thr ? o1 : thr;
+      const uint64_t o2 = shfl_xor_u64(thr, 2);
+      thr = o2 > thr ? o2 : thr;
+    }
+    const float tv = thr ? key_value(thr) : -INFINITY;
+    float v[kBN / kQ];
+#pragma unroll
+    for (int j = 0; j < kBN / kQ; ++j) v[j] = trow[my_q + kQ * j];
+    uint32_t mask = 0u;
+#pragma unroll
+    for (int j = 0; j < kBN / kQ; ++j)
+      mask |= (my_q + kQ * j < ncols && v[j] >= tv) ? (1u << j) : 0u;   // NaN never passes
+    while (mask) {
+      const int j = __builtin_ctz(mask);
+      mask &= mask - 1u;
+      const int c = my_q + kQ * j;
+      const uint64_t key = make_key(trow[c], (uint32_t)(n0 + c));
+      if (key > thr && key > best[15]) insert16(best, key);
+    }
+    __syncthreads();   // the tile is read before the next block's stages overwrite it
+  }
+
+  // the four lists of each row, ranked against each other
+  uint64_t* lists = (uint64_t*)dyn_lds;   // [kBM][kQ * 16]
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lists[my_row * (kQ * 16) + my_q * 16 + i] = best[i];
+  __syncthreads();
+  uint64_t* out16 = lists + kBM * kQ * 16;   // [kBM][16], after the lists
+  static_assert(kBM * kQ * 16 * 8 + kBM * 16 * 8 <= kLds, "lists and results fit");
+  if (my_q == 0)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out16[my_row * 16 + i] = 0ull;
+  __syncthreads();
+  const uint64_t* rl = lists + my_row * (kQ * 16);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {   // unrolled: best[] stays in registers
+    const uint64_t key = best[i];
+    if (key == 0ull) continue;
+    int rank = 0;
+    for (int j = 0; j < kQ * 16; ++j) rank += rl[j] > key ? 1 : 0;
+    if (rank < 16) out16[my_row * 16 + rank] = key;
+  }
+  __syncthreads();
+  // rows of the block that exist: 16 keys each, 4 threads per row
+  if (m0 + my_row < M) {
+    uint64_t* dst = part + ((int64_t)(m0 + my_row) * nranges + nr) * 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[my_q * 4 + i] = out16[my_row * 16 + my_q * 4 + i];
+  }
+}
+
+// One work-group per row: the 16 best of nranges lists of 16 (each best
+// first, empty slots 0).
+constexpr int kMergeThreads = 256;
+__global__ __launch_bounds__(kMergeThreads) void lmhead_merge_kernel(const uint64_t* __restrict__ part,
+                                                                      int nranges, int k,
+                                                                      int32_t* __restrict__ out_idx,
+                                                                      float* __restrict__ out_val) {
+  __shared__ uint64_t surv[kMaxRanges * 16];
+  __shared__ uint64_t heads[kMaxRanges + 16];
+  __shared__ uint64_t sbound[kMergeThreads / 64];
+  __shared__ uint64_t sb2;
+  __shared__ int nsurv;
+  __shared__ uint64_t res[16];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const uint64_t* p = part + (int64_t)row * nranges * 16;
+  // Two lower bounds on the row's 16th best key: the largest of the lists'
+  // 16th keys (that list holds 16 keys at least as large), and the 16th
+  // largest among the first j keys of every list (j = ceil(16 / nranges):
+  // at least 16 distinct keys of the row).  With many short ranges the
+  // second is the tight one (the 16th best of the ranges' best keys).
+  uint64_t b = 0ull;
+  for (int l = tid; l < nranges; l += kMergeThreads) b = p[l * 16 + 15] > b ? p[l * 16 + 15] : b;
+  b = wave_max_u64(b);
+  if (lane_id() == 0) sbound[tid / 64] = b;
+  const int j = (16 + nranges - 1) / nranges;   // nranges * j <= kMaxRanges + 15
+  const int nh = nranges * j;
+  for (int s = tid; s < nh; s += kMergeThreads) heads[s] = p[(s / j) * 16 + s % j];
+  if (tid == 0) {
+    nsurv = 0;
+    sb2 = 0ull;
+  }
+  if (tid < 16) res[tid] = 0ull;
+  __syncthreads();
+  for (int s = tid; s < nh; s += kMergeThreads) {
+    const uint64_t key = heads[s];
+    int rank = 0;
+    for (int q = 0; q < nh; ++q) rank += heads[q] > key ? 1 : 0;
+    if (key != 0ull && rank == 15) sb2 = key;   // keys are distinct: one writer
+  }
+  __syncthreads();
+  uint64_t bound = sb2;
+#pragma unroll
+  for (int w = 0; w < kMergeThreads / 64; ++w) bound = sbound[w] > bound ? sbound[w] : bound;
+  for (int s = tid; s < nranges * 16; s += kMergeThreads) {
+    const uint64_t key = p[s];
+    if (key != 0ull && key >= bound) surv[atomicAdd(&nsurv, 1)] = key;
+  }
+  __syncthreads();
+  const int ns = nsurv;
+  for (int s = tid; s < ns; s += kMergeThreads) {
+    const uint64_t key = surv[s];
+    int rank = 0;
+    for (int j = 0; j < ns; ++j) rank += surv[j] > key ? 1 : 0;
+    if (rank < 16) res[rank] = key;
+  }
+  __syncthreads();
+  if (tid < k) {
+    const uint64_t key = res[tid];
+    out_idx[(int64_t)row * k + tid] = (int32_t)key_index(key);
+    out_val[(int64_t)row * k + tid] = key_value(key);
+  }
+}
+
+bool g_lds_set = false;
+
+}  // namespace
+
+LmHeadPlan lmhead_plan(int M, int64_t vocab, int d) {
+  (void)d;
+  LmHeadPlan p;
+  p.mblocks = (M + kBM - 1) / kBM;
+  p.nblocks = (int)((vocab + kBN - 1) / kBN);
+  // about one work-group per CU (each holds 96 KB of LDS and 8 waves)
+  int nr = 256 / (p.mblocks > 0 ? p.mblocks : 1);
+  if (nr < 1) nr = 1;
+  if (nr > p.nblocks) nr = p.nblocks;
+  if (nr > kMaxRanges) nr = kMaxRanges;
+  if (nr >= 8) nr = nr / 8 * 8;
+  p.nranges = nr;
+  p.xcd_groups = nr % 8 == 0 ? 1 : 0;
+  p.ws_bytes = align256((size_t)M * (size_t)nr * 16 * sizeof(uint64_t));
+  return p;
+}
+
+hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int M, int d, int k,
+                              int32_t* out_idx, float* out_val, void* ws, const LmHeadPlan& plan,
+                              hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  uint64_t* part = (uint64_t*)ws;
+  if (!g_lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    g_lds_set = true;
+  }
+  {
+    ProfileScope ps("lmhead_topk", stream);
+    DF2_TRY(launch(lmhead_topk_kernel, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
+                   stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
+                   plan.nranges, plan.nblocks, plan.xcd_groups, part));
+  }
+  ProfileScope ps("lmhead_merge", stream);
+  DF2_TRY(launch(lmhead_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), 0, stream, ps, part,
+                 plan.nranges, k, out_idx, out_val));
+  return hipGetLastError();
+}
+
+}  // namespace df2

@@ -9,6 +9,8 @@
  *                          drafter, before/after every attention and MLP
  *                          sublayer)
  *   dflash2_topk           keep the K best candidates of every draft position
+ *   dflash2_lm_head_topk   the same from the drafter's hidden states, with
+ *                          the shared LM head fused in (logits never stored)
  *   dflash2_pair_scores    score every adjacent candidate pair
  *   dflash2_selector_tables  per-token A/B tables, once per weight set
  *   dflash2_pair_scores_tab  the pair scores with A/B read from those tables
@@ -24,6 +26,7 @@
  *   [WC]   "DFlash 2 讓 Qwen3.8-27B 快了兩倍" (wiselychen), section
  *          "DFlash 2 的三個改進" and section "輸出完全一致".
  *   [TEAI] "DFlash2 并行投机解码解读" (teaikeji), sections 二 and 五.
+ *   [163]  "大模型推理，加速王者：DFlash" (m.163.com).
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked "host".  All tensors are
@@ -98,6 +101,27 @@ int dflash2_init(void);
 size_t dflash2_topk_workspace_bytes(int64_t rows, int64_t vocab, int k);
 int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k, int32_t* out_idx,
                  float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Drafter logits through the shared LM head, fused with the top-K, so that
+ * the [rows, vocab] logits are never written.  The drafter reuses the
+ * target's embedding and LM head ([163] "大模型推理，加速王者：DFlash",
+ * paragraph before the three-step pipeline); the selector takes its top-k
+ * candidates from that dense head ([WC] 坑 2-4):
+ *   z[r, v] = sum_k h[r, k] * emb[v, k]   (bf16 products, fp32 sums)
+ *   out_idx / out_val [rows, k]: the k best of each row, as dflash2_topk
+ *   orders them (value descending, equal values by lower token id; NaN
+ *   never selected); out_val holds the fp32 logits.
+ *   h    [rows, d] bf16      final hidden state of each draft position
+ *   emb  [vocab, d] bf16     the LM head rows (emb_dt = DF2_BF16)
+ * Limits: d % 64 == 0, d <= 65536, 1 <= k <= min(16, vocab).  h and emb
+ * 16-byte aligned.  ws: per-token-range best-16 lists, sized by
+ * dflash2_lm_head_topk_workspace_bytes (rows x ranges x 16 x 8 bytes; 4 MB
+ * at 480 rows).  Deterministic: the same inputs give the same bits.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_lm_head_topk_workspace_bytes(int rows, int64_t vocab, int d, int k);
+int dflash2_lm_head_topk(const void* h, const void* emb, int emb_dt, int64_t vocab, int rows, int d, int k,
+                         int32_t* out_idx, float* out_val, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Pair scores.  [KDP] "A lightweight path selector", equation

@@ -56,6 +56,24 @@ def test_topk_validation():
     assert L.dflash2_topk(None, 1, 0, 1000, 16, None, None, None, 0, None) == df2.DF2_OK
 
 
+def test_lm_head_topk_validation():
+    L = df2.lib()
+    need = df2.dflash2_lm_head_topk_workspace_bytes(480, 151936, 5120, 16)
+    assert need >= 480 * 16 * 8
+    f = L.dflash2_lm_head_topk
+    a = lambda **kw: [kw.get("h", FAKE), FAKE, kw.get("dt", 1), kw.get("V", 151936), kw.get("rows", 480),
+                      kw.get("d", 5120), kw.get("k", 16), FAKE, FAKE, FAKE, kw.get("ws", need), None]
+    assert f(*a(dt=2)) == df2.DF2_ERR_DTYPE
+    assert f(*a(d=100)) == df2.DF2_ERR_SHAPE
+    assert f(*a(k=17)) == df2.DF2_ERR_SHAPE
+    assert f(*a(k=0)) == df2.DF2_ERR_SHAPE
+    assert f(*a(V=8)) == df2.DF2_ERR_SHAPE          # k > vocab
+    assert f(*a(h=None)) == df2.DF2_ERR_NULL
+    assert f(*a(h=C.c_void_p(0x100008))) == df2.DF2_ERR_SHAPE
+    assert f(*a(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+    assert f(None, None, 1, 151936, 0, 5120, 16, None, None, None, 0, None) == df2.DF2_OK
+
+
 def test_pair_scores_validation():
     L = df2.lib()
     args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, FAKE, kw.get("edt", 1), 151936, FAKE, FAKE,

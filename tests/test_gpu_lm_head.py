@@ -1,0 +1,125 @@
+"""GPU parity of dflash2_lm_head_topk (drafter logits through the shared LM
+head, fused with the top-K) against the oracle (oracle.lm_head_topk: float64
+logits, then the K best by value desc, index asc).
+
+The GPU sums bf16 products in fp32, the oracle in float64, so the two can
+order a pair of tokens differently only when their logits are closer than
+the fp32 rounding error.  Rule (for every row and rank i):
+  * value: |val_g[i] - z64[idx_g[i]]| <= eps[idx_g[i]], with
+    eps[v] = 8 sqrt(d) u sum_k |h_k E_vk| (u = 2^-24): the probabilistic
+    bound of an fp32 sum of d terms (Higham and Mary, "A new approach to
+    probabilistic rounding error analysis", 2019; lambda = 8, failure
+    probability below 1e-13 per logit);
+  * index: idx_g[i] == idx_o[i], or the two tokens' float64 logits differ by
+    at most eps_g + eps_o (the i-th largest of two sequences within eps of
+    each other are within eps of each other); such near-ties are counted and
+    must stay rare.
+Small-integer inputs make every logit exact in fp32 and float64: there the
+result must be bit-identical, ties (frequent) included."""
+import numpy as np
+import pytest
+import torch
+
+import draft_selection_bf16_amd as df2
+import oracle
+import synth
+from gpu_util import DEV, report, ws
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+U32 = 2.0 ** -24
+
+
+def _gpu(h, E, k):
+    rows, d = h.shape
+    idx = torch.empty((rows, k), dtype=torch.int32, device=DEV)
+    val = torch.empty((rows, k), dtype=torch.float32, device=DEV)
+    w = ws(df2.dflash2_lm_head_topk_workspace_bytes(rows, E.shape[0], d, k))
+    df2.dflash2_lm_head_topk(h.to(DEV), E.to(DEV), k, idx, val, w)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), val.cpu().numpy()
+
+
+def _check(h, E, k, rows, gi, gv, label):
+    """Compare GPU rows `rows` (gi, gv: all rows) with the oracle on those rows."""
+    hs = h[torch.as_tensor(rows)]
+    oi, ov = oracle.lm_head_topk(hs, E, k)
+    d = h.shape[1]
+    hf = hs.float().numpy().astype(np.float64)
+    near, n = 0, 0
+    for j, r in enumerate(rows):
+        toks = np.union1d(gi[r], oi[j])
+        Et = E[torch.from_numpy(toks.astype(np.int64))].float().numpy().astype(np.float64)
+        z = dict(zip(toks.tolist(), (Et @ hf[j]).tolist()))
+        eps = dict(zip(toks.tolist(), (8 * np.sqrt(d) * U32 * (np.abs(Et) @ np.abs(hf[j]))).tolist()))
+        for i in range(k):
+            g, o = int(gi[r, i]), int(oi[j, i])
+            assert abs(float(gv[r, i]) - z[g]) <= eps[g], (label, r, i, float(gv[r, i]), z[g], eps[g])
+            n += 1
+            if g != o:
+                assert abs(z[g] - z[o]) <= eps[g] + eps[o], (label, r, i, g, o, z[g], z[o])
+                near += 1
+        assert np.isclose(ov[j, 0], z[int(oi[j, 0])])
+    assert near <= max(2, n // 50), (label, near, n)
+    report(f"lm_head_topk {label}", rows=len(rows), near_tie_swaps=near)
+
+
+def _inputs(rows, V, d, seed, scale_h=1.0):
+    g = torch.Generator().manual_seed(seed)
+    h = (scale_h * torch.randn(rows, d, generator=g)).to(torch.bfloat16)
+    E = (0.02 * torch.randn(V, d, generator=g)).to(torch.bfloat16)
+    return h, E
+
+
+@pytest.mark.parametrize("rows,V,d,k", [(133, 5003, 640, 16), (1, 131, 64, 16), (7, 20011, 256, 16),
+                                        (300, 2500, 128, 5), (64, 17, 192, 16), (260, 1000, 64, 1)])
+def test_lm_head_topk_small_shapes(rows, V, d, k):
+    """Ragged row blocks (133 = 128 + 5, 260), a ragged last token block,
+    fewer tokens than one block (17, 131), k < 16, d from 64 to 640; every
+    row checked."""
+    print(f"[case] lm_head_topk rows={rows} V={V} d={d} k={k}", flush=True)
+    h, E = _inputs(rows, V, d, rows + V)
+    gi, gv = _gpu(h, E, k)
+    _check(h, E, k, list(range(rows)), gi, gv, f"{rows}x{V}x{d}")
+
+
+def test_lm_head_topk_integer_inputs_bit_exact():
+    """Entries in {-3..3}: every logit is an integer, exact in fp32 and in
+    float64, with many ties; indices and values must be identical, ties
+    going to the lower token id."""
+    rng = np.random.default_rng(5)
+    rows, V, d = 150, 3001, 256
+    h = torch.from_numpy(rng.integers(-3, 4, size=(rows, d)).astype(np.float32)).to(torch.bfloat16)
+    E = torch.from_numpy(rng.integers(-3, 4, size=(V, d)).astype(np.float32)).to(torch.bfloat16)
+    gi, gv = _gpu(h, E, 16)
+    oi, ov = oracle.lm_head_topk(h, E, 16)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.astype(np.float64), ov)
+
+
+def test_lm_head_topk_b32_blk16_launch_shape():
+    """480 rows (32 requests x 15 draft positions), vocabulary 151,936,
+    hidden 5120: the launch configuration the benchmark times.  The oracle
+    recomputes sampled rows one by one: the first and last of each 128-row
+    block and two more."""
+    w = synth.WORKLOADS["b32_blk16_v151936_conv"]
+    rows, V, d = w.B * w.T, w.V, w.d
+    print(f"[case] lm_head_topk rows={rows} V={V} d={d}", flush=True)
+    E = synth.embeddings(w, device=DEV)
+    h = synth.context_hidden(w, device=DEV).reshape(rows, d)
+    gi, gv = _gpu(h, E, 16)
+    assert np.all(np.diff(gv, axis=1) <= 0)
+    sample = [0, 127, 128, 255, 256, 383, 384, 479, 77, 301]
+    _check(h.cpu(), E.cpu(), 16, sample, gi, gv, "480x151936x5120")
+
+
+def test_lm_head_topk_b1_blk8_launch_shape():
+    """7 rows (one request, block 8), vocabulary 151,936: a skinny product
+    that streams the whole LM head; every row checked."""
+    w = synth.WORKLOADS["b1_blk8_v151936"]
+    rows, V, d = w.T, w.V, w.d
+    E = synth.embeddings(w, device=DEV)
+    h = synth.context_hidden(w, device=DEV).reshape(rows, d)
+    gi, gv = _gpu(h, E, 16)
+    _check(h.cpu(), E.cpu(), 16, list(range(rows)), gi, gv, "7x151936x5120")
