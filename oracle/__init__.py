@@ -7,7 +7,8 @@ raw 16-bit patterns.  Every function returns fresh numpy outputs.
 
 Parity status per function (details in the C source):
   topk, project, pair_scores, path, verify_greedy, verify_reject, dynconv2,
-  lm_head_topk, philox -- all pinned by the CPU tests in tests/test_oracle_*.py;
+  lm_head_topk, verify_greedy_head, philox -- all pinned by the CPU tests in
+  tests/test_oracle_*.py;
   selector_tables, pair_scores_tab (numpy, below) -- pinned by
   tests/test_oracle_tables.py.
 """
@@ -59,9 +60,10 @@ def _declare(L):
                                        F64, U64, P, P, P, P, P, P]
     L.oracle_dynconv2.argtypes = [P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P]
     L.oracle_lm_head_topk.argtypes = [P, P, I64, I64, C.c_int, C.c_int, P, P]
+    L.oracle_verify_greedy_head.argtypes = [P, P, I64, C.c_int, P, C.c_int, C.c_int, P, P, P, P]
     for f in ("oracle_topk", "oracle_project", "oracle_pair_scores", "oracle_path",
               "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2",
-              "oracle_lm_head_topk"):
+              "oracle_lm_head_topk", "oracle_verify_greedy_head"):
         getattr(L, f).restype = C.c_int
 
 
@@ -276,6 +278,27 @@ def verify_greedy(target, path_tok):
     _check(lib().oracle_verify_greedy(_ptr(za), zdt, V, _ptr(pt), B, T, _ptr(acc), _ptr(out),
                                       _ptr(am)), "oracle_verify_greedy")
     return dict(accept_len=acc, out_tok=out, argmax=am)
+
+
+def verify_greedy_head(h, emb, path_tok):
+    """Greedy verification with the target logits computed from its final
+    hidden states h [B, T+1, d] (bf16) through its LM head emb [V, d] (bf16),
+    in float64.  -> dict(accept_len, out_tok, argmax, margin) (margin: the
+    argmax logit minus the runner-up, per row)."""
+    ha, hdt = host(h)
+    ea, edt = host(emb)
+    assert hdt == BF16 and edt == BF16
+    pt = np.ascontiguousarray(np.asarray(host(path_tok)[0], dtype=np.int32))
+    B, T = pt.shape
+    V, d = ea.shape
+    assert ha.shape == (B, T + 1, d)
+    acc = np.zeros((B,), np.int32)
+    out = np.zeros((B, T + 1), np.int32)
+    am = np.zeros((B, T + 1), np.int32)
+    mg = np.zeros((B, T + 1), np.float64)
+    _check(lib().oracle_verify_greedy_head(_ptr(ha), _ptr(ea), V, d, _ptr(pt), B, T, _ptr(acc), _ptr(out),
+                                           _ptr(am), _ptr(mg)), "oracle_verify_greedy_head")
+    return dict(accept_len=acc, out_tok=out, argmax=am, margin=mg)
 
 
 def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, seed: int,

@@ -559,6 +559,65 @@ int oracle_verify_greedy(const void* target, int dt, int64_t vocab, const int32_
 }
 
 /* ------------------------------------------------------------------ */
+/* Greedy verification straight from the target's hidden states through  */
+/* its LM head: [WC] "輸出完全一致" / [TEAI] 五 (under greedy decoding the  */
+/* output is the target's own argmax chain), with the target logits      */
+/*   Z[b][t][v] = sum_k h[b][t][k] * E[v][k]   (double; h, E bf16)         */
+/* computed here instead of read.  y_t = the lowest v maximising Z[b][t]  */
+/* for t = 0..T, then the longest-prefix rule of oracle_verify_greedy.    */
+/* margin[b][t] (nullable): Z of the argmax minus the runner-up.          */
+/* Pinned by: agreement with oracle_verify_greedy on integer inputs (the */
+/* logits are exact in float); one-hot LM-head rows (the argmax is known */
+/* by inspection); the output equals the argmax chain.                    */
+/* ------------------------------------------------------------------ */
+
+int oracle_verify_greedy_head(const uint16_t* h, const uint16_t* emb, int64_t vocab, int d,
+                              const int32_t* path_tok, int B, int T, int32_t* accept_len,
+                              int32_t* out_tok, int32_t* argmax_out, double* margin) {
+  if (vocab < 1 || d < 1) return 3;
+  const int64_t rows = (int64_t)B * (T + 1);
+  int32_t* y = (int32_t*)malloc(sizeof(int32_t) * (size_t)rows);
+  double* hr = (double*)malloc(sizeof(double) * (size_t)d);
+  double* z = (double*)malloc(sizeof(double) * (size_t)vocab);
+  if (!y || !hr || !z) {
+    free(y); free(hr); free(z);
+    return 1;
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int q = 0; q < d; ++q) hr[q] = (double)bf16_value(h[r * d + q]);
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < vocab; ++v) {
+      double acc = 0.0;
+      for (int q = 0; q < d; ++q) acc += hr[q] * (double)bf16_value(emb[v * d + q]);
+      z[v] = acc;
+    }
+    int64_t arg = 0;
+    for (int64_t v = 1; v < vocab; ++v)
+      if (z[v] > z[arg]) arg = v;
+    double second = -INFINITY;
+    for (int64_t v = 0; v < vocab; ++v)
+      if (v != arg && z[v] > second) second = z[v];
+    y[r] = (int32_t)arg;
+    if (argmax_out) argmax_out[r] = (int32_t)arg;
+    if (margin) margin[r] = z[arg] - second;
+  }
+  for (int b = 0; b < B; ++b) {
+    const int32_t* yb = y + (int64_t)b * (T + 1);
+    int n = 0;
+    while (n < T && path_tok[(int64_t)b * T + n] == yb[n]) ++n;
+    accept_len[b] = n;
+    for (int t = 0; t <= T; ++t) {
+      int32_t v = -1;
+      if (t < n) v = path_tok[(int64_t)b * T + t];
+      else if (t == n) v = yb[n];
+      out_tok[(int64_t)b * (T + 1) + t] = v;
+    }
+  }
+  free(y); free(hr); free(z);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* Speculative rejection sampling.  [KDP] "A lightweight path selector": */
 /* rejection sampling restores the exact target distribution; [WC]       */
 /* "輸出完全一致"; [AREX].  With p_t = softmax(Z_t / tau):                */

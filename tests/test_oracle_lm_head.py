@@ -81,3 +81,48 @@ def test_integer_logits_agree_with_topk():
     ti, tv = oracle.topk(z, 16)
     assert np.array_equal(idx, ti)
     assert np.array_equal(val, tv.astype(np.float64))
+
+
+# ------------------------------------------------ greedy verification from the head
+def test_verify_greedy_head_equals_verify_greedy_on_exact_logits():
+    """Integer inputs: the target logits are exact, so verifying from the
+    hidden states equals oracle.verify_greedy on the logits themselves
+    (argmax ties, frequent here, to the lower id)."""
+    rng = np.random.default_rng(6)
+    B, T, V, d = 6, 5, 400, 24
+    h = rng.integers(-3, 4, size=(B, T + 1, d)).astype(np.float32)
+    E = rng.integers(-3, 4, size=(V, d)).astype(np.float32)
+    Z = (h.astype(np.int64) @ E.astype(np.int64).T).astype(np.float32)
+    y = np.argmax(Z, -1)
+    path = y[:, :T].copy().astype(np.int32)
+    path[1, 2] = (path[1, 2] + 1) % V
+    path[3, 0] = (path[3, 0] + 7) % V
+    o = oracle.verify_greedy_head(_bf16(h), _bf16(E), path)
+    g = oracle.verify_greedy(Z, path)
+    assert np.array_equal(o["argmax"], g["argmax"])
+    assert np.array_equal(o["accept_len"], g["accept_len"])
+    assert np.array_equal(o["out_tok"], g["out_tok"])
+    assert o["accept_len"].tolist() == [T, 2, T, 0, T, T]
+
+
+def test_verify_greedy_head_one_hot_head():
+    """E_v = e_{v mod d} scaled by 1 + v / V: the logit of v is h[v mod d]
+    (1 + v / V), so each row's argmax is known by inspection; the emitted
+    tokens are that argmax chain."""
+    B, T, d = 2, 3, 32
+    V = 4 * d
+    E = np.zeros((V, d), np.float32)
+    scale = 1 + np.round(np.arange(V) / V * 64) / 64     # exact in bf16
+    E[np.arange(V), np.arange(V) % d] = scale
+    rng = np.random.default_rng(7)
+    h = np.round(rng.normal(size=(B, T + 1, d)) * 16) / 16
+    want = np.zeros((B, T + 1), np.int64)
+    for b in range(B):
+        for t in range(T + 1):
+            z = h[b, t, np.arange(V) % d] * scale
+            want[b, t] = min(range(V), key=lambda v: (-z[v], v))
+    path = want[:, :T].astype(np.int32)
+    o = oracle.verify_greedy_head(_bf16(h), _bf16(E), path)
+    assert np.array_equal(o["argmax"], want)
+    assert o["accept_len"].tolist() == [T, T]
+    assert np.array_equal(o["out_tok"], want)
