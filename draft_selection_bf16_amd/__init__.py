@@ -35,6 +35,7 @@ EXPORTS = [
     "dflash2_dynconv2_workspace_bytes", "dflash2_dynconv2",
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_noalloc_max_bytes",
+    "dflash2_verify_greedy_head_workspace_bytes", "dflash2_verify_greedy_head",
     "dflash2_philox4x64", "dflash2_profile_start", "dflash2_profile_stop",
 ]
 
@@ -85,6 +86,9 @@ def lib():
         L.dflash2_verify_greedy.argtypes = [P, I, I64, P, I, I, P, P, P, SZ, P]
         L.dflash2_verify_reject.argtypes = [P, I, I64, P, P, P, P, I, I, I, F, P, I, P, P, P, SZ, P]
         L.dflash2_verify_greedy_noalloc.argtypes = [P, I, I64, P, I, I, P, P, P]
+        L.dflash2_verify_greedy_head_workspace_bytes.argtypes = [I, I, I64, I]
+        L.dflash2_verify_greedy_head_workspace_bytes.restype = SZ
+        L.dflash2_verify_greedy_head.argtypes = [P, P, I, I64, I, P, I, I, P, P, P, SZ, P]
         L.dflash2_verify_greedy_noalloc_max_bytes.restype = SZ
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
         L.dflash2_profile_start.argtypes = [C.c_char_p, I]
@@ -95,7 +99,7 @@ def lib():
                      "dflash2_pair_scores_tab", "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
                      "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
-                     "dflash2_verify_greedy_noalloc",
+                     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_head",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
         _lib = L
@@ -250,6 +254,20 @@ def dflash2_verify_greedy(target, path_tok, accept_len, out_tok, ws, stream=None
     _check(lib().dflash2_verify_greedy(_ptr(target), _dt(target), V, _ptr(path_tok), B, T1 - 1,
                                        _ptr(accept_len), _ptr(out_tok), _ptr(ws), _bytes(ws),
                                        _stream(stream)), "dflash2_verify_greedy")
+
+
+def dflash2_verify_greedy_head_workspace_bytes(B: int, T: int, vocab: int, d: int) -> int:
+    return int(lib().dflash2_verify_greedy_head_workspace_bytes(B, T, vocab, d))
+
+
+def dflash2_verify_greedy_head(h, emb, path_tok, accept_len, out_tok, ws, stream=None):
+    """Greedy verification with the target logits computed from its hidden
+    states h [B, T+1, d] through its LM head emb [V, d] (both bf16)."""
+    B, T1, d = h.shape
+    V = emb.shape[0]
+    _check(lib().dflash2_verify_greedy_head(_ptr(h), _ptr(emb), _dt(emb), V, d, _ptr(path_tok), B, T1 - 1,
+                                            _ptr(accept_len), _ptr(out_tok), _ptr(ws), _bytes(ws),
+                                            _stream(stream)), "dflash2_verify_greedy_head")
 
 
 def dflash2_verify_greedy_noalloc_max_bytes() -> int:

@@ -151,7 +151,7 @@ int dflash2_topk(const void* logits, int dt, int64_t rows, int64_t vocab, int k,
 size_t dflash2_lm_head_topk_workspace_bytes(int rows, int64_t vocab, int d, int k) {
   if (rows <= 0 || vocab <= 0 || d <= 0) return 0;
   (void)k;
-  return lmhead_plan(rows, vocab, d).ws_bytes;
+  return lmhead_plan(rows, vocab, d, 16).ws_bytes;
 }
 
 int dflash2_lm_head_topk(const void* h, const void* emb, int emb_dt, int64_t vocab, int rows, int d, int k,
@@ -165,11 +165,39 @@ int dflash2_lm_head_topk(const void* h, const void* emb, int emb_dt, int64_t voc
   if (rows == 0) return DF2_OK;
   REQUIRE(h && emb && out_idx && out_val, DF2_ERR_NULL, "dflash2_lm_head_topk: null pointer argument");
   REQUIRE(aligned16(h) && aligned16(emb), DF2_ERR_SHAPE, "dflash2_lm_head_topk: h/emb must be 16-byte aligned");
-  LmHeadPlan plan = lmhead_plan(rows, vocab, d);
+  LmHeadPlan plan = lmhead_plan(rows, vocab, d, 16);
   REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE, "dflash2_lm_head_topk: workspace %zu < %zu bytes",
           ws_bytes, plan.ws_bytes);
   return hip_status(launch_lmhead_topk(h, emb, vocab, rows, d, k, out_idx, out_val, ws, plan, stream),
                     "dflash2_lm_head_topk");
+}
+
+// ------------------------------------------------------------------ greedy verify from the head
+size_t dflash2_verify_greedy_head_workspace_bytes(int B, int T, int64_t vocab, int d) {
+  if (B <= 0 || T <= 0 || vocab <= 0 || d <= 0) return 0;
+  return lmhead_plan(B * (T + 1), vocab, d, 1).ws_bytes;
+}
+
+int dflash2_verify_greedy_head(const void* h, const void* emb, int emb_dt, int64_t vocab, int d,
+                               const int32_t* path_tok, int B, int T, int32_t* accept_len, int32_t* out_tok,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_verify_greedy_head: the LM head must be BF16");
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_verify_greedy_head: vocab %lld",
+          (long long)vocab);
+  REQUIRE(d >= 64 && d % 64 == 0 && d <= 65536, DF2_ERR_SHAPE,
+          "dflash2_verify_greedy_head: d %d is not a multiple of 64 in [64, 65536]", d);
+  REQUIRE(B >= 0 && B <= kMaxB / 64, DF2_ERR_SHAPE, "dflash2_verify_greedy_head: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_greedy_head: T %d not in [1, %d]", T, kMaxT);
+  if (B == 0) return DF2_OK;
+  REQUIRE(h && emb && path_tok && accept_len && out_tok, DF2_ERR_NULL,
+          "dflash2_verify_greedy_head: null pointer argument");
+  REQUIRE(aligned16(h) && aligned16(emb), DF2_ERR_SHAPE, "dflash2_verify_greedy_head: h/emb must be 16-byte aligned");
+  LmHeadPlan plan = lmhead_plan(B * (T + 1), vocab, d, 1);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE,
+          "dflash2_verify_greedy_head: workspace %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  return hip_status(launch_verify_greedy_head(h, emb, vocab, d, path_tok, B, T, accept_len, out_tok, ws, plan,
+                                              stream),
+                    "dflash2_verify_greedy_head");
 }
 
 // ------------------------------------------------------------------ pair scores

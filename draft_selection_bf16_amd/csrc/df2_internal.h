@@ -152,12 +152,18 @@ struct LmHeadPlan {
   int nblocks;      // 128-token blocks of the vocabulary
   int nranges;      // token ranges (work-groups per row block)
   int xcd_groups;   // nranges % 8 == 0: a range's row blocks run on one XCD
-  size_t ws_bytes;  // per-range best-16 keys [M, nranges, 16]
+  size_t ws_bytes;  // per-range best keys [M, nranges, keep]
 };
-LmHeadPlan lmhead_plan(int M, int64_t vocab, int d);
+// keep = 16 (the drafter's top-16) or 1 (the target's argmax)
+LmHeadPlan lmhead_plan(int M, int64_t vocab, int d, int keep);
 hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int M, int d, int k,
                               int32_t* out_idx, float* out_val, void* ws, const LmHeadPlan& plan,
                               hipStream_t stream);
+// greedy verification with the target logits computed from h [B, T+1, d]
+// through the LM head (plan for M = B * (T + 1) rows, keep 1)
+hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t vocab, int d,
+                                    const int32_t* path_tok, int B, int T, int32_t* accept_len,
+                                    int32_t* out_tok, void* ws, const LmHeadPlan& plan, hipStream_t stream);
 
 // ---- Philox words -----------------------------------------------------------
 hipError_t launch_philox(const uint64_t* seed_dev, const int32_t* b, const int32_t* t, int n,

@@ -73,7 +73,9 @@ __device__ __forceinline__ void insert16(uint64_t (&l)[16], uint64_t x) {
 }
 
 // grid: mblocks * nranges work-groups of kThreads; dynamic LDS kLds.
-// part[(row * nranges + range) * 16 + i]: the i-th best key of the range.
+// part[(row * nranges + range) * KEEP + i]: the i-th best key of the range
+// (KEEP = 16: the drafter's top-16; KEEP = 1: the target's argmax).
+template <int KEEP>
 __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     const uint16_t* __restrict__ h, int M, const uint16_t* __restrict__ emb, int64_t vocab, int K,
     int mblocks, int nranges, int nblocks, int xcd_groups, uint64_t* __restrict__ part) {
@@ -119,11 +121,13 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) bo[j][s2] = kBM * 128 + r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
   }
-  // the running best-16 of this thread: row tid / 4, columns tid % 4 + 4 j
+  // the running best KEEP keys of this thread: row tid / 4, columns
+  // tid % 4 + 4 j
+  static_assert(KEEP == 16 || KEEP == 1, "best-16 lists or the argmax");
   const int my_row = threadIdx.x / kQ, my_q = threadIdx.x % kQ;
-  uint64_t best[16];
+  uint64_t best[KEEP];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) best[i] = 0ull;
+  for (int i = 0; i < KEEP; ++i) best[i] = 0ull;
   float* tile = (float*)dyn_lds;
 
   for (int nb = nb0; nb < nb1; ++nb) {
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     // its busiest lane needs, not once per value).
     const float* trow = tile + my_row * kOld;
     const int ncols = wrows;   // columns past the vocabulary are not tokens
-    uint64_t thr = best[15];
+    uint64_t thr = best[KEEP - 1];
     {
       const uint64_t o1 = shfl_xor_u64(thr, 1);
       thr = o1 > thr ? o1 : thr;
@@ -214,15 +218,29 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
       mask &= mask - 1u;
       const int c = my_q + kQ * j;
       const uint64_t key = make_key(trow[c], (uint32_t)(n0 + c));
-      if (key > thr && key > best[15]) insert16(best, key);
+      if constexpr (KEEP == 16) {
+        if (key > thr && key > best[15]) insert16(best, key);
+      } else {
+        best[0] = key > best[0] ? key : best[0];
+      }
     }
     __syncthreads();   // the tile is read before the next block's stages overwrite it
   }
 
+  if constexpr (KEEP == 1) {
+    // the row's argmax key of the range: the largest of its four threads'
+    uint64_t m = best[0];
+    const uint64_t o1 = shfl_xor_u64(m, 1);
+    m = o1 > m ? o1 : m;
+    const uint64_t o2 = shfl_xor_u64(m, 2);
+    m = o2 > m ? o2 : m;
+    if (my_q == 0 && m0 + my_row < M) part[(int64_t)(m0 + my_row) * nranges + nr] = m;
+    return;
+  }
   // the four lists of each row, ranked against each other
   uint64_t* lists = (uint64_t*)dyn_lds;   // [kBM][kQ * 16]
 #pragma unroll
-  for (int i = 0; i < 16; ++i) lists[my_row * (kQ * 16) + my_q * 16 + i] = best[i];
+  for (int i = 0; i < KEEP; ++i) lists[my_row * (kQ * 16) + my_q * 16 + i] = best[i];
   __syncthreads();
   uint64_t* out16 = lists + kBM * kQ * 16;   // [kBM][16], after the lists
   static_assert(kBM * kQ * 16 * 8 + kBM * 16 * 8 <= kLds, "lists and results fit");
@@ -232,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
   __syncthreads();
   const uint64_t* rl = lists + my_row * (kQ * 16);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {   // unrolled: best[] stays in registers
+  for (int i = 0; i < KEEP; ++i) {   // unrolled: best[] stays in registers
     const uint64_t key = best[i];
     if (key == 0ull) continue;
     int rank = 0;
@@ -311,11 +329,34 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_merge_kernel(const uint6
   }
 }
 
+// Greedy verification from the argmax keys: one wave per request, lane t
+// (t <= T) takes row (b, t)'s argmax over the token ranges; n = the longest
+// prefix on which the drafted tokens equal the argmax; emitted: the n
+// accepted drafts, then the argmax at n, then -1.
+__global__ __launch_bounds__(64) void greedy_head_final_kernel(const uint64_t* __restrict__ part, int nranges,
+                                                               const int32_t* __restrict__ path_tok, int T,
+                                                               int32_t* __restrict__ accept_len,
+                                                               int32_t* __restrict__ out_tok) {
+  const int b = blockIdx.x, lane = lane_id();
+  uint64_t m = 0ull;
+  if (lane <= T) {
+    const uint64_t* p = part + ((int64_t)b * (T + 1) + lane) * nranges;
+    for (int r = 0; r < nranges; ++r) m = p[r] > m ? p[r] : m;
+  }
+  const int32_t y = (int32_t)key_index(m);
+  const int32_t x = lane < T ? path_tok[(int64_t)b * T + lane] : -1;
+  const uint64_t miss = ballot(lane < T && x != y);
+  const int n = miss ? __ffsll((unsigned long long)miss) - 1 : T;
+  if (lane == 0) accept_len[b] = n;
+  if (lane <= T) out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? x : (lane == n ? y : -1);
+}
+
 bool g_lds_set = false;
+bool g_lds_set1 = false;
 
 }  // namespace
 
-LmHeadPlan lmhead_plan(int M, int64_t vocab, int d) {
+LmHeadPlan lmhead_plan(int M, int64_t vocab, int d, int keep) {
   (void)d;
   LmHeadPlan p;
   p.mblocks = (M + kBM - 1) / kBM;
@@ -328,7 +369,7 @@ LmHeadPlan lmhead_plan(int M, int64_t vocab, int d) {
   if (nr >= 8) nr = nr / 8 * 8;
   p.nranges = nr;
   p.xcd_groups = nr % 8 == 0 ? 1 : 0;
-  p.ws_bytes = align256((size_t)M * (size_t)nr * 16 * sizeof(uint64_t));
+  p.ws_bytes = align256((size_t)M * (size_t)nr * (size_t)keep * sizeof(uint64_t));
   return p;
 }
 
@@ -338,20 +379,44 @@ hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int
   if (M == 0) return hipSuccess;
   uint64_t* part = (uint64_t*)ws;
   if (!g_lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<16>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
     g_lds_set = true;
   }
   {
     ProfileScope ps("lmhead_topk", stream);
-    DF2_TRY(launch(lmhead_topk_kernel, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
+    DF2_TRY(launch(lmhead_topk_kernel<16>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
                    stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
                    plan.nranges, plan.nblocks, plan.xcd_groups, part));
   }
   ProfileScope ps("lmhead_merge", stream);
   DF2_TRY(launch(lmhead_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), 0, stream, ps, part,
                  plan.nranges, k, out_idx, out_val));
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t vocab, int d,
+                                    const int32_t* path_tok, int B, int T, int32_t* accept_len,
+                                    int32_t* out_tok, void* ws, const LmHeadPlan& plan, hipStream_t stream) {
+  if (B == 0) return hipSuccess;
+  const int M = B * (T + 1);
+  uint64_t* part = (uint64_t*)ws;
+  if (!g_lds_set1) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<1>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    g_lds_set1 = true;
+  }
+  {
+    ProfileScope ps("head_argmax", stream);
+    DF2_TRY(launch(lmhead_topk_kernel<1>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
+                   stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
+                   plan.nranges, plan.nblocks, plan.xcd_groups, part));
+  }
+  ProfileScope ps("greedy_head_final", stream);
+  DF2_TRY(launch(greedy_head_final_kernel, dim3((unsigned)B), dim3(64), 0, stream, ps, part, plan.nranges, path_tok,
+                 T, accept_len, out_tok));
   return hipGetLastError();
 }
 

@@ -18,6 +18,8 @@
  *                            dflash2_pair_scores_tab_from_h)
  *   dflash2_path_viterbi   pick one path through the K x K lattices
  *   dflash2_verify_greedy  accept the longest prefix the target agrees with
+ *   dflash2_verify_greedy_head  the same from the target's hidden states,
+ *                          with its LM head fused in (logits never stored)
  *   dflash2_verify_reject  speculative rejection sampling with a residual draw
  *
  * Sources (the pages that define the operations; cited by title/section):
@@ -278,6 +280,28 @@ int dflash2_verify_greedy(const void* target_logits, int dt, int64_t vocab, cons
 size_t dflash2_verify_greedy_noalloc_max_bytes(void);
 int dflash2_verify_greedy_noalloc(const void* target_logits, int dt, int64_t vocab, const int32_t* path_tok,
                                   int B, int T, int32_t* accept_len, int32_t* out_tok, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy verification with the target's LM head fused in: the target
+ * logits are computed from the target's final hidden states and argmaxed
+ * on the fly, never stored ([WC] "輸出完全一致", [TEAI] 五: under greedy
+ * decoding the output is the target's own token-by-token argmax chain):
+ *   Z[b, t, v] = sum_k h[b, t, k] * emb[v, k]  (bf16 products, fp32 sums)
+ *   y_t = argmax_v Z[b, t, v] (lowest id on ties), then the rule of
+ *   dflash2_verify_greedy: n = longest prefix with path_tok == y,
+ *   out_tok = (path_tok[0..n-1], y_n, -1 ...).
+ *   h    [B, T+1, d] bf16  the target's final hidden state at each
+ *                          verified position (row T gives the bonus token)
+ *   emb  [vocab, d] bf16   the target's LM head rows (emb_dt = DF2_BF16)
+ *   path_tok [B, T]; accept_len [B]; out_tok [B, T+1] as in
+ *   dflash2_verify_greedy.
+ * Limits: d % 64 == 0, d <= 65536, 1 <= T <= 63, B * (T + 1) rows.
+ * ws: per-token-range argmax keys, dflash2_verify_greedy_head_workspace_bytes.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_verify_greedy_head_workspace_bytes(int B, int T, int64_t vocab, int d);
+int dflash2_verify_greedy_head(const void* h, const void* emb, int emb_dt, int64_t vocab, int d,
+                               const int32_t* path_tok, int B, int T, int32_t* accept_len, int32_t* out_tok,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Speculative rejection sampling.  [KDP] "A lightweight path selector":

@@ -74,6 +74,21 @@ def test_lm_head_topk_validation():
     assert f(None, None, 1, 151936, 0, 5120, 16, None, None, None, 0, None) == df2.DF2_OK
 
 
+def test_verify_greedy_head_validation():
+    L = df2.lib()
+    need = df2.dflash2_verify_greedy_head_workspace_bytes(32, 15, 151936, 5120)
+    assert need >= 32 * 16 * 8
+    f = L.dflash2_verify_greedy_head
+    a = lambda **kw: [kw.get("h", FAKE), FAKE, kw.get("dt", 1), 151936, kw.get("d", 5120), FAKE, kw.get("B", 32),
+                      kw.get("T", 15), FAKE, FAKE, FAKE, kw.get("ws", need), None]
+    assert f(*a(dt=0)) == df2.DF2_ERR_DTYPE
+    assert f(*a(d=96)) == df2.DF2_ERR_SHAPE
+    assert f(*a(T=64)) == df2.DF2_ERR_SHAPE
+    assert f(*a(h=None)) == df2.DF2_ERR_NULL
+    assert f(*a(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+    assert f(None, None, 1, 151936, 5120, None, 0, 15, None, None, None, 0, None) == df2.DF2_OK
+
+
 def test_pair_scores_validation():
     L = df2.lib()
     args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, FAKE, kw.get("edt", 1), 151936, FAKE, FAKE,

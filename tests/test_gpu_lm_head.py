@@ -15,7 +15,12 @@ the fp32 rounding error.  Rule (for every row and rank i):
     each other are within eps of each other); such near-ties are counted and
     must stay rare.
 Small-integer inputs make every logit exact in fp32 and float64: there the
-result must be bit-identical, ties (frequent) included."""
+result must be bit-identical, ties (frequent) included.
+
+dflash2_verify_greedy_head (greedy verification with the target's LM head
+fused in) is compared with oracle.verify_greedy_head the same way: accepted
+lengths and emitted tokens exact, except for a request whose deciding
+argmax had a top-2 gap within twice the fp32 bound."""
 import numpy as np
 import pytest
 import torch
@@ -123,3 +128,107 @@ def test_lm_head_topk_b1_blk8_launch_shape():
     h = synth.context_hidden(w, device=DEV).reshape(rows, d)
     gi, gv = _gpu(h, E, 16)
     _check(h.cpu(), E.cpu(), 16, list(range(rows)), gi, gv, "7x151936x5120")
+
+
+# ------------------------------------------------ greedy verification from the head
+def _verify_head_gpu(h, E, path):
+    B, T1, d = h.shape
+    acc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, T1), dtype=torch.int32, device=DEV)
+    w = ws(df2.dflash2_verify_greedy_head_workspace_bytes(B, T1 - 1, E.shape[0], d))
+    df2.dflash2_verify_greedy_head(h.to(DEV), E.to(DEV), path.to(DEV), acc, out, w)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy(), out.cpu().numpy()
+
+
+def _paths_from_chain(y, T, seed):
+    """Drafts equal to the target's argmax chain up to a planted mismatch at
+    a random position (or none), so every accepted length occurs."""
+    rng = np.random.default_rng(seed)
+    B = y.shape[0]
+    path = y[:, :T].astype(np.int32).copy()
+    cut = rng.integers(0, T + 1, size=B)
+    for b in range(B):
+        if cut[b] < T:
+            path[b, cut[b]] = (path[b, cut[b]] + 1 + rng.integers(0, 1000)) % 151936
+    return torch.from_numpy(path), cut
+
+
+def _check_verify_head(h, E, path, ga, go, reqs, label):
+    """reqs: request indices to recompute with the oracle.  Exact unless a
+    row's argmax had a near-tie (top-2 gap within twice the fp32 bound)."""
+    hs = h[torch.as_tensor(reqs)]
+    o = oracle.verify_greedy_head(hs, E, path[torch.as_tensor(reqs)])
+    d = h.shape[-1]
+    emax = float(E.float().abs().max())
+    near = 0
+    for j, b in enumerate(reqs):
+        if ga[b] == o["accept_len"][j] and np.array_equal(go[b], o["out_tok"][j]):
+            continue
+        hb = hs[j].float().numpy().astype(np.float64)
+        eps = 8 * np.sqrt(d) * U32 * np.abs(hb).sum(-1) * emax      # per row, an upper bound of the fp32 bound
+        n = min(int(ga[b]), int(o["accept_len"][j]))
+        assert o["margin"][j, n] <= 2 * eps[n], (label, b, int(ga[b]), int(o["accept_len"][j]))
+        near += 1
+    report(f"verify_greedy_head {label}", requests=len(reqs), near_tie_rows=near,
+           mean_accept=float(np.mean(ga[reqs])))
+    assert near <= max(1, len(reqs) // 8)
+
+
+@pytest.mark.parametrize("B,T,V,d", [(3, 7, 5003, 640), (5, 15, 2049, 128), (2, 1, 300, 64)])
+def test_verify_greedy_head_small(B, T, V, d):
+    g = torch.Generator().manual_seed(B * 100 + T)
+    h = torch.randn(B, T + 1, d, generator=g).to(torch.bfloat16)
+    E = (0.02 * torch.randn(V, d, generator=g)).to(torch.bfloat16)
+    y = oracle.verify_greedy_head(h, E, torch.zeros(B, T, dtype=torch.int32))["argmax"]
+    path, _ = _paths_from_chain(y, T, B)
+    path = path % V
+    ga, go = _verify_head_gpu(h, E, path)
+    _check_verify_head(h, E, path, ga, go, list(range(B)), f"B{B}T{T}V{V}d{d}")
+
+
+def test_verify_greedy_head_integer_inputs_bit_exact():
+    """Exact logits with frequent argmax ties (lowest id wins on both sides)."""
+    rng = np.random.default_rng(8)
+    B, T, V, d = 4, 7, 2000, 128
+    h = torch.from_numpy(rng.integers(-2, 3, size=(B, T + 1, d)).astype(np.float32)).to(torch.bfloat16)
+    E = torch.from_numpy(rng.integers(-2, 3, size=(V, d)).astype(np.float32)).to(torch.bfloat16)
+    y = oracle.verify_greedy_head(h, E, torch.zeros(B, T, dtype=torch.int32))["argmax"]
+    path, _ = _paths_from_chain(y, T, 9)
+    path = path % V
+    ga, go = _verify_head_gpu(h, E, path)
+    o = oracle.verify_greedy_head(h, E, path)
+    assert np.array_equal(ga, o["accept_len"]) and np.array_equal(go, o["out_tok"])
+
+
+def test_verify_greedy_head_b32_blk16_launch_shape():
+    """32 requests x 16 verified rows, vocabulary 151,936, hidden 5120 (the
+    launch shape of the batch-32, block-16 cycle); requests 0 and 31
+    recomputed by the oracle, with drafts built from its argmax chain."""
+    w = synth.WORKLOADS["b32_blk16_v151936_conv"]
+    B, T, V, d = w.B, w.T, w.V, w.d
+    print(f"[case] verify_greedy_head B={B} T={T} V={V} d={d}", flush=True)
+    E = synth.embeddings(w, device=DEV)
+    g = torch.Generator().manual_seed(31)
+    h = torch.randn(B, T + 1, d, generator=g).to(torch.bfloat16)
+    reqs = [0, 31]
+    Ec = E.cpu()
+    y = np.zeros((B, T + 1), np.int64)
+    y[reqs] = oracle.verify_greedy_head(h[reqs], Ec, torch.zeros(2, T, dtype=torch.int32))["argmax"]
+    path, _ = _paths_from_chain(y, T, 10)
+    ga, go = _verify_head_gpu(h, E, path)
+    _check_verify_head(h, Ec, path, ga, go, reqs, "B32T15V151936")
+
+
+def test_verify_greedy_head_b1_blk8_launch_shape():
+    w = synth.WORKLOADS["b1_blk8_v151936"]
+    B, T, V, d = w.B, w.T, w.V, w.d
+    E = synth.embeddings(w, device=DEV)
+    g = torch.Generator().manual_seed(32)
+    h = torch.randn(B, T + 1, d, generator=g).to(torch.bfloat16)
+    Ec = E.cpu()
+    y = oracle.verify_greedy_head(h, Ec, torch.zeros(B, T, dtype=torch.int32))["argmax"]
+    path = torch.from_numpy(y[:, :T].astype(np.int32))          # all drafts accepted: the bonus row counts
+    ga, go = _verify_head_gpu(h, E, path)
+    _check_verify_head(h, Ec, path, ga, go, [0], "B1T7V151936")
+    assert ga[0] == T
