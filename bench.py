@@ -39,6 +39,7 @@ STRESS = "b64_blk16_v262144_stress"
 KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm", "h_gemm",
                "proj_reduce", "pair_epilogue", "path", "argmax_part", "greedy_final",
                "sumexp_part", "reject_decide", "residual_chunk", "residual_find"]
+EVICT_BYTES = 1 << 30          # written between cold replays: 4x the 256 MB Infinity Cache
 
 
 def parse():
@@ -51,6 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-tables", action="store_true", help="skip the per-token table cycles")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache replays")
+    ap.add_argument("--no-heads", action="store_true",
+                    help="skip the fused LM-head legs (drafter top-16, target greedy verification)")
     ap.add_argument("--cpu-sample", type=int, default=0,
                     help="requests the oracle recomputes (0: all of the batch)")
     ap.add_argument("--json-out", default=None)
@@ -114,6 +118,88 @@ def replay_spread(cyc, n):
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
     return dict(median=round(ms[n // 2], 5), p90=round(ms[min(n - 1, (9 * n) // 10)], 5), n=n)
+
+
+def cold_replays(cyc, n, evict):
+    """Median and 90th percentile of single replays, each after `evict` (a
+    1 GiB buffer) has been overwritten, so that no input of the cycle is
+    left in the Infinity Cache or the L2s; the fill runs outside the events."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        evict.fill_(1)
+        a.record()
+        cyc.replay()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return dict(median_us=round(1e3 * ms[n // 2], 2), p90_us=round(1e3 * ms[min(n - 1, (9 * n) // 10)], 2), n=n)
+
+
+def heads_leg(dev, steps):
+    """The fused LM-head kernels at the benchmark's shapes: the drafter's
+    top-16 from its hidden states (dflash2_lm_head_topk; logits h E^T never
+    stored) and greedy verification from the target's hidden states
+    (dflash2_verify_greedy_head).  Per call: HIP events around `steps`
+    back-to-back calls; per kernel: the library's timing hook.  MFMA
+    fraction = 2 rows V d flops per call against the dense bf16 peak."""
+    import torch
+    import synth
+    import draft_selection_bf16_amd as df2
+    out = {}
+    E = None
+    for name in ("b32_blk16_v151936_conv", "b1_blk8_v151936"):
+        w = synth.WORKLOADS[name]
+        if E is None or E.shape[0] != w.V:
+            E = synth.embeddings(w, device=dev)
+        d, V = w.d, w.V
+        rows = w.B * w.T
+        h = synth.context_hidden(w, device=dev).reshape(rows, d)
+        idx = torch.empty((rows, 16), dtype=torch.int32, device=dev)
+        val = torch.empty((rows, 16), dtype=torch.float32, device=dev)
+        wsb = torch.empty(max(1, df2.dflash2_lm_head_topk_workspace_bytes(rows, V, d, 16)), dtype=torch.uint8,
+                          device=dev)
+        g = torch.Generator().manual_seed(5)
+        ht = torch.randn(w.B, w.T + 1, d, generator=g).to(torch.bfloat16).to(dev)
+        path = torch.randint(0, V, (w.B, w.T), generator=g, dtype=torch.int32).to(dev)
+        acc = torch.empty((w.B,), dtype=torch.int32, device=dev)
+        otok = torch.empty((w.B, w.T + 1), dtype=torch.int32, device=dev)
+        wsv = torch.empty(max(1, df2.dflash2_verify_greedy_head_workspace_bytes(w.B, w.T, V, d)),
+                          dtype=torch.uint8, device=dev)
+        calls = {"lm_head_topk": (lambda: df2.dflash2_lm_head_topk(h, E, 16, idx, val, wsb), rows,
+                                  ("lmhead_topk", "lmhead_merge")),
+                 "verify_greedy_head": (lambda: df2.dflash2_verify_greedy_head(ht, E, path, acc, otok, wsv),
+                                        w.B * (w.T + 1), ("head_argmax", "greedy_head_final"))}
+        res = {}
+        for key, (fn, nrows, tags) in calls.items():
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / steps
+            kern = {}
+            for tag in tags:
+                df2.dflash2_profile_start(tag, steps)
+                for _ in range(steps):
+                    fn()
+                ms = df2.dflash2_profile_stop(steps)
+                kern[tag] = round(1e3 * sum(ms) / max(1, len(ms)), 2)
+            flops = 2 * nrows * V * d
+            tf = flops / (us * 1e-6) / 1e12
+            res[key] = dict(rows=nrows, us_per_call=round(us, 2), kernels_us=kern, tflops=round(tf, 1),
+                            mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
+                            lm_head_read_tbs=round(V * d * 2 / (us * 1e-6) / 1e12, 2))
+        out[name] = res
+        del h, idx, val, wsb, ht, path, acc, otok, wsv
+    del E
+    torch.cuda.empty_cache()
+    return out
 
 
 def profile_kernels(cyc, steps):
@@ -248,6 +334,7 @@ def roofline_of(w, tag, avg_us):
 
 
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_b32_blk16_v151936_conv.txt")
+TRACE = os.path.join(ROOT, "profiles", "cycle_b32_blk16_v151936_conv_kernel_trace.txt")
 
 def source_hash():
     import glob
@@ -285,7 +372,27 @@ def measured_traffic(tag):
                        r["write_kib"] * float(kv["write_factor"])))
 
 
-def cpu_baseline(cyc, w, nreq, min_seconds=10.0, max_reps=4):
+def trace_avg_us(tag):
+    """Average duration (us) of kernel `tag` in the committed rocprofv3
+    kernel-trace summary of the benchmark cycle, or None when the summary is
+    missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRACE):
+        return None
+    sha, avg = None, None
+    for line in open(TRACE):
+        line = line.strip()
+        if line.startswith("# source_sha256"):
+            sha = line.split("=", 1)[1].strip()
+        elif line and not line.startswith("#"):
+            parts = line.split()
+            if parts[0] == tag and len(parts) >= 3:
+                avg = float(parts[2])
+    if sha != source_hash():
+        return None
+    return avg
+
+
+def cpu_baseline(cyc, w, nreq, min_seconds=10.0, max_reps=4, one_core_req=1):
     """The oracle's cycle for `nreq` of the requests (all 20 conv sites on
     those requests, top-16, pair scores, Viterbi, greedy verification),
     repeated until about `min_seconds` of oracle time (at most `max_reps`
@@ -327,11 +434,35 @@ def cpu_baseline(cyc, w, nreq, min_seconds=10.0, max_reps=4):
     while secs < min_seconds and reps < max_reps:
         secs += one_pass()
         reps += 1
-    return dict(value=round(nreq * reps / secs, 4), unit="blocks/s", cores=oracle.num_threads(),
-                kind="oracle", seconds=round(secs, 2),
-                sample=f"{reps} pass(es) over {nreq} of {w.B} requests of {w.name}: 20 conv sites, "
-                       f"top-16, pair scores, Viterbi path, greedy verify (embedding-row gather "
-                       f"excluded)")
+    cores = oracle.num_threads()
+    out = dict(value=round(nreq * reps / secs, 4), unit="blocks/s", cores=cores,
+               kind="oracle", seconds=round(secs, 2),
+               sample=f"{reps} pass(es) over {nreq} of {w.B} requests of {w.name}: 20 conv sites, "
+                      f"top-16, pair scores, Viterbi path, greedy verify (embedding-row gather "
+                      f"excluded)")
+    # the same oracle on one core, over `one_core_req` requests
+    n1 = max(1, min(one_core_req, nreq))
+    rows = rows[:n1]
+    z, Z, h, last = z[:n1], Z[:n1], h[:n1], last[:n1]
+    sites = [(x[:n1], xp[:n1], wt, bs) for x, xp, wt, bs in sites]
+    oracle.set_num_threads(1)
+    try:
+        s1 = one_pass()
+    finally:
+        oracle.set_num_threads(cores)
+    out["one_core"] = dict(value=round(n1 / s1, 4), unit="blocks/s", cores=1, seconds=round(s1, 2),
+                           sample=f"1 pass over {n1} request(s) of {w.name}, same steps")
+    import platform
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    out["host"] = dict(cpu=cpu, os_cpu_count=os.cpu_count(), machine=platform.machine())
+    return out
 
 
 def main():
@@ -367,6 +498,8 @@ def main():
     ms, wall = time_graph(cyc, args.steps, args.warmup)
     value = w.B / (ms / 1e3)
     spread = replay_spread(cyc, min(args.steps, 100))
+    evict = None if args.no_cold else torch.empty(EVICT_BYTES, dtype=torch.uint8, device=dev)
+    cold = None if evict is None else cold_replays(cyc, min(args.steps, 50), evict)
 
     # the same cycle without the conv sites (top-K + select + verify only)
     cyc_nc, _ = build_cycle(w, dev, E=E, conv=False)
@@ -382,6 +515,12 @@ def main():
         roof = roofline_of(w, dom, kernels[dom]["avg_us"])
         if roof is not None and w.name == "b32_blk16_v151936_conv":
             roof["traffic"] = measured_traffic(dom)
+            # the same kernel's average duration in the committed rocprofv3
+            # trace of this command, and the fraction it gives
+            tus = trace_avg_us(dom)
+            if tus:
+                rt = roofline_of(w, dom, tus)
+                roof["trace"] = dict(avg_us=round(tus, 2), achieved=rt["achieved"], frac=rt["frac"])
         for k, v in kernels.items():
             rl = roofline_of(w, k, v["avg_us"])
             if rl:
@@ -390,7 +529,6 @@ def main():
     sweep = {}
     if not args.no_sweep:
         log("sweep")
-        del cyc_nc
         for name in ("b1_blk8_v151936", "b8_blk8_v151936_sampled", "b32_blk8_v151936",
                      "b1_blk16_v151936", "b8_blk16_v151936"):
             ws_ = synth.WORKLOADS[name]
@@ -400,10 +538,16 @@ def main():
             sweep[name] = dict(B=ws_.B, block=ws_.block, path=ws_.path_mode, verify=ws_.verify,
                                us_per_cycle=round(m2 * 1e3, 2), blocks_per_s=round(ws_.B / (m2 / 1e3), 1),
                                hbm_frac=hbm_frac(ws_, False, m2 * 1e3))
+            if evict is not None:
+                cr = cold_replays(c2, min(args.steps, 50), evict)
+                sweep[name]["cold"] = dict(cr, hbm_frac=hbm_frac(ws_, False, cr["median_us"]))
             del c2
         sweep[w.name + " (no conv)"] = dict(B=w.B, block=w.block, us_per_cycle=round(ms_nc * 1e3, 2),
                                             blocks_per_s=round(w.B / (ms_nc / 1e3), 1),
                                             hbm_frac=hbm_frac(w, False, ms_nc * 1e3))
+        if evict is not None:
+            cr = cold_replays(cyc_nc, min(args.steps, 50), evict)
+            sweep[w.name + " (no conv)"]["cold"] = dict(cr, hbm_frac=hbm_frac(w, False, cr["median_us"]))
         if w.name != STRESS:
             # the stress cycle (64 requests, vocabulary 262,144, half greedy and half
             # rejection verification), with and without its 20 conv sites
@@ -419,6 +563,12 @@ def main():
                     blocks_per_s=round(ws_.B / (m2 / 1e3), 1), hbm_frac=hbm_frac(ws_, conv, m2 * 1e3))
                 del c2
             del E4
+
+    del cyc_nc
+    heads = None
+    if not args.no_heads:
+        log("fused LM-head legs")
+        heads = heads_leg(dev, min(args.steps, 20))
 
     tabs = None
     if not args.no_tables:
@@ -452,11 +602,13 @@ def main():
         "hbm_frac": hbm_frac(w, True, ms * 1e3),
         "hbm_frac_without_conv": hbm_frac(w, False, ms_nc * 1e3),
         "replay_ms": spread,
+        "cold_replay": None if cold is None else dict(cold, hbm_frac=hbm_frac(w, True, cold["median_us"])),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "sweep": sweep,
         "tables": tabs,
+        "heads": heads,
         "wall_s_timed": round(wall, 3),
     }
     s = json.dumps(line)

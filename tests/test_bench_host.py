@@ -62,3 +62,18 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_trace_summary_parser(tmp_path, monkeypatch):
+    """The trace figure is read only when the summary was taken from the
+    current kernel sources."""
+    f = tmp_path / "trace.txt"
+    f.write_text("# command: x\n# source_sha256 = abc\nkernel calls avg_us min_us max_us total_us\n"
+                 "conv_gemm 10 12.50 9.9 19.1 125.0\ntopk_chunk 5 33.0 30 38 165\n")
+    monkeypatch.setattr(bench, "TRACE", str(f))
+    monkeypatch.setattr(bench, "source_hash", lambda: "abc")
+    assert bench.trace_avg_us("conv_gemm") == 12.5
+    assert bench.trace_avg_us("topk_chunk") == 33.0
+    assert bench.trace_avg_us("path") is None
+    monkeypatch.setattr(bench, "source_hash", lambda: "changed")
+    assert bench.trace_avg_us("conv_gemm") is None
