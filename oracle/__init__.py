@@ -7,7 +7,7 @@ raw 16-bit patterns.  Every function returns fresh numpy outputs.
 
 Parity status per function (details in the C source):
   topk, project, pair_scores, path, verify_greedy, verify_reject, dynconv2,
-  lm_head_topk, verify_greedy_head, philox -- all pinned by the CPU tests in
+  lm_head_topk, verify_greedy_head, verify_reject_head, philox -- all pinned by the CPU tests in
   tests/test_oracle_*.py;
   selector_tables, pair_scores_tab (numpy, below) -- pinned by
   tests/test_oracle_tables.py.
@@ -61,9 +61,11 @@ def _declare(L):
     L.oracle_dynconv2.argtypes = [P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P]
     L.oracle_lm_head_topk.argtypes = [P, P, I64, I64, C.c_int, C.c_int, P, P]
     L.oracle_verify_greedy_head.argtypes = [P, P, I64, C.c_int, P, C.c_int, C.c_int, P, P, P, P]
+    L.oracle_verify_reject_head.argtypes = [P, P, I64, C.c_int, P, P, P, P, C.c_int, C.c_int, C.c_int, F64,
+                                            U64, P, P, P, P, P, P]
     for f in ("oracle_topk", "oracle_project", "oracle_pair_scores", "oracle_path",
               "oracle_verify_greedy", "oracle_verify_reject", "oracle_dynconv2",
-              "oracle_lm_head_topk", "oracle_verify_greedy_head"):
+              "oracle_lm_head_topk", "oracle_verify_greedy_head", "oracle_verify_reject_head"):
         getattr(L, f).restype = C.c_int
 
 
@@ -327,6 +329,33 @@ def verify_reject(target, path_tok, path_rank, cand_idx, q, temperature: float, 
            "oracle_verify_reject")
     return dict(accept_len=acc, out_tok=out, margin_accept=ma, margin_sample=ms,
                 fallbacks=int(fb[0]))
+
+
+def verify_reject_head(h, emb, path_tok, path_rank, cand_idx, q, temperature: float, seed: int, b_ids=None):
+    """Rejection-sampling verification with the target logits computed in
+    float64 from its hidden states h [B, T+1, d] through its LM head emb
+    [V, d] (both bf16); outputs as verify_reject."""
+    ha, hdt = host(h)
+    ea, edt = host(emb)
+    assert hdt == BF16 and edt == BF16
+    pt = np.ascontiguousarray(np.asarray(host(path_tok)[0], dtype=np.int32))
+    pr = np.ascontiguousarray(np.asarray(host(path_rank)[0], dtype=np.int32))
+    ci = np.ascontiguousarray(np.asarray(host(cand_idx)[0], dtype=np.int32))
+    qa = np.ascontiguousarray(np.asarray(host(q)[0], dtype=np.float32))
+    B, T = pt.shape
+    K = ci.shape[-1]
+    V, d = ea.shape
+    assert ha.shape == (B, T + 1, d)
+    acc = np.zeros((B,), np.int32)
+    out = np.zeros((B, T + 1), np.int32)
+    ma = np.zeros((B, T), np.float64)
+    ms = np.zeros((B,), np.float64)
+    fb = np.zeros((1,), np.int32)
+    bi = _bids(b_ids, B)
+    _check(lib().oracle_verify_reject_head(_ptr(ha), _ptr(ea), V, d, _ptr(pt), _ptr(pr), _ptr(ci), _ptr(qa), B, T,
+                                           K, float(temperature), int(seed) & (2**64 - 1), _ptr(bi), _ptr(acc),
+                                           _ptr(out), _ptr(ma), _ptr(ms), _ptr(fb)), "oracle_verify_reject_head")
+    return dict(accept_len=acc, out_tok=out, margin_accept=ma, margin_sample=ms, fallbacks=int(fb[0]))
 
 
 def dynconv2(x, x_prev, w, base=None, group: int = 16) -> np.ndarray:

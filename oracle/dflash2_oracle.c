@@ -33,10 +33,12 @@
 #include <omp.h>
 #endif
 
-/* dtype codes accepted by the oracle */
+/* dtype codes accepted by the oracle (OR_FP64: double logits, accepted by
+ * the verification functions only) */
 #define OR_FP32 0
 #define OR_BF16 1
 #define OR_FP16 2
+#define OR_FP64 3
 
 /* path modes */
 #define OR_PATH_VITERBI 0
@@ -79,6 +81,12 @@ static float elem(const void* p, int dt, int64_t i) {
   if (dt == OR_FP32) return ((const float*)p)[i];
   if (dt == OR_BF16) return bf16_value(((const uint16_t*)p)[i]);
   return fp16_value(((const uint16_t*)p)[i]);
+}
+
+/* the same in double, with double logits (OR_FP64) read as they are */
+static double elemd(const void* p, int dt, int64_t i) {
+  if (dt == OR_FP64) return ((const double*)p)[i];
+  return (double)elem(p, dt, i);
 }
 
 /* ------------------------------------------------------------------ */
@@ -643,11 +651,11 @@ static void softmax_row(const void* target, int dt, int64_t base, int64_t vocab,
                         double* p) {
   double m = -INFINITY, z = 0.0;
   for (int64_t v = 0; v < vocab; ++v) {
-    double x = (double)elem(target, dt, base + v) / tau;
+    double x = elemd(target, dt, base + v) / tau;
     if (x > m) m = x;
   }
   for (int64_t v = 0; v < vocab; ++v) {
-    p[v] = exp((double)elem(target, dt, base + v) / tau - m);
+    p[v] = exp(elemd(target, dt, base + v) / tau - m);
     z += p[v];
   }
   for (int64_t v = 0; v < vocab; ++v) p[v] /= z;
@@ -723,6 +731,45 @@ int oracle_verify_reject(const void* target, int dt, int64_t vocab, const int32_
   }
   if (fallbacks) *fallbacks = nfb;
   return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Rejection-sampling verification from the target's hidden states       */
+/* through its LM head: the target logits Z[b][t][v] = sum_k h[b][t][k]  */
+/* E[v][k] are computed in double (instead of read) and verified as in   */
+/* oracle_verify_reject, in double throughout.                           */
+/* Pinned by: agreement with oracle_verify_reject on integer inputs,     */
+/* whose logits are exact in float (the same uniforms give the same      */
+/* accepted lengths and tokens).                                         */
+/* ------------------------------------------------------------------ */
+
+int oracle_verify_reject_head(const uint16_t* h, const uint16_t* emb, int64_t vocab, int d,
+                              const int32_t* path_tok, const int32_t* path_rank, const int32_t* cand_idx,
+                              const float* q, int B, int T, int K, double temperature, uint64_t seed,
+                              const int32_t* b_ids, int32_t* accept_len, int32_t* out_tok,
+                              double* margin_accept, double* margin_sample, int32_t* fallbacks) {
+  if (vocab < 1 || d < 1) return 3;
+  const int64_t rows = (int64_t)B * (T + 1);
+  double* z = (double*)malloc(sizeof(double) * (size_t)rows * (size_t)vocab);
+  double* hr = (double*)malloc(sizeof(double) * (size_t)d);
+  if (!z || !hr) {
+    free(z); free(hr);
+    return 1;
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int qd = 0; qd < d; ++qd) hr[qd] = (double)bf16_value(h[r * d + qd]);
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < vocab; ++v) {
+      double acc = 0.0;
+      for (int qd = 0; qd < d; ++qd) acc += hr[qd] * (double)bf16_value(emb[v * d + qd]);
+      z[r * vocab + v] = acc;
+    }
+  }
+  int rc = oracle_verify_reject(z, OR_FP64, vocab, path_tok, path_rank, cand_idx, q, B, T, K, temperature,
+                                seed, b_ids, accept_len, out_tok, margin_accept, margin_sample, fallbacks);
+  free(z);
+  free(hr);
+  return rc;
 }
 
 /* ------------------------------------------------------------------ */

@@ -126,3 +126,27 @@ def test_verify_greedy_head_one_hot_head():
     assert np.array_equal(o["argmax"], want)
     assert o["accept_len"].tolist() == [T, T]
     assert np.array_equal(o["out_tok"], want)
+
+
+def test_verify_reject_head_equals_verify_reject_on_exact_logits():
+    """Integer inputs: the target logits are exact in float, so rejection
+    verification from the hidden states draws the same uniforms and decides
+    exactly as oracle.verify_reject on the logits (sampled proposals, mixed
+    accepted lengths, resampled and bonus tokens)."""
+    rng = np.random.default_rng(11)
+    B, T, K, V, d = 40, 4, 4, 60, 16
+    h = rng.integers(-2, 3, size=(B, T + 1, d)).astype(np.float32)
+    E = rng.integers(-1, 2, size=(V, d)).astype(np.float32)
+    Z = (h.astype(np.int64) @ E.astype(np.int64).T).astype(np.float32)
+    # candidates: each position's K best target tokens (so drafts are often accepted)
+    cand = np.argsort(-Z[:, :T, :], axis=-1, kind="stable")[..., :K].astype(np.int32)
+    q = rng.dirichlet(np.ones(K), size=(B, T)).astype(np.float32)
+    rank = np.array([[rng.choice(K, p=q[b, t] / q[b, t].sum()) for t in range(T)] for b in range(B)],
+                    np.int32)
+    tok = np.take_along_axis(cand, rank[..., None], -1)[..., 0].astype(np.int32)
+    for tau in (1.0, 0.5):
+        o = oracle.verify_reject_head(_bf16(h), _bf16(E), tok, rank, cand, q, tau, 21, b_ids=np.arange(B) + 3)
+        g = oracle.verify_reject(Z, tok, rank, cand, q, tau, 21, b_ids=np.arange(B) + 3)
+        assert np.array_equal(o["accept_len"], g["accept_len"])
+        assert np.array_equal(o["out_tok"], g["out_tok"])
+        assert len(set(o["accept_len"].tolist())) >= 3
