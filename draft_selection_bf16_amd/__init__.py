@@ -36,6 +36,7 @@ EXPORTS = [
     "dflash2_verify_workspace_bytes", "dflash2_verify_greedy", "dflash2_verify_reject",
     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_noalloc_max_bytes",
     "dflash2_verify_greedy_head_workspace_bytes", "dflash2_verify_greedy_head",
+    "dflash2_verify_reject_head_workspace_bytes", "dflash2_verify_reject_head",
     "dflash2_philox4x64", "dflash2_profile_start", "dflash2_profile_stop",
 ]
 
@@ -89,6 +90,9 @@ def lib():
         L.dflash2_verify_greedy_head_workspace_bytes.argtypes = [I, I, I64, I]
         L.dflash2_verify_greedy_head_workspace_bytes.restype = SZ
         L.dflash2_verify_greedy_head.argtypes = [P, P, I, I64, I, P, I, I, P, P, P, SZ, P]
+        L.dflash2_verify_reject_head_workspace_bytes.argtypes = [I, I, I64, I, I]
+        L.dflash2_verify_reject_head_workspace_bytes.restype = SZ
+        L.dflash2_verify_reject_head.argtypes = [P, P, I, I64, I, P, P, P, P, I, I, I, F, P, I, P, P, P, SZ, P]
         L.dflash2_verify_greedy_noalloc_max_bytes.restype = SZ
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
         L.dflash2_profile_start.argtypes = [C.c_char_p, I]
@@ -99,7 +103,7 @@ def lib():
                      "dflash2_pair_scores_tab", "dflash2_h_projection", "dflash2_pair_scores_tab_from_h",
                      "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
-                     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_head",
+                     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_head", "dflash2_verify_reject_head",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
         _lib = L
@@ -268,6 +272,24 @@ def dflash2_verify_greedy_head(h, emb, path_tok, accept_len, out_tok, ws, stream
     _check(lib().dflash2_verify_greedy_head(_ptr(h), _ptr(emb), _dt(emb), V, d, _ptr(path_tok), B, T1 - 1,
                                             _ptr(accept_len), _ptr(out_tok), _ptr(ws), _bytes(ws),
                                             _stream(stream)), "dflash2_verify_greedy_head")
+
+
+def dflash2_verify_reject_head_workspace_bytes(B: int, T: int, vocab: int, d: int, K: int) -> int:
+    return int(lib().dflash2_verify_reject_head_workspace_bytes(B, T, vocab, d, K))
+
+
+def dflash2_verify_reject_head(h, emb, path_tok, path_rank, cand_idx, q, temperature, seed_dev,
+                               accept_len, out_tok, ws, b0=0, stream=None):
+    """Rejection verification with the target logits computed from its
+    hidden states h [B, T+1, d] through its LM head emb [V, d] (both bf16).
+    b0: index of h[0]'s request in the batch the seed covers."""
+    B, T1, d = h.shape
+    V = emb.shape[0]
+    K = cand_idx.shape[-1]
+    _check(lib().dflash2_verify_reject_head(_ptr(h), _ptr(emb), _dt(emb), V, d, _ptr(path_tok), _ptr(path_rank),
+                                            _ptr(cand_idx), _ptr(q), B, T1 - 1, K, float(temperature),
+                                            _ptr(seed_dev), int(b0), _ptr(accept_len), _ptr(out_tok), _ptr(ws),
+                                            _bytes(ws), _stream(stream)), "dflash2_verify_reject_head")
 
 
 def dflash2_verify_greedy_noalloc_max_bytes() -> int:

@@ -200,6 +200,40 @@ int dflash2_verify_greedy_head(const void* h, const void* emb, int emb_dt, int64
                     "dflash2_verify_greedy_head");
 }
 
+size_t dflash2_verify_reject_head_workspace_bytes(int B, int T, int64_t vocab, int d, int K) {
+  if (B <= 0 || T <= 0 || vocab <= 0 || d <= 0 || K <= 0) return 0;
+  return head_reject_plan(B, T, vocab, d, K).ws_bytes;
+}
+
+int dflash2_verify_reject_head(const void* h, const void* emb, int emb_dt, int64_t vocab, int d,
+                               const int32_t* path_tok, const int32_t* path_rank, const int32_t* cand_idx,
+                               const float* q, int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                               int b0, int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_verify_reject_head: the LM head must be BF16");
+  REQUIRE(temperature > 0.f && isfinite(temperature), DF2_ERR_UNSUPPORTED,
+          "dflash2_verify_reject_head: needs a finite temperature > 0 (got %g)", (double)temperature);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_verify_reject_head: vocab %lld",
+          (long long)vocab);
+  REQUIRE(d >= 64 && d % 64 == 0 && d <= 65536, DF2_ERR_SHAPE,
+          "dflash2_verify_reject_head: d %d is not a multiple of 64 in [64, 65536]", d);
+  REQUIRE(B >= 0 && B <= kMaxB / 64, DF2_ERR_SHAPE, "dflash2_verify_reject_head: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_verify_reject_head: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_verify_reject_head: K %d not in [1, 16]", K);
+  REQUIRE(b0 >= 0 && (int64_t)b0 + B <= ((int64_t)1 << 31) - 1, DF2_ERR_SHAPE,
+          "dflash2_verify_reject_head: b0 %d (with B %d) outside [0, 2^31 - 1]", b0, B);
+  if (B == 0) return DF2_OK;
+  REQUIRE(h && emb && path_tok && path_rank && cand_idx && q && seed_dev && accept_len && out_tok, DF2_ERR_NULL,
+          "dflash2_verify_reject_head: null pointer argument");
+  REQUIRE(aligned16(h) && aligned16(emb), DF2_ERR_SHAPE, "dflash2_verify_reject_head: h/emb must be 16-byte aligned");
+  HeadRejectPlan plan = head_reject_plan(B, T, vocab, d, K);
+  REQUIRE(ws && ws_bytes >= plan.ws_bytes, DF2_ERR_WORKSPACE,
+          "dflash2_verify_reject_head: workspace %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+  return hip_status(launch_verify_reject_head(h, emb, vocab, d, path_tok, path_rank, cand_idx, q, B, T, K,
+                                              temperature, seed_dev, b0, accept_len, out_tok, ws, plan, stream),
+                    "dflash2_verify_reject_head");
+}
+
 // ------------------------------------------------------------------ pair scores
 namespace {
 // projection tiling: 128-row tiles, one work-group per CU, 8 waves (two per

@@ -55,6 +55,25 @@ __device__ __forceinline__ uint64_t make_key(float f, uint32_t idx) {
 __device__ __forceinline__ uint32_t key_index(uint64_t k) { return ~(uint32_t)k; }
 __device__ __forceinline__ float key_value(uint64_t k) { return value_of_ord((uint32_t)(k >> 32)); }
 
+// Online-softmax partial of a set of logits: key = make_key of its maximum
+// (value, lowest index), s = sum of exp2((z - value(key)) c).  Combine two
+// partials (key 0 = empty), the sum kept relative to the larger maximum.
+__device__ __forceinline__ void combine_part(uint64_t& k, float& s, uint64_t k2, float s2, float c) {
+  if (k2 == 0ull) return;
+  if (k == 0ull) {
+    k = k2;
+    s = s2;
+    return;
+  }
+  float m1 = key_value(k), m2 = key_value(k2);
+  if (k2 > k) {
+    s = s * exp2f((m1 - m2) * c) + s2;
+    k = k2;
+  } else {
+    s = s + s2 * exp2f((m2 - m1) * c);
+  }
+}
+
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);

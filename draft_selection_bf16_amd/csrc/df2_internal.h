@@ -156,6 +156,39 @@ struct LmHeadPlan {
 };
 // keep = 16 (the drafter's top-16) or 1 (the target's argmax)
 LmHeadPlan lmhead_plan(int M, int64_t vocab, int d, int keep);
+// tokens per block of the fused LM-head kernels (the token side of a tile)
+constexpr int kHeadBlock = 128;
+// Online-softmax partial of one 128-token block of one row: key = the
+// block's (max logit, lowest index), s = sum of exp2((z - max) c).
+struct BlockStat {
+  uint64_t key;
+  float s;
+  float pad;
+};
+// Statistics mode of the fused LM-head kernel (rejection verification):
+// rows are (b, t) = (row / (T + 1), row % (T + 1)) of a [B, T+1] block.
+struct HeadStats {
+  float c;                 // log2(e) / temperature
+  int T, K;
+  const int32_t* cand;     // [B, T, K] candidates (t < T)
+  const int32_t* xtok;     // [B, T] drafted tokens
+  BlockStat* stats;        // [rows, nblocks]
+  float* zc;               // [rows, K] logits of the candidates (t < T)
+  float* zx;               // [rows] logit of the drafted token (t < T)
+};
+hipError_t launch_head_stats(const void* h, const void* emb, int64_t vocab, int M, int d, const HeadStats& hs,
+                             const LmHeadPlan& plan, hipStream_t stream);
+struct HeadRejectPlan {
+  LmHeadPlan lm;
+  size_t off_stats, off_rowst, off_zc, off_zx, off_dec, off_zblk;
+  size_t ws_bytes;
+};
+HeadRejectPlan head_reject_plan(int B, int T, int64_t vocab, int d, int K);
+hipError_t launch_verify_reject_head(const void* h, const void* emb, int64_t vocab, int d,
+                                     const int32_t* path_tok, const int32_t* path_rank, const int32_t* cand_idx,
+                                     const float* q, int B, int T, int K, float temperature,
+                                     const uint64_t* seed_dev, int b0, int32_t* accept_len, int32_t* out_tok,
+                                     void* ws, const HeadRejectPlan& plan, hipStream_t stream);
 hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int M, int d, int k,
                               int32_t* out_idx, float* out_val, void* ws, const LmHeadPlan& plan,
                               hipStream_t stream);

@@ -60,6 +60,7 @@ constexpr int kMaxRanges = 256;
 static_assert(kBM * kOld * 4 <= kLds, "fp32 tile fits the stages");
 static_assert(kBM * kQ * 16 * 8 <= kLds, "the rows' lists fit the stages");
 static_assert(kQ == 4 && kBN % kQ == 0, "four threads per row");
+static_assert(kBN == kHeadBlock, "statistics are kept per token block");
 
 // Insert key x into the list l[0] > l[1] > ... > l[15] (0 = empty) when it
 // is larger than l[15]: every entry moves down one place past x.
@@ -75,10 +76,13 @@ __device__ __forceinline__ void insert16(uint64_t (&l)[16], uint64_t x) {
 // grid: mblocks * nranges work-groups of kThreads; dynamic LDS kLds.
 // part[(row * nranges + range) * KEEP + i]: the i-th best key of the range
 // (KEEP = 16: the drafter's top-16; KEEP = 1: the target's argmax).
+// KEEP = 0 (statistics for rejection verification): per row and 128-token
+// block the online-softmax partial hs.stats, and the logits of the row's
+// candidates (hs.zc) and drafted token (hs.zx) as their blocks go by.
 template <int KEEP>
 __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     const uint16_t* __restrict__ h, int M, const uint16_t* __restrict__ emb, int64_t vocab, int K,
-    int mblocks, int nranges, int nblocks, int xcd_groups, uint64_t* __restrict__ part) {
+    int mblocks, int nranges, int nblocks, int xcd_groups, uint64_t* __restrict__ part, HeadStats hs) {
   const int bid = blockIdx.x;
   int mb, nr;
   if (xcd_groups) {   // nranges % 8 == 0: the row blocks of a token range share an XCD
@@ -123,12 +127,27 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
   }
   // the running best KEEP keys of this thread: row tid / 4, columns
   // tid % 4 + 4 j
-  static_assert(KEEP == 16 || KEEP == 1, "best-16 lists or the argmax");
+  static_assert(KEEP == 16 || KEEP == 1 || KEEP == 0, "best-16 lists, the argmax, or statistics");
   const int my_row = threadIdx.x / kQ, my_q = threadIdx.x % kQ;
-  uint64_t best[KEEP];
+  uint64_t best[KEEP > 0 ? KEEP : 1];
 #pragma unroll
-  for (int i = 0; i < KEEP; ++i) best[i] = 0ull;
+  for (int i = 0; i < (KEEP > 0 ? KEEP : 1); ++i) best[i] = 0ull;
   float* tile = (float*)dyn_lds;
+  // statistics mode: this thread's four candidates of its row (ranks
+  // 4 q .. 4 q + 3) and, for q = 0, the drafted token
+  int32_t cid[4] = {-1, -1, -1, -1};
+  int32_t xt = -1;
+  if constexpr (KEEP == 0) {
+    const int r = m0 + my_row, b = r / (hs.T + 1), t = r % (hs.T + 1);
+    if (r < M && t < hs.T) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = my_q * 4 + i;
+        if (k < hs.K) cid[i] = hs.cand[((int64_t)b * hs.T + t) * hs.K + k];
+      }
+      if (my_q == 0) xt = hs.xtok[(int64_t)b * hs.T + t];
+    }
+  }
 
   for (int nb = nb0; nb < nb1; ++nb) {
     const int64_t n0 = (int64_t)nb * kBN;
@@ -198,7 +217,53 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     // its busiest lane needs, not once per value).
     const float* trow = tile + my_row * kOld;
     const int ncols = wrows;   // columns past the vocabulary are not tokens
-    uint64_t thr = best[KEEP - 1];
+    if constexpr (KEEP == 0) {
+      // the block's online-softmax partial of this row: each thread over its
+      // columns, then the row's four threads combined (symmetrically: all
+      // four hold the same result)
+      float v[kBN / kQ];
+#pragma unroll
+      for (int j = 0; j < kBN / kQ; ++j) v[j] = trow[my_q + kQ * j];
+      uint64_t mk = 0ull;
+#pragma unroll
+      for (int j = 0; j < kBN / kQ; ++j) {
+        const int c = my_q + kQ * j;
+        const uint64_t key = make_key(v[j], (uint32_t)(n0 + c));
+        if (c < ncols && v[j] == v[j] && key > mk) mk = key;
+      }
+      float sum = 0.f;
+      if (mk) {
+        const float m = key_value(mk);
+#pragma unroll
+        for (int j = 0; j < kBN / kQ; ++j)
+          if (my_q + kQ * j < ncols && v[j] == v[j]) sum += v[j] == m ? 1.f : exp2f((v[j] - m) * hs.c);
+      }
+#pragma unroll
+      for (int msk = 1; msk <= 2; msk <<= 1) {
+        const uint64_t k2 = shfl_xor_u64(mk, msk);
+        const float s2 = __shfl_xor(sum, msk);
+        uint64_t ka = mk < k2 ? mk : k2, kb = mk < k2 ? k2 : mk;
+        float sa = mk < k2 ? sum : s2, sb = mk < k2 ? s2 : sum;
+        combine_part(kb, sb, ka, sa, hs.c);
+        mk = kb;
+        sum = sb;
+      }
+      const int r = m0 + my_row;
+      if (my_q == 0 && r < M) {
+        BlockStat bs;
+        bs.key = mk;
+        bs.s = sum;
+        bs.pad = 0.f;
+        hs.stats[(int64_t)r * nblocks + nb] = bs;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (cid[i] >= n0 && cid[i] < n0 + ncols) hs.zc[(int64_t)r * hs.K + my_q * 4 + i] = trow[cid[i] - n0];
+      if (xt >= n0 && xt < n0 + ncols) hs.zx[r] = trow[xt - n0];
+      __syncthreads();   // the tile is read before the next block's stages overwrite it
+      continue;
+    }
+    uint64_t thr = best[KEEP > 0 ? KEEP - 1 : 0];
     {
       const uint64_t o1 = shfl_xor_u64(thr, 1);
       thr = o1 > thr ? o1 : thr;
@@ -227,6 +292,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     __syncthreads();   // the tile is read before the next block's stages overwrite it
   }
 
+  if constexpr (KEEP == 0) return;
   if constexpr (KEEP == 1) {
     // the row's argmax key of the range: the largest of its four threads'
     uint64_t m = best[0];
@@ -353,6 +419,7 @@ __global__ __launch_bounds__(64) void greedy_head_final_kernel(const uint64_t* _
 
 bool g_lds_set = false;
 bool g_lds_set1 = false;
+bool g_lds_set0 = false;
 
 }  // namespace
 
@@ -388,7 +455,7 @@ hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int
     ProfileScope ps("lmhead_topk", stream);
     DF2_TRY(launch(lmhead_topk_kernel<16>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
                    stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
-                   plan.nranges, plan.nblocks, plan.xcd_groups, part));
+                   plan.nranges, plan.nblocks, plan.xcd_groups, part, HeadStats{}));
   }
   ProfileScope ps("lmhead_merge", stream);
   DF2_TRY(launch(lmhead_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), 0, stream, ps, part,
@@ -412,11 +479,27 @@ hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t voc
     ProfileScope ps("head_argmax", stream);
     DF2_TRY(launch(lmhead_topk_kernel<1>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
                    stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
-                   plan.nranges, plan.nblocks, plan.xcd_groups, part));
+                   plan.nranges, plan.nblocks, plan.xcd_groups, part, HeadStats{}));
   }
   ProfileScope ps("greedy_head_final", stream);
   DF2_TRY(launch(greedy_head_final_kernel, dim3((unsigned)B), dim3(64), 0, stream, ps, part, plan.nranges, path_tok,
                  T, accept_len, out_tok));
+  return hipGetLastError();
+}
+
+hipError_t launch_head_stats(const void* h, const void* emb, int64_t vocab, int M, int d, const HeadStats& hs,
+                             const LmHeadPlan& plan, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (!g_lds_set0) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<0>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    g_lds_set0 = true;
+  }
+  ProfileScope ps("head_stats", stream);
+  DF2_TRY(launch(lmhead_topk_kernel<0>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
+                 stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks, plan.nranges,
+                 plan.nblocks, plan.xcd_groups, (uint64_t*)nullptr, hs));
   return hipGetLastError();
 }
 

@@ -288,22 +288,6 @@ struct SumExp {
   __device__ void vec(const u32x4& v, int64_t i0) { vec_as_floats<DT>(*this, v, i0); }
 };
 
-// combine two (key, s) partials, both sums relative to their own max
-__device__ __forceinline__ void combine_part(uint64_t& k, float& s, uint64_t k2, float s2, float c) {
-  if (k2 == 0ull) return;
-  if (k == 0ull) {
-    k = k2;
-    s = s2;
-    return;
-  }
-  float m1 = key_value(k), m2 = key_value(k2);
-  if (k2 > k) {
-    s = s * exp2f((m1 - m2) * c) + s2;
-    k = k2;
-  } else {
-    s = s + s2 * exp2f((m2 - m1) * c);
-  }
-}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void sumexp_part_kernel(const void* __restrict__ z,

@@ -21,6 +21,8 @@
  *   dflash2_verify_greedy_head  the same from the target's hidden states,
  *                          with its LM head fused in (logits never stored)
  *   dflash2_verify_reject  speculative rejection sampling with a residual draw
+ *   dflash2_verify_reject_head  the same from the target's hidden states,
+ *                          with its LM head fused in (logits never stored)
  *
  * Sources (the pages that define the operations; cited by title/section):
  *   [KDP]  "DFlash 2: Keep Drafting Parallel" (Inco AI blog; zh-CN mirror
@@ -295,7 +297,7 @@ int dflash2_verify_greedy_noalloc(const void* target_logits, int dt, int64_t voc
  *   emb  [vocab, d] bf16   the target's LM head rows (emb_dt = DF2_BF16)
  *   path_tok [B, T]; accept_len [B]; out_tok [B, T+1] as in
  *   dflash2_verify_greedy.
- * Limits: d % 64 == 0, d <= 65536, 1 <= T <= 63, B * (T + 1) rows.
+ * Limits: d % 64 == 0, d <= 65536, 1 <= T <= 63, B <= 16384.
  * ws: per-token-range argmax keys, dflash2_verify_greedy_head_workspace_bytes.
  * ------------------------------------------------------------------------ */
 size_t dflash2_verify_greedy_head_workspace_bytes(int B, int T, int64_t vocab, int d);
@@ -332,6 +334,33 @@ int dflash2_verify_reject(const void* target_logits, int dt, int64_t vocab, cons
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Rejection sampling with the target's LM head fused in: the rule of
+ * dflash2_verify_reject ([KDP] "A lightweight path selector"; [WC]
+ * "輸出完全一致") on the logits
+ *   Z[b, t, v] = sum_k h[b, t, k] * emb[v, k]  (bf16 products, fp32 sums)
+ * of the shared LM head ([163], paragraph before the three-step pipeline),
+ * which are reduced to per-128-token softmax partials on the fly and never
+ * stored.  The residual draw finds its 128-token block from those partials
+ * (the block's mass less min(p, q~) of its candidates) and recomputes that
+ * block's 128 logits of row n (fp32 dot products, another summation order
+ * than the matrix-core pass: a draw that falls within about 1e-6 of a
+ * boundary may come out on its other side).
+ *   h    [B, T+1, d] bf16; emb [vocab, d] bf16 (emb_dt = DF2_BF16), both
+ *        16-byte aligned
+ *   path_tok, path_rank [B, T]; cand_idx [B, T, K]; q [B, T, K]; seed_dev,
+ *   b0, accept_len, out_tok, temperature: as in dflash2_verify_reject.
+ * Limits: d % 64 == 0, d <= 65536, 1 <= T <= 63, 1 <= K <= 16, B <= 16384.
+ * ws: block partials [B * (T+1), ceil(vocab / 128)] of 16 bytes plus small
+ * per-row and per-request records, dflash2_verify_reject_head_workspace_bytes.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_verify_reject_head_workspace_bytes(int B, int T, int64_t vocab, int d, int K);
+int dflash2_verify_reject_head(const void* h, const void* emb, int emb_dt, int64_t vocab, int d,
+                               const int32_t* path_tok, const int32_t* path_rank, const int32_t* cand_idx,
+                               const float* q, int B, int T, int K, float temperature, const uint64_t* seed_dev,
+                               int b0, int32_t* accept_len, int32_t* out_tok, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Philox4x64-10 words as the sampling steps above draw them (Salmon et al.,
  * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11): for each i,
  * out[4i..4i+3] = Philox4x64-10(key = (seed, 0), counter = (t[i], b[i], 0, 0)).
@@ -347,7 +376,10 @@ int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t
  * stream-side overhead), for at most max_launches launches.  Tags:
  *   "topk_chunk", "topk_merge", "project_gemm", "pair_epilogue", "path",
  *   "argmax_part", "greedy_final", "sumexp_part", "reject_decide",
- *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue", "philox".
+ *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue", "philox",
+ *   "lmhead_topk", "lmhead_merge", "head_argmax", "greedy_head_final",
+ *   "head_stats", "head_row_reduce", "head_decide", "head_block_logits",
+ *   "head_draw".
  * dflash2_profile_stop waits for the recorded events, writes up to `max`
  * per-launch durations in milliseconds to ms (host) and their count to *n,
  * and disarms.  Not for use during graph capture.  Events are created on

@@ -110,6 +110,10 @@ static int run(int B, int T, int K, int V, int d, int r) {
   double* mg = (double*)malloc(sizeof(double) * (size_t)B * (T + 1));
   CHECK(oracle_verify_greedy_head(ht, emb, V, d, ptok, B, T, acc, out, am, mg));
   CHECK(oracle_verify_greedy_head(ht, emb, V, d, ptok, B, T, acc, out, NULL, NULL));
+  CHECK(oracle_verify_reject_head(ht, emb, V, d, ptok, prank, idx, q, B, T, K, 1.0, 7, bids, acc, out, ma, ms,
+                                  &fb));
+  CHECK(oracle_verify_reject_head(ht, emb, V, d, ptok, prank, idx, q, B, T, K, 0.6, 8, NULL, acc, out, NULL,
+                                  NULL, NULL));
   free(logits); free(idx); free(val); free(emb); free(h); free(wa); free(wb); free(wh); free(last);
   free(proj); free(S); free(al); free(ac); free(bc); free(hh); free(prank); free(ptok); free(q);
   free(pscore); free(margin); free(bids); free(target); free(acc); free(out); free(am); free(ma);

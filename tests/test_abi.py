@@ -89,6 +89,30 @@ def test_verify_greedy_head_validation():
     assert f(None, None, 1, 151936, 5120, None, 0, 15, None, None, None, 0, None) == df2.DF2_OK
 
 
+def test_verify_reject_head_validation():
+    L = df2.lib()
+    need = df2.dflash2_verify_reject_head_workspace_bytes(32, 15, 151936, 5120, 16)
+    # block partials of every row and 128-token block dominate the workspace
+    assert need >= 32 * 16 * ((151936 + 127) // 128) * 16
+    f = L.dflash2_verify_reject_head
+    a = lambda **kw: [kw.get("h", FAKE), FAKE, kw.get("dt", 1), 151936, kw.get("d", 5120), FAKE, FAKE, FAKE,
+                      FAKE, kw.get("B", 32), kw.get("T", 15), kw.get("K", 16), kw.get("tau", 1.0), FAKE,
+                      kw.get("b0", 0), FAKE, FAKE, FAKE, kw.get("ws", need), None]
+    assert f(*a(dt=0)) == df2.DF2_ERR_DTYPE
+    assert f(*a(tau=0.0)) == df2.DF2_ERR_UNSUPPORTED
+    assert f(*a(tau=float("inf"))) == df2.DF2_ERR_UNSUPPORTED
+    assert f(*a(d=96)) == df2.DF2_ERR_SHAPE
+    assert f(*a(T=64)) == df2.DF2_ERR_SHAPE
+    assert f(*a(K=17)) == df2.DF2_ERR_SHAPE
+    assert f(*a(B=16385)) == df2.DF2_ERR_SHAPE
+    assert f(*a(b0=-1)) == df2.DF2_ERR_SHAPE
+    assert f(*a(b0=2 ** 31 - 32)) == df2.DF2_ERR_SHAPE
+    assert f(*a(h=None)) == df2.DF2_ERR_NULL
+    assert f(*a(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+    assert f(None, None, 1, 151936, 5120, None, None, None, None, 0, 15, 16, 1.0, None, 0, None, None, None, 0,
+             None) == df2.DF2_OK
+
+
 def test_pair_scores_validation():
     L = df2.lib()
     args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, FAKE, kw.get("edt", 1), 151936, FAKE, FAKE,
