@@ -140,8 +140,8 @@ def cold_replays(cyc, n, evict):
 def heads_leg(dev, steps):
     """The fused LM-head kernels at the benchmark's shapes: the drafter's
     top-16 from its hidden states (dflash2_lm_head_topk; logits h E^T never
-    stored) and greedy verification from the target's hidden states
-    (dflash2_verify_greedy_head).  Per call: HIP events around `steps`
+    stored) and greedy and rejection verification from the target's hidden
+    states (dflash2_verify_greedy_head, dflash2_verify_reject_head).  Per call: HIP events around `steps`
     back-to-back calls; per kernel: the library's timing hook.  MFMA
     fraction = 2 rows V d flops per call against the dense bf16 peak."""
     import torch
@@ -167,10 +167,23 @@ def heads_leg(dev, steps):
         otok = torch.empty((w.B, w.T + 1), dtype=torch.int32, device=dev)
         wsv = torch.empty(max(1, df2.dflash2_verify_greedy_head_workspace_bytes(w.B, w.T, V, d)),
                           dtype=torch.uint8, device=dev)
+        # rejection verification: 16 candidates per position, q uniform over
+        # them, the drafted token one of them
+        cand = torch.randint(0, V, (w.B, w.T, 16), generator=g, dtype=torch.int32).to(dev)
+        qq = torch.full((w.B, w.T, 16), 1.0 / 16, dtype=torch.float32, device=dev)
+        rank = torch.randint(0, 16, (w.B, w.T), generator=g, dtype=torch.int32).to(dev)
+        rpath = torch.gather(cand, 2, rank.long()[..., None])[..., 0].contiguous()
+        seed = torch.tensor([7], dtype=torch.int64, device=dev)
+        wsr = torch.empty(max(1, df2.dflash2_verify_reject_head_workspace_bytes(w.B, w.T, V, d, 16)),
+                          dtype=torch.uint8, device=dev)
         calls = {"lm_head_topk": (lambda: df2.dflash2_lm_head_topk(h, E, 16, idx, val, wsb), rows,
                                   ("lmhead_topk", "lmhead_merge")),
                  "verify_greedy_head": (lambda: df2.dflash2_verify_greedy_head(ht, E, path, acc, otok, wsv),
-                                        w.B * (w.T + 1), ("head_argmax", "greedy_head_final"))}
+                                        w.B * (w.T + 1), ("head_argmax", "greedy_head_final")),
+                 "verify_reject_head": (lambda: df2.dflash2_verify_reject_head(ht, E, rpath, rank, cand, qq, 1.0,
+                                                                               seed, acc, otok, wsr),
+                                        w.B * (w.T + 1), ("head_stats", "head_row_reduce", "head_decide",
+                                                          "head_block_logits", "head_draw"))}
         res = {}
         for key, (fn, nrows, tags) in calls.items():
             for _ in range(2):
@@ -196,7 +209,7 @@ def heads_leg(dev, steps):
                             mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4),
                             lm_head_read_tbs=round(V * d * 2 / (us * 1e-6) / 1e12, 2))
         out[name] = res
-        del h, idx, val, wsb, ht, path, acc, otok, wsv
+        del h, idx, val, wsb, ht, path, acc, otok, wsv, cand, qq, rank, rpath, seed, wsr
     del E
     torch.cuda.empty_cache()
     return out

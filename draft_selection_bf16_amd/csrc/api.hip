@@ -253,8 +253,7 @@ constexpr int kSmallProjRows = 1024;
 int split_for(const GemmTiling& t, int maxs, int B, int T, int K, int d, int r) {
   const int bm = t.bm, bn = t.bn;
   auto tl = [&](int m, int n) { return ((m + bm - 1) / bm) * ((n + bn - 1) / bn); };
-  const int mc = B * T * K;
-  const int tiles = (r % bn == 0 ? tl(mc, 2 * r) : 2 * tl(mc, r)) + tl(B, r) + tl(B * T, r);
+  const int tiles = tl(B * T * K, r) + tl(B * (T - 1) * K, r) + tl(B, r) + tl(B * T, r);
   int ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks > d / 64 / 4) ks = d / 64 / 4;
   if (ks > maxs) ks = maxs;
@@ -332,57 +331,51 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   float* alast = (float*)((char*)ws + pw.alast);
   float* hg = (float*)((char*)ws + pw.h);
   GemmSeg s[4] = {};
-  // candidates: [A | B] = E[cand] [W_A; W_B]^T
+  // candidates, B half: B = E[cand] W_B^T into columns r .. 2r - 1 of ab
   s[0].x = (const uint16_t*)emb;
   s[0].gather = cand_idx;
   s[0].x_rows = vocab;
   s[0].ldx = d;
   s[0].M = B * T * K;
-  s[0].w0 = (const uint16_t*)w_a;
-  s[0].w1 = (const uint16_t*)w_b;
+  s[0].w0 = s[0].w1 = (const uint16_t*)w_b;
   s[0].n0 = r;
-  s[0].N = 2 * r;
-  s[0].out = ab;
+  s[0].N = r;
+  s[0].out = ab + r;
   s[0].ldo = 2 * r;
   s[0].out_kstride = (int64_t)pw.ab_k;
   s[0].gate = DF2_GATE_IDENTITY;
-  // last verified tokens: A only
+  // candidates, A half: only positions 0 .. T-2 precede another position
+  // (the last block position's A is never read), so the leading (T - 1) K
+  // rows of every request's T K candidates (none when T = 1)
   s[1] = s[0];
-  s[1].gather = last_tok;
-  s[1].M = B;
-  s[1].w1 = (const uint16_t*)w_a;
-  s[1].N = r;
-  s[1].out = alast;
-  s[1].ldo = r;
-  s[1].out_kstride = (int64_t)pw.alast_k;
-  // gate: H = gate(h W_H^T), the gate applied by the epilogue
-  s[2].x = (const uint16_t*)h;
-  s[2].gather = nullptr;
-  s[2].x_rows = (int64_t)B * T;
-  s[2].ldx = d;
-  s[2].M = B * T;
-  s[2].w0 = (const uint16_t*)w_h;
-  s[2].w1 = (const uint16_t*)w_h;
-  s[2].n0 = r;
-  s[2].N = r;
-  s[2].out = hg;
+  s[1].M = B * (T - 1) * K;
+  s[1].grp_rows = (T - 1) * K;
+  s[1].grp_stride = T * K;
+  s[1].w0 = s[1].w1 = (const uint16_t*)w_a;
+  s[1].out = ab;
+  // last verified tokens: A only
+  s[2] = s[0];
+  s[2].gather = last_tok;
+  s[2].M = B;
+  s[2].w0 = s[2].w1 = (const uint16_t*)w_a;
+  s[2].out = alast;
   s[2].ldo = r;
-  s[2].out_kstride = (int64_t)pw.h_k;
-  s[2].gate = DF2_GATE_IDENTITY;
-  // W tiles are 128 rows and may not straddle W_A / W_B: for r not a
-  // multiple of 128 the candidate rows are projected as two problems
-  int nseg = 3;
-  if (r % 128 != 0) {
-    s[3] = s[0];
-    s[0].w1 = s[0].w0;
-    s[0].N = r;
-    s[3].w0 = s[3].w1 = (const uint16_t*)w_b;
-    s[3].n0 = r;
-    s[3].N = r;
-    s[3].out = ab + r;
-    nseg = 4;
-  }
-  hipError_t e = launch_gemm(s, nseg, d, pw.split, proj_tiling(B, T, K, d, r), "project_gemm", stream);
+  s[2].out_kstride = (int64_t)pw.alast_k;
+  // gate: H = gate(h W_H^T), the gate applied by the epilogue
+  s[3].x = (const uint16_t*)h;
+  s[3].gather = nullptr;
+  s[3].x_rows = (int64_t)B * T;
+  s[3].ldx = d;
+  s[3].M = B * T;
+  s[3].w0 = (const uint16_t*)w_h;
+  s[3].w1 = (const uint16_t*)w_h;
+  s[3].n0 = r;
+  s[3].N = r;
+  s[3].out = hg;
+  s[3].ldo = r;
+  s[3].out_kstride = (int64_t)pw.h_k;
+  s[3].gate = DF2_GATE_IDENTITY;
+  hipError_t e = launch_gemm(s, 4, d, pw.split, proj_tiling(B, T, K, d, r), "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, pw.split, (int64_t)pw.ab_k, (int64_t)pw.alast_k,
                                          (int64_t)pw.h_k, gate, cand_val, B, T, K, r, scores, stream),

@@ -78,6 +78,10 @@ struct GemmSeg {
   int64_t ldo;
   int64_t out_kstride;    // elements between K-slice partial outputs
   int gate;               // 0 identity, 1 sigmoid (only when ksplit == 1)
+  // grouped rows (grp_rows > 0): product row m is row
+  // (m / grp_rows) * grp_stride + m % grp_rows of the gather list (or of x)
+  // and of out -- the leading grp_rows of every group of grp_stride rows
+  int grp_rows, grp_stride;
   int tiles_m, tiles_n;   // filled by the launcher
 };
 // Work-group tile BM x BN, LDS stages, waves per work-group.

@@ -95,10 +95,13 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   float* const sout = S_.out;
   const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
   const int gate = S_.gate;
+  const int grows = S_.grp_rows, gstride = S_.grp_stride;
   const int tbegin = Pb.tile_begin[si];
   asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
-               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate),
-               "s"(tbegin));   // one round trip
+               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate), "s"(grows),
+               "s"(gstride), "s"(tbegin));   // one round trip
+  // product row -> row of the gather list / x and of out
+  auto phys = [&](int m) { return grows > 0 ? (m / grows) * gstride + m % grows : m; };
   const int local = tile - tbegin;
   const int m0 = (local / tiles_n) * BM, n0 = (local % tiles_n) * BN;
   const int nkt = K / BK;
@@ -133,7 +136,7 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
 #pragma unroll
   for (int a = 0; a < ALD; ++a) {
     const int m = m0 + 8 * (wave + NW * a) + sub;
-    src[a] = m < M ? m : M - 1;
+    src[a] = phys(m < M ? m : M - 1);
   }
   if (sgather) {
 #pragma unroll
@@ -237,7 +240,7 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
       if (gate)
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = apply_gate(v[e], gate);
-      *(f32x4*)(out + (int64_t)m * ldo + n) = v;
+      *(f32x4*)(out + (int64_t)phys(m) * ldo + n) = v;
     }
   }
 }
@@ -285,6 +288,7 @@ hipError_t gemm::make_problem(const GemmSeg* segs, int nseg, int K, int ksplit, 
     if ((uint64_t)s.x_rows * (uint64_t)s.ldx * 2u > lim) return hipErrorInvalidValue;
     if ((uint64_t)s.N * (uint64_t)K * 2u > lim) return hipErrorInvalidValue;
     if (s.n0 < s.N && s.n0 % bn != 0) return hipErrorInvalidValue;
+    if (s.grp_rows < 0 || (s.grp_rows > 0 && s.grp_stride < s.grp_rows)) return hipErrorInvalidValue;
     s.tiles_m = (s.M + bm - 1) / bm;
     s.tiles_n = (s.N + bn - 1) / bn;
     P.s[P.nseg] = s;

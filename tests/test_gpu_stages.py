@@ -267,7 +267,8 @@ def test_pair_scores_mid_with_intermediates(gate):
     So, inter = oracle.pair_scores(idx, val, last, E, h, wa, wb, wh, gate=gate, intermediates=True)
     worst = close(Sg, So)
     ab, al, hg = _ws_views(wsp, 3, 7, 16, 256, gate)
-    close(ab[..., :256], inter["a_cand"])
+    # A of the last block position is never a predecessor and is not computed
+    close(ab[:, :-1, :, :256], inter["a_cand"][:, :-1])
     close(ab[..., 256:], inter["b_cand"])
     close(al, inter["a_last"])
     close(hg, inter["h"])
