@@ -1,258 +1,6 @@
-// gemm.hip -- bf16 MFMA GEMM (out = gate(X W^T), fp32 accumulation).
-//
-// Used for the rank-r projections of the path selector (A(tok) = W_A E[tok],
-// B(tok) = W_B E[tok], H = gate(W_H h_t); "DFlash 2: Keep Drafting Parallel",
-// section "A lightweight path selector") and for the tap corrections of the
-// two-tap conv (c_t = W x_t; section "A lightweight local convolution").
-// Both operands are K-contiguous rows (X: [M, K], W: [N, K]), so every lane
-// feeds the MFMA with 16 contiguous bytes of one row.
-//
-// Tiling: work-group = 4 or 8 waves (2 x 2 or 2 x 4), tile BM x BN (BM = 64
-// or 128; BN = 128 in the instantiations), K-tiles of 64.  X rows may be
-// gathered through an index list (candidate tokens into the embedding table).  Up to four independent
-// problems share one launch.  An optional K split writes per-slice partial
-// products (no atomics; the consumer sums the slices in a fixed order).
-// Work-groups are renumbered so that each XCD runs a contiguous range of
-// tiles (the N-tiles of one M-block then share that XCD's L2 for X), or,
-// with a K split, so that the slice index varies fastest.
-// This file is compiled with the VGPR form of the MFMA instructions: the
-// accumulators live in ordinary VGPRs, which keeps the accumulate chain free
-// of register copies.
-#include "df2_device.h"
-#include "df2_internal.h"
-#include "mfma_tile.h"
-
-namespace df2 {
-
-// dynamic LDS of the GEMM (declared outside any anonymous namespace: an
-// extern with internal linkage keeps the host-side launch stub from being
-// emitted)
-extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-
-namespace gemm {
-
-using mfma::BK;
-constexpr int kXcds = 8;
-
-constexpr int kMaxSeg = 4;
-
-// The scalars every work-group needs first lead the kernel arguments, so
-// that one scalar load fetches them all (the segment's fields follow in a
-// second round trip, once the segment index is known).
-struct Problem {
-  int ksplit;  // slice s covers K-tiles [s nkt / ksplit, (s + 1) nkt / ksplit)
-  int K;       // full reduction length; W rows are K apart
-  int nseg;
-  int tile_begin[kMaxSeg + 1];   // entries from nseg on hold the tile total
-  GemmSeg s[kMaxSeg];
-};
-
-__device__ __forceinline__ float apply_gate(float z, int gate) {
-  return gate == 1 ? 1.0f / (1.0f + expf(-z)) : z;
-}
-
-// The K-tiles are copied by direct buffer-to-LDS loads (no register
-// staging) into S LDS stages, S - 1 of them in flight while the MFMAs of the
-// current one run; one barrier per K-tile.  The stage layout, the chunk
-// swizzle and the load helper are in mfma_tile.h.
-using mfma::load_lds16;
-using mfma::swz;
-using mfma::vmcnt_imm;
-
-// The tile of work-group `bid` of a grid of `nb` (the body of the GEMM
-// kernel; NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8)).
-template <int BM, int BN, int S, int NW>
-__device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
-  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
-  static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
-  constexpr int kThreads = NW * 64;
-  constexpr int WCOL = NW / 2;                  // waves along N
-  constexpr int WM = BM / 2, WN = BN / WCOL;
-  constexpr int FM = WM / 16, FN = WN / 16;
-  constexpr int ALD = BM / (8 * NW), BLD = BN / (8 * NW);   // load instructions per wave per stage
-  constexpr int LPW = ALD + BLD;
-  constexpr int STAGE = (BM + BN) * BK * 2;     // bytes
-
-  // Every kernel-argument scalar is read up front and every choice below is
-  // a select, not a branch: the scalar loads then go out together instead
-  // of one dependent round trip each.
-  const int ksplit = Pb.ksplit, K = Pb.K;
-  const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
-  asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
-  const int full = nb / kXcds * kXcds;
-  const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
-  const int tile = ksplit == 1 ? bx : bid / ksplit;
-  const int ks = ksplit == 1 ? 0 : bid % ksplit;
-  // tile_begin[i] for i >= nseg is the tile total
-  const int si = (tile >= tb1 ? 1 : 0) + (tile >= tb2 ? 1 : 0) + (tile >= tb3 ? 1 : 0);
-  static_assert(kMaxSeg == 4, "segment index select");
-  const GemmSeg& S_ = Pb.s[si];
-  const uint16_t* sx = S_.x;
-  const int32_t* sgather = S_.gather;
-  const int x_rows = S_.x_rows, ldx = S_.ldx, M = S_.M, N = S_.N, sn0 = S_.n0;
-  const uint16_t *w0 = S_.w0, *w1 = S_.w1;
-  const int tiles_n = S_.tiles_n;
-  float* const sout = S_.out;
-  const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
-  const int gate = S_.gate;
-  const int grows = S_.grp_rows, gstride = S_.grp_stride;
-  const int tbegin = Pb.tile_begin[si];
-  asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
-               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate), "s"(grows),
-               "s"(gstride), "s"(tbegin));   // one round trip
-  // product row -> row of the gather list / x and of out
-  auto phys = [&](int m) { return grows > 0 ? (m / grows) * gstride + m % grows : m; };
-  const int local = tile - tbegin;
-  const int m0 = (local / tiles_n) * BM, n0 = (local % tiles_n) * BN;
-  const int nkt = K / BK;
-  const int kt0 = ks * nkt / ksplit, kt1 = (ks + 1) * nkt / ksplit;
-  const int k_begin = kt0 * BK;
-  const int nk = kt1 - kt0;
-  const int wave = wave_id(), lane = lane_id();
-  const int wm = wave / WCOL, wn = wave % WCOL;
-
-  const bool from_w0 = n0 < sn0;
-  const uint16_t* wbase = from_w0 ? w0 + (int64_t)n0 * K : w1 + (int64_t)(n0 - sn0) * K;
-  const int wrows = (from_w0 ? (sn0 < N ? sn0 : N) : N) - n0;
-  // in 64 bits: rows x ldx x 2 exceeds INT_MAX for tables over 2 GiB (the
-  // launcher keeps it under 2^32 - 2K - 16)
-  const uint32_t xbytes = (uint32_t)((uint64_t)(uint32_t)x_rows * (uint64_t)(uint32_t)ldx * 2u);
-  const uint32_t wbytes = (uint32_t)((int64_t)wrows * K * 2);
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc((void*)sx, 0, (int)xbytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, (int)wbytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t xnone = __builtin_amdgcn_make_buffer_rsrc((void*)sx, 0, 0, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t wnone = __builtin_amdgcn_make_buffer_rsrc((void*)wbase, 0, 0, kBufferWord3);
-  // out of range for the whole K walk, whether or not the range check adds
-  // the scalar offset (the launcher keeps bytes + 2K + 16 <= 2^32)
-  const uint32_t kOut = 0xFFFFFFF0u - (uint32_t)K * 2u;
-
-  // lane offsets of this wave's load instructions: instruction a fills rows
-  // 8 (wave + NW a) .. + 7 of the X tile, b likewise of the W tile.  X rows
-  // come through the gather list when there is one: its entries are loaded
-  // unconditionally (clamped row) so that all of them are in flight at once.
-  const int sub = lane >> 3, slot = lane & 7;
-  uint32_t xo[ALD], wo[BLD];
-  int src[ALD];
-#pragma unroll
-  for (int a = 0; a < ALD; ++a) {
-    const int m = m0 + 8 * (wave + NW * a) + sub;
-    src[a] = phys(m < M ? m : M - 1);
-  }
-  if (sgather) {
-#pragma unroll
-    for (int a = 0; a < ALD; ++a) src[a] = sgather[src[a]];
-  }
-#pragma unroll
-  for (int a = 0; a < ALD; ++a) {
-    const int row = 8 * (wave + NW * a) + sub;
-    const int c = slot ^ swz(row);
-    const bool ok = m0 + row < M && src[a] >= 0 && src[a] < x_rows;
-    xo[a] = ok ? (uint32_t)(((int64_t)src[a] * ldx + k_begin + c * 8) * 2) : kOut;
-  }
-#pragma unroll
-  for (int b = 0; b < BLD; ++b) {
-    const int row = 8 * (wave + NW * b) + sub;
-    const int c = slot ^ swz(row);
-    wo[b] = row < wrows ? (uint32_t)(((int64_t)row * K + k_begin + c * 8) * 2) : kOut;
-  }
-  // K-tile t goes to stage t % S; tiles past the end read nothing (empty
-  // resources: zeros, no traffic) so that every step issues the same loads
-  auto issue = [&](int t) {
-    const bool in = t < nk;
-    uint8_t* sb = dyn_lds + (t % S) * STAGE;
-    const int so = __builtin_amdgcn_readfirstlane(in ? t * BK * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rx = in ? xres : xnone, rw = in ? wres : wnone;
-#pragma unroll
-    for (int a = 0; a < ALD; ++a)
-      load_lds16(rx, sb + (wave + NW * a) * 8 * 128, xo[a], so);
-#pragma unroll
-    for (int b = 0; b < BLD; ++b)
-      load_lds16(rw, sb + BM * 128 + (wave + NW * b) * 8 * 128, wo[b], so);
-  };
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int fr = lane & 15, fq = lane >> 4;
-  // fragment byte offsets inside a stage (rows fixed per lane, chunk 4 s + fq)
-  int ao[FM][2], bo[FN][2];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = wm * WM + i * 16 + fr;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) ao[i][s2] = r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
-  }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int r = wn * WN + j * 16 + fr;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) bo[j][s2] = BM * 128 + r * 128 + 16 * ((4 * s2 + fq) ^ swz(r));
-  }
-
-#pragma unroll
-  for (int t = 0; t < S - 1; ++t) issue(t);
-  for (int t = 0; t < nk; ++t) {
-    // this wave's copies of tile t are done; the barrier makes everyone's
-    // visible and frees the stage read in step t - 1 for tile t + S - 1
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPW));
-    __builtin_amdgcn_s_barrier();
-    issue(t + S - 1);
-    const uint8_t* st = dyn_lds + (t % S) * STAGE;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8 a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)(st + ao[i][s2]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)(st + bo[j][s2]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-
-  // Output through LDS: the accumulators (lane holds column lane & 15, rows
-  // 4 (lane >> 4) + e of each 16 x 16 block) go to a row-major tile (rows
-  // padded to BN + 4 floats), then whole rows leave with 16-byte stores.
-  constexpr int OLD = BN + 4;
-  static_assert(BM * OLD * 4 <= S * STAGE, "output tile must fit the stages");
-  float* so = (float*)dyn_lds;
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();   // every wave is done with the stages
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        so[(wm * WM + i * 16 + fq * 4 + e) * OLD + wn * WN + j * 16 + fr] = acc[i][j][e];
-  __syncthreads();
-  float* out = sout + (int64_t)ks * out_kstride;
-  for (int q = threadIdx.x; q < BM * BN / 4; q += kThreads) {
-    const int r = q / (BN / 4), c = (q % (BN / 4)) * 4;
-    const int m = m0 + r, n = n0 + c;
-    if (m < M && n < N) {   // N % 4 == 0: a group of 4 is all in or all out
-      f32x4 v = *(const f32x4*)&so[r * OLD + c];
-      if (gate)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = apply_gate(v[e], gate);
-      *(f32x4*)(out + (int64_t)phys(m) * ldo + n) = v;
-    }
-  }
-}
-
-// Fill P for up to kMaxSeg problems (hipErrorInvalidValue for shapes the
-// kernel does not take), and raise a kernel's dynamic-LDS limit once.
-hipError_t make_problem(const GemmSeg* segs, int nseg, int K, int ksplit, int bm, int bn, Problem& P,
-                        int& tiles);
-hipError_t allow_lds(const void* fn, int bytes, bool& done);
-
-}  // namespace gemm
-}  // namespace df2
+// gemm.hip -- launcher of the bf16 MFMA GEMM (the tile itself is in
+// gemm_tile.h): one work-group per tile and K slice.
+#include "gemm_tile.h"
 
 namespace df2 {
 using namespace gemm;
