@@ -37,6 +37,7 @@ EXPORTS = [
     "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_noalloc_max_bytes",
     "dflash2_verify_greedy_head_workspace_bytes", "dflash2_verify_greedy_head",
     "dflash2_verify_reject_head_workspace_bytes", "dflash2_verify_reject_head",
+    "dflash2_cycle_fused_workspace_bytes", "dflash2_cycle_fused_init", "dflash2_cycle_fused",
     "dflash2_philox4x64", "dflash2_profile_start", "dflash2_profile_stop",
 ]
 
@@ -93,6 +94,11 @@ def lib():
         L.dflash2_verify_reject_head_workspace_bytes.argtypes = [I, I, I64, I, I]
         L.dflash2_verify_reject_head_workspace_bytes.restype = SZ
         L.dflash2_verify_reject_head.argtypes = [P, P, I, I64, I, P, P, P, P, I, I, I, F, P, I, P, P, P, SZ, P]
+        L.dflash2_cycle_fused_workspace_bytes.argtypes = [I, I, I, I64, I, I]
+        L.dflash2_cycle_fused_workspace_bytes.restype = SZ
+        L.dflash2_cycle_fused_init.argtypes = [I, I, I, I64, I, I, P, SZ, P]
+        L.dflash2_cycle_fused.argtypes = [P, I, P, I, I64, P, I, P, P, P, P, P, I, I, I, I, I, I, I,
+                                          P, P, P, P, P, P, P, P, P, P, P, SZ, P]
         L.dflash2_verify_greedy_noalloc_max_bytes.restype = SZ
         L.dflash2_philox4x64.argtypes = [P, P, P, I, P, P]
         L.dflash2_profile_start.argtypes = [C.c_char_p, I]
@@ -104,6 +110,7 @@ def lib():
                      "dflash2_path_viterbi",
                      "dflash2_dynconv2", "dflash2_verify_greedy", "dflash2_verify_reject",
                      "dflash2_verify_greedy_noalloc", "dflash2_verify_greedy_head", "dflash2_verify_reject_head",
+                     "dflash2_cycle_fused_init", "dflash2_cycle_fused",
                      "dflash2_philox4x64"):
             getattr(L, name).restype = I
         _lib = L
@@ -290,6 +297,33 @@ def dflash2_verify_reject_head(h, emb, path_tok, path_rank, cand_idx, q, tempera
                                             _ptr(cand_idx), _ptr(q), B, T1 - 1, K, float(temperature),
                                             _ptr(seed_dev), int(b0), _ptr(accept_len), _ptr(out_tok), _ptr(ws),
                                             _bytes(ws), _stream(stream)), "dflash2_verify_reject_head")
+
+
+def dflash2_cycle_fused_workspace_bytes(B: int, T: int, K: int, vocab: int, d: int, r: int) -> int:
+    return int(lib().dflash2_cycle_fused_workspace_bytes(B, T, K, vocab, d, r))
+
+
+def dflash2_cycle_fused_init(B: int, T: int, K: int, vocab: int, d: int, r: int, ws, stream=None):
+    """Zero the control words of a fresh dflash2_cycle_fused workspace."""
+    _check(lib().dflash2_cycle_fused_init(B, T, K, vocab, d, r, _ptr(ws), _bytes(ws), _stream(stream)),
+           "dflash2_cycle_fused_init")
+
+
+def dflash2_cycle_fused(logits, target, emb, h, w_a, w_b, w_h, last_tok, path_mode, cand_idx, cand_val, scores,
+                        path_rank, path_tok, q, path_score, accept_len, out_tok, status, ws,
+                        gate=DF2_GATE_IDENTITY, stream=None):
+    """top-K, pair scores, path (VITERBI / GREEDY) and greedy verification of
+    a small batch in one launch; status [1] int32 receives 0 on success."""
+    B, T, V = logits.shape
+    K = cand_idx.shape[-1]
+    d = emb.shape[1]
+    r = w_a.shape[0]
+    _check(lib().dflash2_cycle_fused(_ptr(logits), _dt(logits), _ptr(target), _dt(target), V, _ptr(emb), _dt(emb),
+                                     _ptr(h), _ptr(w_a), _ptr(w_b), _ptr(w_h), _ptr(last_tok), B, T, K, d, r,
+                                     int(gate), int(path_mode), _ptr(cand_idx), _ptr(cand_val), _ptr(scores),
+                                     _ptr(path_rank), _ptr(path_tok), _ptr(q), _ptr(path_score), _ptr(accept_len),
+                                     _ptr(out_tok), _ptr(status), _ptr(ws), _bytes(ws), _stream(stream)),
+           "dflash2_cycle_fused")
 
 
 def dflash2_verify_greedy_noalloc_max_bytes() -> int:

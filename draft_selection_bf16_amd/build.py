@@ -34,7 +34,8 @@ FLAGS = [
 # per-source extras: the GEMM keeps its MFMA accumulators in ordinary VGPRs
 # (its loop then needs no accumulator copies)
 EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "lmhead.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+         "lmhead.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "cycle_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

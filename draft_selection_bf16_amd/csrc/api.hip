@@ -10,6 +10,7 @@
 
 #include "dflash2.h"
 #include "df2_internal.h"
+#include "cycle_fused.h"
 
 using namespace df2;
 
@@ -298,39 +299,14 @@ PairWs pair_ws(int B, int T, int K, int d, int r) {
   w.total = off;
   return w;
 }
-}  // namespace
-
-size_t dflash2_pair_scores_workspace_bytes(int B, int T, int K, int d, int r) {
-  if (B <= 0 || T <= 0 || K <= 0 || r <= 0 || d < 64) return 0;
-  return pair_ws(B, T, K, d, r).total;
-}
-
-int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
-                        const void* emb, int emb_dt, int64_t vocab, const void* h, const void* w_a,
-                        const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
-                        int gate, float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
-  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_pair_scores: embedding table must be BF16");
-  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_pair_scores: B %d", B);
-  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_pair_scores: T %d not in [1, %d]", T, kMaxT);
-  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_pair_scores: K %d not in [1, 16]", K);
-  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: d %d is not a positive multiple of 64", d);
-  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: r %d not a multiple of 16 in [16, 256]", r);
-  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores: vocab %lld", (long long)vocab);
-  REQUIRE((uint64_t)vocab * (uint64_t)d * 2u < (1ull << 32), DF2_ERR_UNSUPPORTED,
-          "dflash2_pair_scores: embedding table of %lld x %d bf16 is 4 GiB or more", (long long)vocab, d);
-  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores: gate %d", gate);
-  if (B == 0) return DF2_OK;
-  REQUIRE(cand_idx && cand_val && last_tok && emb && h && w_a && w_b && w_h && scores, DF2_ERR_NULL,
-          "dflash2_pair_scores: null pointer argument");
-  REQUIRE(aligned16(emb) && aligned16(h) && aligned16(w_a) && aligned16(w_b) && aligned16(w_h),
-          DF2_ERR_SHAPE, "dflash2_pair_scores: emb/h/w_* must be 16-byte aligned");
-  PairWs pw = pair_ws(B, T, K, d, r);
-  REQUIRE(ws && ws_bytes >= pw.total, DF2_ERR_WORKSPACE, "dflash2_pair_scores: workspace %zu < %zu bytes",
-          ws_bytes, pw.total);
-  float* ab = (float*)((char*)ws + pw.ab);
-  float* alast = (float*)((char*)ws + pw.alast);
-  float* hg = (float*)((char*)ws + pw.h);
-  GemmSeg s[4] = {};
+// The projection problems of the pair scores, in the order [B(cand),
+// A(cand), A(last), H]: candidates' B = E[cand] W_B^T into columns r .. 2r-1
+// of ab, their A (positions 0 .. T-2 only) into columns 0 .. r-1, A of the
+// last verified tokens, and H = h W_H^T (the gate is applied by the epilogue).
+void proj_segments(const int32_t* cand_idx, const int32_t* last_tok, const void* emb, int64_t vocab, const void* h,
+                   const void* w_a, const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
+                   const PairWs& pw, float* ab, float* alast, float* hg, GemmSeg* s) {
+  for (int i = 0; i < 4; ++i) s[i] = GemmSeg{};
   // candidates, B half: B = E[cand] W_B^T into columns r .. 2r - 1 of ab
   s[0].x = (const uint16_t*)emb;
   s[0].gather = cand_idx;
@@ -375,11 +351,172 @@ int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const in
   s[3].ldo = r;
   s[3].out_kstride = (int64_t)pw.h_k;
   s[3].gate = DF2_GATE_IDENTITY;
+}
+}  // namespace
+
+size_t dflash2_pair_scores_workspace_bytes(int B, int T, int K, int d, int r) {
+  if (B <= 0 || T <= 0 || K <= 0 || r <= 0 || d < 64) return 0;
+  return pair_ws(B, T, K, d, r).total;
+}
+
+int dflash2_pair_scores(const int32_t* cand_idx, const float* cand_val, const int32_t* last_tok,
+                        const void* emb, int emb_dt, int64_t vocab, const void* h, const void* w_a,
+                        const void* w_b, const void* w_h, int B, int T, int K, int d, int r,
+                        int gate, float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(emb_dt == DF2_BF16, DF2_ERR_DTYPE, "dflash2_pair_scores: embedding table must be BF16");
+  REQUIRE(B >= 0 && B <= kMaxB, DF2_ERR_SHAPE, "dflash2_pair_scores: B %d", B);
+  REQUIRE(T >= 1 && T <= kMaxT, DF2_ERR_SHAPE, "dflash2_pair_scores: T %d not in [1, %d]", T, kMaxT);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_pair_scores: K %d not in [1, 16]", K);
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: d %d is not a positive multiple of 64", d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE, "dflash2_pair_scores: r %d not a multiple of 16 in [16, 256]", r);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_pair_scores: vocab %lld", (long long)vocab);
+  REQUIRE((uint64_t)vocab * (uint64_t)d * 2u < (1ull << 32), DF2_ERR_UNSUPPORTED,
+          "dflash2_pair_scores: embedding table of %lld x %d bf16 is 4 GiB or more", (long long)vocab, d);
+  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_pair_scores: gate %d", gate);
+  if (B == 0) return DF2_OK;
+  REQUIRE(cand_idx && cand_val && last_tok && emb && h && w_a && w_b && w_h && scores, DF2_ERR_NULL,
+          "dflash2_pair_scores: null pointer argument");
+  REQUIRE(aligned16(emb) && aligned16(h) && aligned16(w_a) && aligned16(w_b) && aligned16(w_h),
+          DF2_ERR_SHAPE, "dflash2_pair_scores: emb/h/w_* must be 16-byte aligned");
+  PairWs pw = pair_ws(B, T, K, d, r);
+  REQUIRE(ws && ws_bytes >= pw.total, DF2_ERR_WORKSPACE, "dflash2_pair_scores: workspace %zu < %zu bytes",
+          ws_bytes, pw.total);
+  float* ab = (float*)((char*)ws + pw.ab);
+  float* alast = (float*)((char*)ws + pw.alast);
+  float* hg = (float*)((char*)ws + pw.h);
+  GemmSeg s[4];
+  proj_segments(cand_idx, last_tok, emb, vocab, h, w_a, w_b, w_h, B, T, K, d, r, pw, ab, alast, hg, s);
   hipError_t e = launch_gemm(s, 4, d, pw.split, proj_tiling(B, T, K, d, r), "project_gemm", stream);
   if (e != hipSuccess) return hip_status(e, "dflash2_pair_scores (projection)");
   return hip_status(launch_pair_epilogue(ab, alast, hg, pw.split, (int64_t)pw.ab_k, (int64_t)pw.alast_k,
                                          (int64_t)pw.h_k, gate, cand_val, B, T, K, r, scores, stream),
                     "dflash2_pair_scores (epilogue)");
+}
+
+// ------------------------------------------------------------------ fused small-batch cycle
+namespace {
+struct FusedWs {
+  TopkPlan tp;
+  int vsplits;
+  int64_t vchunk;
+  PairWs pw;
+  size_t off_tpart, off_pair, off_vpart, off_ctr, total;
+};
+FusedWs fused_ws(int B, int T, int K, int64_t vocab, int d, int r) {
+  FusedWs w;
+  w.tp = fused_topk_plan((int64_t)B * T, vocab, K);
+  w.vsplits = fused_verify_splits(B, T, vocab, w.vchunk);
+  w.pw = pair_ws(B, T, K, d, r);
+  size_t off = 0;
+  w.off_tpart = off;
+  off += align256(w.tp.ws_bytes);
+  w.off_pair = off;
+  off += align256(w.pw.total);
+  w.off_vpart = off;
+  off += align256((size_t)B * (T + 1) * w.vsplits * sizeof(uint64_t));
+  w.off_ctr = off;
+  off += align256(fused_ctr_bytes(B * T));
+  w.total = off;
+  return w;
+}
+constexpr int kMaxFusedRows = 1024;   // B * T
+}  // namespace
+
+size_t dflash2_cycle_fused_workspace_bytes(int B, int T, int K, int64_t vocab, int d, int r) {
+  if (B <= 0 || T <= 0 || K <= 0 || vocab <= 0 || d < 64 || r <= 0) return 0;
+  return fused_ws(B, T, K, vocab, d, r).total;
+}
+
+int dflash2_cycle_fused_init(int B, int T, int K, int64_t vocab, int d, int r, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  REQUIRE(B >= 0 && T >= 1 && T <= kMaxT && (int64_t)B * T <= kMaxFusedRows && K >= 1 && K <= 16 && d >= 64 &&
+              r >= 16 && vocab >= 1 && vocab < kMaxVocab,
+          DF2_ERR_SHAPE, "dflash2_cycle_fused_init: shape B %d T %d K %d d %d r %d", B, T, K, d, r);
+  if (B == 0) return DF2_OK;
+  FusedWs w = fused_ws(B, T, K, vocab, d, r);
+  REQUIRE(ws && ws_bytes >= w.total, DF2_ERR_WORKSPACE, "dflash2_cycle_fused_init: workspace %zu < %zu bytes",
+          ws_bytes, w.total);
+  return hip_status(launch_fused_ctr_clear((char*)ws + w.off_ctr, B * T, stream), "dflash2_cycle_fused_init");
+}
+
+int dflash2_cycle_fused(const void* logits, int logits_dt, const void* target, int target_dt, int64_t vocab,
+                        const void* emb, int emb_dt, const void* h, const void* w_a, const void* w_b,
+                        const void* w_h, const int32_t* last_tok, int B, int T, int K, int d, int r, int gate,
+                        int path_mode, int32_t* cand_idx, float* cand_val, float* scores, int32_t* path_rank,
+                        int32_t* path_tok, float* q, float* path_score, int32_t* accept_len, int32_t* out_tok,
+                        int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(logits_dt == DF2_BF16 && target_dt == DF2_BF16 && emb_dt == DF2_BF16, DF2_ERR_DTYPE,
+          "dflash2_cycle_fused: logits, target logits and embedding table must be BF16");
+  REQUIRE(path_mode == DF2_PATH_VITERBI || path_mode == DF2_PATH_GREEDY, DF2_ERR_UNSUPPORTED,
+          "dflash2_cycle_fused: path mode %d (VITERBI or GREEDY)", path_mode);
+  REQUIRE(gate == DF2_GATE_IDENTITY || gate == DF2_GATE_SIGMOID, DF2_ERR_UNSUPPORTED, "dflash2_cycle_fused: gate %d",
+          gate);
+  REQUIRE(B >= 0 && T >= 1 && T <= kMaxT && (int64_t)B * T <= kMaxFusedRows, DF2_ERR_SHAPE,
+          "dflash2_cycle_fused: B %d T %d (1 <= T <= %d, B T <= %d)", B, T, kMaxT, kMaxFusedRows);
+  REQUIRE(K >= 1 && K <= 16, DF2_ERR_SHAPE, "dflash2_cycle_fused: K %d not in [1, 16]", K);
+  REQUIRE(d >= 64 && d % 64 == 0, DF2_ERR_SHAPE, "dflash2_cycle_fused: d %d is not a positive multiple of 64", d);
+  REQUIRE(r >= 16 && r <= 256 && r % 16 == 0, DF2_ERR_SHAPE,
+          "dflash2_cycle_fused: r %d not a multiple of 16 in [16, 256]", r);
+  REQUIRE(vocab >= 1 && vocab < kMaxVocab, DF2_ERR_SHAPE, "dflash2_cycle_fused: vocab %lld", (long long)vocab);
+  REQUIRE((uint64_t)vocab * (uint64_t)d * 2u < (1ull << 32), DF2_ERR_UNSUPPORTED,
+          "dflash2_cycle_fused: embedding table of %lld x %d bf16 is 4 GiB or more", (long long)vocab, d);
+  if (B == 0) return DF2_OK;
+  REQUIRE(logits && target && emb && h && w_a && w_b && w_h && last_tok && cand_idx && cand_val && scores &&
+              path_rank && path_tok && q && accept_len && out_tok && status,
+          DF2_ERR_NULL, "dflash2_cycle_fused: null pointer argument");
+  REQUIRE(aligned16(emb) && aligned16(h) && aligned16(w_a) && aligned16(w_b) && aligned16(w_h) && aligned16(scores),
+          DF2_ERR_SHAPE, "dflash2_cycle_fused: emb/h/w_*/scores must be 16-byte aligned");
+  FusedWs w = fused_ws(B, T, K, vocab, d, r);
+  REQUIRE(ws && ws_bytes >= w.total, DF2_ERR_WORKSPACE, "dflash2_cycle_fused: workspace %zu < %zu bytes", ws_bytes,
+          w.total);
+  char* base = (char*)ws;
+  float* ab = (float*)(base + w.off_pair + w.pw.ab);
+  float* alast = (float*)(base + w.off_pair + w.pw.alast);
+  float* hg = (float*)(base + w.off_pair + w.pw.h);
+  GemmSeg s[4], f[4];
+  proj_segments(cand_idx, last_tok, emb, vocab, h, w_a, w_b, w_h, B, T, K, d, r, w.pw, ab, alast, hg, s);
+  f[0] = s[2];   // A(last) and H first: they need no candidates
+  f[1] = s[3];
+  f[2] = s[0];
+  f[3] = s[1];
+  FusedArgs a{};
+  a.logits = logits;
+  a.target = target;
+  a.vocab = vocab;
+  a.B = B;
+  a.T = T;
+  a.K = K;
+  a.r = r;
+  a.gate = gate;
+  a.mode = path_mode;
+  a.tsplits = w.tp.splits;
+  a.tchunk = w.tp.chunk;
+  a.tpart = (uint64_t*)(base + w.off_tpart);
+  a.cand_idx = cand_idx;
+  a.cand_val = cand_val;
+  a.P.ksplit = w.pw.split;
+  a.ab = ab;
+  a.alast = alast;
+  a.hg = hg;
+  a.ab_k = (int64_t)w.pw.ab_k;
+  a.alast_k = (int64_t)w.pw.alast_k;
+  a.h_k = (int64_t)w.pw.h_k;
+  a.n0 = (int64_t)B * T * K * 2 * r / 4;
+  a.n1 = (int64_t)B * r / 4;
+  a.n2 = (int64_t)B * T * r / 4;
+  a.scores = scores;
+  a.path_rank = path_rank;
+  a.path_tok = path_tok;
+  a.q = q;
+  a.path_score = path_score;
+  a.vsplits = w.vsplits;
+  a.vchunk = w.vchunk;
+  a.vpart = (uint64_t*)(base + w.off_vpart);
+  a.accept_len = accept_len;
+  a.out_tok = out_tok;
+  a.ctr = (uint32_t*)(base + w.off_ctr);
+  a.status = status;
+  return hip_status(launch_cycle_fused(a, f, d, stream), "dflash2_cycle_fused");
 }
 
 // ------------------------------------------------------------------ per-token tables

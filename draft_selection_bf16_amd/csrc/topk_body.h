@@ -399,11 +399,11 @@ __device__ __forceinline__ void topk_chunk_body(const void* __restrict__ logits,
   // Keep up to 64 keys per wave (no final cut), then filter every wave's
   // keys by two lower bounds on the chunk's 16th best key: the largest
   // published threshold (a value some wave saw at least 16 keys reach) and
-  // the smallest of the waves' second-best keys (the waves' best and second
-  // best are 16 distinct keys).  The 16 best all pass; a few dozen keys
-  // survive at V = 151,936.  Survivors are ranked against each other by all
-  // threads.  With massive ties (more than 512 survivors) every wave first
-  // takes its own 16 best and wave 0 merges the 8 x 16.
+  // the smallest of the waves' (16 / NW)-th best keys (with 8 waves their
+  // second best).  The 16 best all pass; a few dozen keys survive at
+  // V = 151,936.  Survivors are ranked against each other by all threads.
+  // With massive ties (more survivors than threads) every wave first takes
+  // its own 16 best and wave 0 merges the NW x 16.
   flush<E>(F, wave, kWave);
   if (lane == 0) publish(F, wave);
   auto& ssurv = L.ssurv;
@@ -418,15 +418,19 @@ __device__ __forceinline__ void topk_chunk_body(const void* __restrict__ logits,
     keys[i] = s2 < F.cnt ? F.buf[s2] : 0ull;
   }
   {
-    uint64_t m1 = 0ull;
+    // this wave's (16 / NW)-th largest key (0 if it holds fewer): the NW
+    // waves' best 16 / NW keys are 16 distinct keys at least as large as
+    // the smallest of these
+    static_assert(16 % NW == 0, "16 / NW keys per wave");
+    uint64_t m = ~0ull;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) m1 = keys[i] > m1 ? keys[i] : m1;
-    m1 = wave_max_u64(m1);
-    uint64_t m2 = 0ull;   // keys are distinct: only m1 itself is excluded
+    for (int j = 0; j < 16 / NW; ++j) {
+      uint64_t c = 0ull;   // keys are distinct: the largest below the previous one
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) m2 = (keys[i] != m1 && keys[i] > m2) ? keys[i] : m2;
-    m2 = wave_max_u64(m2);
-    if (lane == 0) s2nd[wave] = m2;
+      for (int i = 0; i < kPer; ++i) c = (keys[i] < m && keys[i] > c) ? keys[i] : c;
+      m = wave_max_u64(c);
+    }
+    if (lane == 0) s2nd[wave] = m;
   }
   if (threadIdx.x == 0) snsurv = 0;
   if (threadIdx.x < 16) sbest[threadIdx.x] = 0ull;

@@ -28,6 +28,7 @@ from typing import List, Optional
 import torch
 
 from . import (DF2_GATE_IDENTITY, DF2_PATH_GREEDY, DF2_PATH_SAMPLE, DF2_PATH_VITERBI,
+               dflash2_cycle_fused, dflash2_cycle_fused_init, dflash2_cycle_fused_workspace_bytes,
                dflash2_dynconv2, dflash2_dynconv2_workspace_bytes, dflash2_init,
                dflash2_pair_scores, dflash2_pair_scores_tab, dflash2_pair_scores_tab_workspace_bytes,
                dflash2_pair_scores_workspace_bytes, dflash2_path_viterbi, dflash2_selector_tables,
@@ -58,13 +59,15 @@ class Cycle:
     verify: "greedy" | "reject" | "mixed" (first `greedy_rows` requests greedy,
     the rest rejection sampling).  tables: score pairs from per-token A/B
     tables built once here, instead of projecting the candidates' embedding
-    rows every cycle.
+    rows every cycle.  fused: run top-K, pair scores, path and verification
+    as one persistent launch (dflash2_cycle_fused; greedy verification,
+    VITERBI or GREEDY paths, bf16 logits, B T <= 1024), with the same results.
     """
 
     def __init__(self, *, logits, target, emb, h, w_a, w_b, w_h, last_tok, K: int,
                  path_mode: str, verify: str, tau: float = 1.0, gate: int = DF2_GATE_IDENTITY,
                  conv_sites: Optional[List[ConvSite]] = None, greedy_rows: Optional[int] = None,
-                 seed: int = 0, tables: bool = False):
+                 seed: int = 0, tables: bool = False, fused: bool = False):
         dflash2_init()
         dev = logits.device
         self.B, self.T, self.V = logits.shape
@@ -96,6 +99,13 @@ class Cycle:
         else:
             self.ws_pair = _ws(dflash2_pair_scores_workspace_bytes(B, T, K, self.d, self.r), dev)
         self.ws_verify = _ws(dflash2_verify_workspace_bytes(B, T, V), dev)
+        self.fused = fused
+        if fused:
+            if verify != "greedy" or path_mode == "sample" or tables:
+                raise ValueError("the fused cycle runs greedy verification with VITERBI or GREEDY paths")
+            self.status = torch.zeros((1,), **i32)
+            self.ws_fused = _ws(dflash2_cycle_fused_workspace_bytes(B, T, K, V, self.d, self.r), dev)
+            dflash2_cycle_fused_init(B, T, K, V, self.d, self.r, self.ws_fused)
         conv_bytes = 0
         for s in self.conv_sites:
             Bc, L, dc = s.x.shape
@@ -142,9 +152,18 @@ class Cycle:
         else:
             raise ValueError(self.verify)
 
+    def run_fused(self):
+        dflash2_cycle_fused(self.logits, self.target, self.emb, self.h, self.w_a, self.w_b, self.w_h,
+                            self.last_tok, self.path_mode, self.cand_idx, self.cand_val, self.scores,
+                            self.path_rank, self.path_tok, self.q, self.path_score, self.accept_len,
+                            self.out_tok, self.status, self.ws_fused, gate=self.gate)
+
     def run(self, conv: bool = True):
         if conv:
             self.run_conv()
+        if self.fused:
+            self.run_fused()
+            return
         self.run_topk()
         self.run_pair_scores()
         self.run_path()

@@ -23,6 +23,8 @@
  *   dflash2_verify_reject  speculative rejection sampling with a residual draw
  *   dflash2_verify_reject_head  the same from the target's hidden states,
  *                          with its LM head fused in (logits never stored)
+ *   dflash2_cycle_fused    top-K, pair scores, path and greedy verification
+ *                          of a small batch in one persistent launch
  *
  * Sources (the pages that define the operations; cited by title/section):
  *   [KDP]  "DFlash 2: Keep Drafting Parallel" (Inco AI blog; zh-CN mirror
@@ -361,6 +363,40 @@ int dflash2_verify_reject_head(const void* h, const void* emb, int emb_dt, int64
                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * One whole cycle of a small batch in one launch: dflash2_topk, then
+ * dflash2_pair_scores, dflash2_path_viterbi (VITERBI or GREEDY) and
+ * dflash2_verify_greedy on the same arguments, with the same results bit for
+ * bit ([KDP] "A lightweight path selector"; [WC] 坑 6: at batch 1 decoding
+ * speed is set by launch overhead).  The stages run as work-groups of one
+ * launch that wait for each other through counters in the workspace instead
+ * of kernel boundaries.
+ *   logits [B, T, vocab] bf16 (drafter), target [B, T+1, vocab] bf16,
+ *   emb [vocab, d], h [B, T, d], w_a, w_b, w_h [r, d] bf16, last_tok [B],
+ *   gate: as dflash2_pair_scores; path_mode: DF2_PATH_VITERBI or
+ *   DF2_PATH_GREEDY.
+ *   Outputs: cand_idx, cand_val [B, T, K]; scores [B, T, K, K]; path_rank,
+ *   path_tok [B, T]; q [B, T, K]; path_score [B] (may be NULL); accept_len
+ *   [B]; out_tok [B, T+1]; status [1] int32 (device): 0, 1 if a stage
+ *   waited too long for another, 2 if the control words were not zero at
+ *   the start (the outputs are then not valid).
+ * Limits: B T <= 1024, 1 <= T <= 63, 1 <= K <= 16, d % 64 == 0, r % 16 == 0
+ * in [16, 256]; vocab * d * 2 < 2^32.
+ * ws: dflash2_cycle_fused_workspace_bytes.  Its control words must be zero
+ * before the first call: call dflash2_cycle_fused_init once after allocating
+ * it (every call leaves them zero again).  Calls that share a workspace must
+ * be ordered on one stream.
+ * ------------------------------------------------------------------------ */
+size_t dflash2_cycle_fused_workspace_bytes(int B, int T, int K, int64_t vocab, int d, int r);
+int dflash2_cycle_fused_init(int B, int T, int K, int64_t vocab, int d, int r, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+int dflash2_cycle_fused(const void* logits, int logits_dt, const void* target, int target_dt, int64_t vocab,
+                        const void* emb, int emb_dt, const void* h, const void* w_a, const void* w_b,
+                        const void* w_h, const int32_t* last_tok, int B, int T, int K, int d, int r, int gate,
+                        int path_mode, int32_t* cand_idx, float* cand_val, float* scores, int32_t* path_rank,
+                        int32_t* path_tok, float* q, float* path_score, int32_t* accept_len, int32_t* out_tok,
+                        int32_t* status, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Philox4x64-10 words as the sampling steps above draw them (Salmon et al.,
  * "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11): for each i,
  * out[4i..4i+3] = Philox4x64-10(key = (seed, 0), counter = (t[i], b[i], 0, 0)).
@@ -379,7 +415,7 @@ int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t
  *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue", "philox",
  *   "lmhead_topk", "lmhead_merge", "head_argmax", "greedy_head_final",
  *   "head_stats", "head_row_reduce", "head_decide", "head_block_logits",
- *   "head_draw".
+ *   "head_draw", "cycle_fused", "fused_clear".
  * dflash2_profile_stop waits for the recorded events, writes up to `max`
  * per-launch durations in milliseconds to ms (host) and their count to *n,
  * and disarms.  Not for use during graph capture.  Events are created on

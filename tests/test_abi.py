@@ -113,6 +113,32 @@ def test_verify_reject_head_validation():
              None) == df2.DF2_OK
 
 
+def test_cycle_fused_validation():
+    L = df2.lib()
+    need = df2.dflash2_cycle_fused_workspace_bytes(1, 7, 16, 151936, 5120, 256)
+    assert need > 0
+    f = L.dflash2_cycle_fused
+    a = lambda **kw: [FAKE, kw.get("ldt", 1), FAKE, kw.get("tdt", 1), 151936, FAKE, 1, kw.get("h", FAKE), FAKE,
+                      FAKE, FAKE, FAKE, kw.get("B", 1), kw.get("T", 7), kw.get("K", 16), kw.get("d", 5120),
+                      kw.get("r", 256), kw.get("gate", 0), kw.get("mode", 0)] + [FAKE] * 10 + [FAKE, kw.get("ws", need),
+                                                                                      None]
+    assert f(*a(ldt=0)) == df2.DF2_ERR_DTYPE
+    assert f(*a(tdt=2)) == df2.DF2_ERR_DTYPE
+    assert f(*a(mode=2)) == df2.DF2_ERR_UNSUPPORTED      # SAMPLE paths run in the multi-launch cycle
+    assert f(*a(gate=3)) == df2.DF2_ERR_UNSUPPORTED
+    assert f(*a(T=64)) == df2.DF2_ERR_SHAPE
+    assert f(*a(B=147)) == df2.DF2_ERR_SHAPE               # B T > 1024
+    assert f(*a(K=17)) == df2.DF2_ERR_SHAPE
+    assert f(*a(d=100)) == df2.DF2_ERR_SHAPE
+    assert f(*a(r=8)) == df2.DF2_ERR_SHAPE
+    assert f(*a(h=None)) == df2.DF2_ERR_NULL
+    assert f(*a(ws=need - 1)) == df2.DF2_ERR_WORKSPACE
+    assert f(*a(B=0)) == df2.DF2_OK
+    g = L.dflash2_cycle_fused_init
+    assert g(1, 7, 16, 151936, 5120, 256, FAKE, need - 1, None) == df2.DF2_ERR_WORKSPACE
+    assert g(1, 64, 16, 151936, 5120, 256, FAKE, need, None) == df2.DF2_ERR_SHAPE
+
+
 def test_pair_scores_validation():
     L = df2.lib()
     args = lambda **kw: [kw.get("ci", FAKE), FAKE, FAKE, FAKE, kw.get("edt", 1), 151936, FAKE, FAKE,
