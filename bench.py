@@ -67,7 +67,7 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def build_cycle(w, dev, E=None, conv=True, tables=False):
+def build_cycle(w, dev, E=None, conv=True, tables=False, fused=False):
     import torch
     import synth
     from draft_selection_bf16_amd.cycle import ConvSite, Cycle
@@ -85,7 +85,7 @@ def build_cycle(w, dev, E=None, conv=True, tables=False):
             sites.append(ConvSite(x, xp, wt, bs, torch.empty(x.shape, dtype=torch.bfloat16, device=dev)))
     cyc = Cycle(logits=z, target=Z, emb=E, h=h, w_a=wa, w_b=wb, w_h=wh, last_tok=last, K=w.K,
                 path_mode=w.path_mode, verify=w.verify, tau=w.tau if w.tau > 0 else 1.0,
-                conv_sites=sites, seed=w.seed, tables=tables)
+                conv_sites=sites, seed=w.seed, tables=tables, fused=fused)
     return cyc, E
 
 
@@ -555,6 +555,14 @@ def main():
                 cr = cold_replays(c2, min(args.steps, 50), evict)
                 sweep[name]["cold"] = dict(cr, hbm_frac=hbm_frac(ws_, False, cr["median_us"]))
             del c2
+            if ws_.B == 1 and ws_.verify == "greedy":
+                # the same cycle as one persistent launch (dflash2_cycle_fused)
+                c2, _ = build_cycle(ws_, dev, E=E, conv=False, fused=True)
+                c2.capture(conv=False)
+                m2, _ = time_graph(c2, args.steps, args.warmup)
+                sweep[name]["fused_us_per_cycle"] = round(m2 * 1e3, 2)
+                sweep[name]["fused_status"] = int(c2.status.item())
+                del c2
         sweep[w.name + " (no conv)"] = dict(B=w.B, block=w.block, us_per_cycle=round(ms_nc * 1e3, 2),
                                             blocks_per_s=round(w.B / (ms_nc / 1e3), 1),
                                             hbm_frac=hbm_frac(w, False, ms_nc * 1e3))
