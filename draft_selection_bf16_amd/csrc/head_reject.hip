@@ -21,7 +21,7 @@
 //     the block where the running mass passes u2 * total, and what is left
 //     of u2 * total at its start.
 //  4. head_block_logits: the 128 logits of that block of row n, recomputed
-//     (16 threads per token, fixed-order fp32 dot products).
+//     (a wave per token, fixed-order fp32 dot products).
 //  5. head_draw: one wave per request walks the block's residual weights in
 //     index order to the drawn token.
 // Fallbacks are those of verify.hip: no residual mass -> the row's argmax
@@ -36,7 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kTokPerGroup = 16;                          // block-logit tokens per work-group
+constexpr int kTokPerGroup = kWaves;                      // block-logit tokens per work-group (a wave each)
 constexpr int kGroupsPerBlock = kHeadBlock / kTokPerGroup;
 
 struct HeadDec {   // per-request decision
@@ -59,7 +59,20 @@ __global__ __launch_bounds__(kThreads) void head_row_reduce_kernel(const BlockSt
   const BlockStat* p = stats + (int64_t)row * nblocks;
   uint64_t k = 0ull;
   float s = 0.f;
-  for (int j = lane; j < nblocks; j += kWave) combine_part(k, s, p[j].key, p[j].s, c);
+  // each lane's partials j = lane, lane + 64, ... in index order, requested
+  // eight at a time before they are folded
+  constexpr int kBatch = 8;
+  for (int j0 = lane; j0 < nblocks; j0 += kWave * kBatch) {
+    BlockStat v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int j = j0 + u * kWave;
+      v[u] = p[j < nblocks ? j : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (j0 + u * kWave < nblocks) combine_part(k, s, v[u].key, v[u].s, c);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     const uint64_t k2 = shfl_xor_u64(k, m);
@@ -250,9 +263,10 @@ __global__ __launch_bounds__(kThreads) void head_decide_kernel(
   dec[b] = d;
 }
 
-// the logits of block dec.nb of row (b, n): work-group g of request b takes
-// tokens 16 g .. 16 g + 15 of the block, 16 threads per token (16-byte
-// chunks c, c + 16, ... of the row in order, then a fixed butterfly)
+// the logits of block dec.nb of row (b, n): one wave per token (four per
+// work-group, 32 work-groups per request); lane l takes the 16-byte chunks
+// l, l + 64, ... of the two rows, all requested before the products, summed
+// in chunk order, then a fixed butterfly over the wave
 __global__ __launch_bounds__(kThreads) void head_block_logits_kernel(const uint16_t* __restrict__ h,
                                                                      const uint16_t* __restrict__ emb,
                                                                      int64_t vocab, int d, int T,
@@ -261,24 +275,35 @@ __global__ __launch_bounds__(kThreads) void head_block_logits_kernel(const uint1
   const int b = blockIdx.x / kGroupsPerBlock, g = blockIdx.x % kGroupsPerBlock;
   const HeadDec dd = dec[b];
   if (dd.nb < 0) return;
-  const int tok = g * kTokPerGroup + threadIdx.x / 16, l = threadIdx.x % 16;
+  const int tok = g * kTokPerGroup + wave_id(), lane = lane_id();
   const int64_t v = (int64_t)dd.nb * kHeadBlock + tok;
-  const bool valid = v < vocab;
+  if (v >= vocab) return;   // the same in the whole wave
   const u32x4* hr = (const u32x4*)(h + ((int64_t)b * (T + 1) + dd.n) * d);
-  const u32x4* er = (const u32x4*)(emb + (valid ? v : 0) * d);
+  const u32x4* er = (const u32x4*)(emb + v * d);
+  const int nch = d / 8;   // 16-byte chunks per row (d % 64 == 0: a multiple of 8)
+  constexpr int kBatch = 8;
   float acc = 0.f;
-  if (valid)
-    for (int ch = l; ch < d / 8; ch += 16) {
-      const u32x4 a = hr[ch], e = er[ch];
+  for (int c0 = lane; c0 < nch; c0 += kWave * kBatch) {
+    u32x4 a[kBatch], e[kBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += bf16_lo(a[i]) * bf16_lo(e[i]);
-        acc += bf16_hi(a[i]) * bf16_hi(e[i]);
-      }
+    for (int u = 0; u < kBatch; ++u) {
+      const int ch = c0 + u * kWave;
+      a[u] = hr[ch < nch ? ch : 0];
+      e[u] = er[ch < nch ? ch : 0];
     }
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (valid && l == 0) zblk[(int64_t)b * kHeadBlock + tok] = acc;
+    for (int u = 0; u < kBatch; ++u) {
+      if (c0 + u * kWave < nch) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc += bf16_lo(a[u][i]) * bf16_lo(e[u][i]);
+          acc += bf16_hi(a[u][i]) * bf16_hi(e[u][i]);
+        }
+      }
+    }
+  }
+  acc = wave_sum_f32(acc);
+  if (lane == 0) zblk[(int64_t)b * kHeadBlock + tok] = acc;
 }
 
 // one wave per request: lane L weighs tokens 2 L and 2 L + 1 of the block

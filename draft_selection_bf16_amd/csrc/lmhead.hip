@@ -395,21 +395,38 @@ __global__ __launch_bounds__(kMergeThreads) void lmhead_merge_kernel(const uint6
   }
 }
 
-// Greedy verification from the argmax keys: one wave per request, lane t
-// (t <= T) takes row (b, t)'s argmax over the token ranges; n = the longest
-// prefix on which the drafted tokens equal the argmax; emitted: the n
-// accepted drafts, then the argmax at n, then -1.
-__global__ __launch_bounds__(64) void greedy_head_final_kernel(const uint64_t* __restrict__ part, int nranges,
-                                                               const int32_t* __restrict__ path_tok, int T,
-                                                               int32_t* __restrict__ accept_len,
-                                                               int32_t* __restrict__ out_tok) {
-  const int b = blockIdx.x, lane = lane_id();
-  uint64_t m = 0ull;
-  if (lane <= T) {
-    const uint64_t* p = part + ((int64_t)b * (T + 1) + lane) * nranges;
-    for (int r = 0; r < nranges; ++r) m = p[r] > m ? p[r] : m;
+// Greedy verification from the argmax keys: one work-group of four waves
+// per request; wave w takes rows t = w, w + 4, ... (t <= T), its lanes the
+// row's ranges (all their keys requested before the maximum is taken), and
+// the row's argmax goes to LDS; then wave 0 finds n = the longest prefix on
+// which the drafted tokens equal the argmax and emits the n accepted drafts,
+// the argmax at n, then -1.
+constexpr int kFinalThreads = 256;
+__global__ __launch_bounds__(kFinalThreads) void greedy_head_final_kernel(const uint64_t* __restrict__ part,
+                                                                          int nranges,
+                                                                          const int32_t* __restrict__ path_tok,
+                                                                          int T, int32_t* __restrict__ accept_len,
+                                                                          int32_t* __restrict__ out_tok) {
+  __shared__ uint64_t sy[64];
+  const int b = blockIdx.x, lane = lane_id(), wave = threadIdx.x / kWave;
+  constexpr int kPer = kMaxRanges / kWave;   // keys per lane per row (nranges <= kMaxRanges)
+  for (int t = wave; t <= T; t += kFinalThreads / kWave) {
+    const uint64_t* p = part + ((int64_t)b * (T + 1) + t) * nranges;
+    uint64_t k[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = lane + i * kWave;
+      k[i] = r < nranges ? p[r] : 0ull;
+    }
+    uint64_t m = 0ull;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) m = k[i] > m ? k[i] : m;
+    m = wave_max_u64(m);
+    if (lane == 0) sy[t] = m;
   }
-  const int32_t y = (int32_t)key_index(m);
+  __syncthreads();
+  if (wave != 0) return;
+  const int32_t y = lane <= T ? (int32_t)key_index(sy[lane]) : -1;
   const int32_t x = lane < T ? path_tok[(int64_t)b * T + lane] : -1;
   const uint64_t miss = ballot(lane < T && x != y);
   const int n = miss ? __ffsll((unsigned long long)miss) - 1 : T;
@@ -482,8 +499,8 @@ hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t voc
                    plan.nranges, plan.nblocks, plan.xcd_groups, part, HeadStats{}));
   }
   ProfileScope ps("greedy_head_final", stream);
-  DF2_TRY(launch(greedy_head_final_kernel, dim3((unsigned)B), dim3(64), 0, stream, ps, part, plan.nranges, path_tok,
-                 T, accept_len, out_tok));
+  DF2_TRY(launch(greedy_head_final_kernel, dim3((unsigned)B), dim3(kFinalThreads), 0, stream, ps, part, plan.nranges,
+                 path_tok, T, accept_len, out_tok));
   return hipGetLastError();
 }
 
