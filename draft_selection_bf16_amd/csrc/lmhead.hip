@@ -216,7 +216,9 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     // into keys and inserted (the wave runs the insertion loop as often as
     // its busiest lane needs, not once per value).
     const float* trow = tile + my_row * kOld;
-    const int ncols = wrows;   // columns past the vocabulary are not tokens
+    // columns past the vocabulary are not tokens; rows past M (zeros) are
+    // not rows: their threads skip the fold
+    const int ncols = m0 + my_row < M ? wrows : 0;
     if constexpr (KEEP == 0) {
       // the block's online-softmax partial of this row: each thread over its
       // columns, then the row's four threads combined (symmetrically: all
