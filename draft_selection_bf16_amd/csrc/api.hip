@@ -241,7 +241,7 @@ namespace {
 // SIMD) over 3 LDS stages.  In the batch-32 / block-16 cycle (replayed
 // graph, top-K + pair scores + path + verify): 142.1 us against 144.7 us
 // with 4 waves over 4 stages and 143.9-145.2 us with 64-row tiles.
-constexpr GemmTiling kProjTiling{128, 128, 3, 8};
+constexpr GemmTiling kProjTiling{128, 128, 3, 8, 1};
 // The projection's K split: with few tiles (small batches) the reduction
 // over d is split so that up to about one work-group per CU takes part
 // (slices of >= 4 K-tiles, at most kMaxProjSplit).  The slices are summed
@@ -249,7 +249,7 @@ constexpr GemmTiling kProjTiling{128, 128, 3, 8};
 // pair epilogue, which gates H after the sum.
 constexpr int kMaxProjSplit = 8;
 constexpr int kMaxProjSplitSmall = 16;
-constexpr GemmTiling kProjTilingSmall{64, 128, 3, 4};
+constexpr GemmTiling kProjTilingSmall{64, 128, 3, 4, 1};
 constexpr int kSmallProjRows = 1024;
 int split_for(const GemmTiling& t, int maxs, int B, int T, int K, int d, int r) {
   const int bm = t.bm, bn = t.bn;
@@ -567,7 +567,7 @@ namespace {
 // reduction over d is split so that about one work-group per CU takes part
 // (64 x 128 tiles; slices of >= 4 K-tiles, at most kMaxHSplit); the
 // table-mode pair epilogue sums the slices in slice order itself.
-constexpr GemmTiling kHTiling{64, 128, 3, 4};
+constexpr GemmTiling kHTiling{64, 128, 3, 4, 1};
 constexpr int kMaxHSplit = 16;
 int h_split(int B, int T, int d, int r) {
   const int tiles = ((B * T + kHTiling.bm - 1) / kHTiling.bm) * ((r + kHTiling.bn - 1) / kHTiling.bn);

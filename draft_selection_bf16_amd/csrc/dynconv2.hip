@@ -132,7 +132,7 @@ ConvPlan conv_plan(int B, int L, int d, int group) {
   // tiles (96 KB), which halve the W bytes per work-group (64 requests,
   // block 16: 926.4 against 949.1 us per cycle with 20 sites)
   const int M = B * L, N = 2 * (d / 16);
-  p.tiling = M >= 1024 ? GemmTiling{128, 128, 3, 4} : GemmTiling{64, 128, 3, 4};
+  p.tiling = M >= 1024 ? GemmTiling{128, 128, 3, 4, 1} : GemmTiling{64, 128, 3, 4, 1};
   const int bm = p.tiling.bm;
   const int tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int nk = d / 64;

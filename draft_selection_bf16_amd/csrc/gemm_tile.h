@@ -58,7 +58,8 @@ __device__ __forceinline__ float apply_gate(float z, int gate) {
 
 // The K-tiles are copied by direct buffer-to-LDS loads (no register
 // staging) into S LDS stages, S - 1 of them in flight while the MFMAs of the
-// current one run; one barrier per K-tile.  The stage layout, the chunk
+// current one run; one barrier per K-tile (where the next copies are issued
+// within a K step: ISSUE below).  The stage layout, the chunk
 // swizzle and the load helper are in mfma_tile.h.
 using mfma::load_lds16;
 using mfma::swz;
@@ -66,7 +67,17 @@ using mfma::vmcnt_imm;
 
 // The tile of work-group `bid` of a grid of `nb` (the body of the GEMM
 // kernel; NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8)).
-template <int BM, int BN, int S, int NW>
+// ISSUE: where in a K step the copies of tile t + S - 1 are issued (into
+// the stage read in step t - 1, which every wave left before this step's
+// barrier): 0 right after the barrier (the longest lead: best for the
+// conv's few-K-tile, feed-bound tiles), 1 between the two halves of the
+// tile's MFMAs, 2 after them (the copy queue is often full, and an issue
+// that stalls then overlaps the matrix pipe's work instead of delaying it:
+// per K-tile of the batch-32 projection, issuing first spent 244 of 1,237
+// cycles in the issue; 55.7 -> 47.5 us alone).  Measured on one box, the
+// batch-32 / block-16 step was 0.5220 ms with 0 everywhere, 0.5239 with 2
+// and 0.5206 with 1 (the cycle without the conv 132.5 / 128.6 / 129.0 us).
+template <int BM, int BN, int S, int NW, int ISSUE>
 __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
   static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
@@ -203,7 +214,7 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
     // visible and frees the stage read in step t - 1 for tile t + S - 1
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * LPW));
     __builtin_amdgcn_s_barrier();
-    issue(t + S - 1);
+    if constexpr (ISSUE == 0) issue(t + S - 1);
     const uint8_t* st = dyn_lds + (t % S) * STAGE;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -217,7 +228,10 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+      if constexpr (ISSUE == 1)
+        if (s2 == 0) issue(t + S - 1);
     }
+    if constexpr (ISSUE == 2) issue(t + S - 1);
   }
 
   // Output through LDS: the accumulators (lane holds column lane & 15, rows

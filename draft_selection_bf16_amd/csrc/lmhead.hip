@@ -180,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     for (int t = 0; t < nkt; ++t) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kS - 2) * kLPW));
       __builtin_amdgcn_s_barrier();
-      issue(t + kS - 1);
       const uint8_t* st = dyn_lds + (t % kS) * kStage;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -195,6 +194,9 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
           for (int j = 0; j < kFN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
       }
+      // next copies behind the MFMAs, into the stage every wave left before
+      // this step's barrier (as in gemm_tile.h)
+      issue(t + kS - 1);
     }
     // the fp32 tile through LDS (lane holds column lane & 15, rows
     // 4 (lane >> 4) + e of each 16 x 16 block), then each thread folds its
