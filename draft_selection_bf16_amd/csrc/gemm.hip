@@ -6,9 +6,9 @@ namespace df2 {
 using namespace gemm;
 namespace {
 
-template <int BM, int BN, int S, int NW, int ISSUE>
+template <int BM, int BN, int S, int NW, int ISSUE, bool ONE_SEG>
 __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
-  run_tile<BM, BN, S, NW, ISSUE>(Pb, blockIdx.x, gridDim.x);
+  run_tile<BM, BN, S, NW, ISSUE, ONE_SEG>(Pb, blockIdx.x, gridDim.x);
 }
 
 }  // namespace
@@ -59,17 +59,21 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)(tiles * ksplit));
   ProfileScope ps(tag, stream);
-#define DF2_GEMM_LAUNCH(BMV, BNV, SV, NWV, IV)                                                     \
-  if (t.bm == BMV && t.bn == BNV && t.stages == SV && t.waves == NWV && t.issue == IV) {           \
-    constexpr int kLds = SV * (BMV + BNV) * BK * 2;                                                \
-    static bool done = false;                                                                      \
-    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, BNV, SV, NWV, IV>, kLds, done);     \
-    if (e != hipSuccess) return e;                                                                 \
-    return launch(gemm_dma_kernel<BMV, BNV, SV, NWV, IV>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
+#define DF2_GEMM_LAUNCH(BMV, BNV, SV, NWV, IV, ONE)                                                  \
+  if (t.bm == BMV && t.bn == BNV && t.stages == SV && t.waves == NWV && t.issue == IV &&               \
+      (P.nseg == 1) == ONE) {                                                                          \
+    constexpr int kLds = SV * (BMV + BNV) * BK * 2;                                                    \
+    static bool done = false;                                                                          \
+    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, BNV, SV, NWV, IV, ONE>, kLds, done);    \
+    if (e != hipSuccess) return e;                                                                     \
+    return launch(gemm_dma_kernel<BMV, BNV, SV, NWV, IV, ONE>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
   }
-  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1)   // the conv's taps from 1,024 rows
-  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1)   // projection, per-token tables
-  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // the conv's taps, H, projection at small batches
+  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1, true)    // the conv's taps from 1,024 rows
+  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1, false)
+  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1, false)   // projection, per-token tables
+  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1, true)
+  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1, true)     // the conv's taps, H
+  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1, false)    // projection at small batches
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
 }

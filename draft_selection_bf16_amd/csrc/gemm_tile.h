@@ -77,7 +77,10 @@ using mfma::vmcnt_imm;
 // cycles in the issue; 55.7 -> 47.5 us alone).  Measured on one box, the
 // batch-32 / block-16 step was 0.5220 ms with 0 everywhere, 0.5239 with 2
 // and 0.5206 with 1 (the cycle without the conv 132.5 / 128.6 / 129.0 us).
-template <int BM, int BN, int S, int NW, int ISSUE>
+// ONE_SEG: the problem has a single segment (segment 0): its fields are
+// fetched in the same round of scalar loads as the header (a round trip of
+// the prologue less; the conv's tap GEMM and H take this form).
+template <int BM, int BN, int S, int NW, int ISSUE, bool ONE_SEG>
 __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
   static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
@@ -93,14 +96,16 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   // a select, not a branch: the scalar loads then go out together instead
   // of one dependent round trip each.
   const int ksplit = Pb.ksplit, K = Pb.K;
-  const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
-  asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
   const int full = nb / kXcds * kXcds;
   const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
-  const int tile = ksplit == 1 ? bx : bid / ksplit;
-  const int ks = ksplit == 1 ? 0 : bid % ksplit;
-  // tile_begin[i] for i >= nseg is the tile total
-  const int si = (tile >= tb1 ? 1 : 0) + (tile >= tb2 ? 1 : 0) + (tile >= tb3 ? 1 : 0);
+  int si = 0;
+  if constexpr (!ONE_SEG) {
+    const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
+    asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
+    const int tile_ = ksplit == 1 ? bx : bid / ksplit;
+    // tile_begin[i] for i >= nseg is the tile total
+    si = (tile_ >= tb1 ? 1 : 0) + (tile_ >= tb2 ? 1 : 0) + (tile_ >= tb3 ? 1 : 0);
+  }
   static_assert(kMaxSeg == 4, "segment index select");
   const GemmSeg& S_ = Pb.s[si];
   const uint16_t* sx = S_.x;
@@ -112,10 +117,12 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
   const int gate = S_.gate;
   const int grows = S_.grp_rows, gstride = S_.grp_stride;
-  const int tbegin = Pb.tile_begin[si];
+  const int tbegin = ONE_SEG ? 0 : Pb.tile_begin[si];
   asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
                "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate), "s"(grows),
-               "s"(gstride), "s"(tbegin));   // one round trip
+               "s"(gstride), "s"(tbegin), "s"(ksplit), "s"(K));   // one round trip
+  const int tile = ksplit == 1 ? bx : bid / ksplit;
+  const int ks = ksplit == 1 ? 0 : bid % ksplit;
   // product row -> row of the gather list / x and of out
   auto phys = [&](int m) { return grows > 0 ? (m / grows) * gstride + m % grows : m; };
   const int local = tile - tbegin;
