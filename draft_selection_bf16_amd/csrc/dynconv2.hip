@@ -37,12 +37,15 @@ constexpr int kChunks = 3;       // 16-byte x chunks per thread kept in flight (
 // that consecutive rows run on one XCD (work-group i on XCD i mod 8), where
 // x_{t-1} is the previous row's x_t, already in that XCD's L2.
 template <bool Y_BF16>
+// The arguments a work-group needs first (all but y) fit the 56 bytes that
+// the command processor preloads into SGPRs, the grid size among them, so
+// the kernel starts without a scalar load (y is fetched behind the loads).
 __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ x_prev,
-    const float* __restrict__ base, const float* __restrict__ part, int ksplit, int64_t kstride,
+    const float* __restrict__ base, const float* __restrict__ part, int ksplit, int nb, int64_t kstride,
     int L, int d, void* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) float sc[kMaxTaps];
-  const int nb = gridDim.x, full = nb / 8 * 8;
+  const int full = nb / 8 * 8;
   const int bid = blockIdx.x;
   const int row = bid < full ? (bid % 8) * (full / 8) + bid / 8 : bid;   // b * L + t
   const int b = row / L, t = row % L;
@@ -178,10 +181,10 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
   ProfileScope ps("conv_epilogue", stream);
   if (y_dt == 1)
     DF2_TRY(launch(conv_epilogue_kernel<true>, dim3(M), dim3(kThreads), 0, stream, ps,
-        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y));
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, M, (int64_t)M * N, L, d, y));
   else
     DF2_TRY(launch(conv_epilogue_kernel<false>, dim3(M), dim3(kThreads), 0, stream, ps,
-        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, (int64_t)M * N, L, d, y));
+        (const uint16_t*)x, (const uint16_t*)x_prev, base, part, plan.ksplit, M, (int64_t)M * N, L, d, y));
   return hipGetLastError();
 }
 

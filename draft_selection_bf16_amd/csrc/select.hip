@@ -29,22 +29,24 @@ namespace df2 {
 namespace {
 using namespace selectd;
 
-__global__ __launch_bounds__(64) void slice_reduce_kernel(float* __restrict__ p0, int64_t n0, int64_t k0,
-                                                           float* __restrict__ p1, int64_t n1, int64_t k1,
-                                                           float* __restrict__ p2, int64_t n2, int64_t k2,
-                                                           int split) {
+// Kernel arguments are ordered so that what a work-group needs first falls
+// in the 56 bytes the command processor preloads into SGPRs (no scalar load
+// before the first memory request).
+__global__ __launch_bounds__(64) void slice_reduce_kernel(float* __restrict__ p0, float* __restrict__ p1,
+                                                           float* __restrict__ p2, int n0, int n1, int n2,
+                                                           int split, int64_t k0, int64_t k1, int64_t k2) {
   slice_reduce_elem(p0, n0, k0, p1, n1, k1, p2, n2, k2, split, (int64_t)blockIdx.x * 64 + threadIdx.x);
 }
 
 template <bool TAB>
 __global__ __launch_bounds__(256) void pair_epilogue_kernel(const float* __restrict__ ab,
                                                             const float* __restrict__ a_last,
-                                                            const float* __restrict__ h_part, int gate,
-                                                            const float* __restrict__ cand_val,
+                                                            const float* __restrict__ h_part,
+                                                            const float* __restrict__ cand_val, int T, int K,
+                                                            int r, int gate, float* __restrict__ scores,
                                                             const int32_t* __restrict__ cand_idx,
                                                             const int32_t* __restrict__ last_tok, int64_t vocab,
-                                                            int hsplit, int64_t h_k, int T, int K, int r,
-                                                            float* __restrict__ scores) {
+                                                            int hsplit, int64_t h_k) {
   __shared__ PairLds<TAB> L;
   pair_epilogue_body<TAB>(ab, a_last, h_part, gate, cand_val, cand_idx, last_tok, vocab, hsplit, h_k, T, K, r,
                           scores, blockIdx.x, L);
@@ -74,14 +76,16 @@ hipError_t launch_pair_epilogue(float* ab, float* a_last, float* h, int split,
     // then reads one slice
     const int64_t n0 = (int64_t)B * T * K * 2 * r / 4, n1 = (int64_t)B * r / 4, n2 = (int64_t)B * T * r / 4;
     const int64_t n = n0 + n1 + n2;
+    // a split projection has few tiles, so n is far below 2^31 (the kernel
+    // takes the counts as int)
+    if (n >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     ProfileScope pr("proj_reduce", stream);
     DF2_TRY(launch(slice_reduce_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, pr,
-                   ab, n0, ab_k, a_last, n1, alast_k, h, n2, h_k, split));
+                   ab, a_last, h, (int)n0, (int)n1, (int)n2, split, ab_k, alast_k, h_k));
   }
   ProfileScope ps("pair_epilogue", stream);
-  DF2_TRY(launch(pair_epilogue_kernel<false>, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, gate,
-                 cand_val, (const int32_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, 1, (int64_t)0, T, K, r,
-                 scores));
+  DF2_TRY(launch(pair_epilogue_kernel<false>, dim3(B * T), dim3(256), 0, stream, ps, ab, a_last, h, cand_val, T, K,
+                 r, gate, scores, (const int32_t*)nullptr, (const int32_t*)nullptr, (int64_t)0, 1, (int64_t)0));
   return hipGetLastError();
 }
 
@@ -92,7 +96,7 @@ hipError_t launch_pair_epilogue_tab(const float* tab, int64_t vocab, const int32
   if (B * T == 0) return hipSuccess;
   ProfileScope ps("pair_epilogue", stream);
   DF2_TRY(launch(pair_epilogue_kernel<true>, dim3(B * T), dim3(256), 0, stream, ps, tab, (const float*)nullptr,
-                 h, gate, cand_val, cand_idx, last_tok, vocab, split, h_k, T, K, r, scores));
+                 h, cand_val, T, K, r, gate, scores, cand_idx, last_tok, vocab, split, h_k));
   return hipGetLastError();
 }
 
