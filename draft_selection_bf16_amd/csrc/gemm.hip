@@ -6,9 +6,27 @@ namespace df2 {
 using namespace gemm;
 namespace {
 
-template <int BM, int BN, int S, int NW, int ISSUE, bool ONE_SEG>
+template <int BM, int BN, int S, int NW, int ISSUE>
 __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
-  run_tile<BM, BN, S, NW, ISSUE, ONE_SEG>(Pb, blockIdx.x, gridDim.x);
+  run_tile<BM, BN, S, NW, ISSUE>(Pb, blockIdx.x, gridDim.x);
+}
+
+// (the fields as separate arguments: an aggregate passed by value is not
+// preloaded into SGPRs, scalars and pointers are)
+template <int BM, int BN, int S, int NW, int ISSUE>
+__global__ __launch_bounds__(NW * 64) void gemm_dense_kernel(const uint16_t* x, const uint16_t* w, float* out,
+                                                             int M, int N, int K, int ksplit, int ldx, int ldo) {
+  DenseProblem D;
+  D.x = x;
+  D.w = w;
+  D.out = out;
+  D.M = M;
+  D.N = N;
+  D.K = K;
+  D.ksplit = ksplit;
+  D.ldx = ldx;
+  D.ldo = ldo;
+  run_tile_dense<BM, BN, S, NW, ISSUE>(D, blockIdx.x);
 }
 
 }  // namespace
@@ -59,21 +77,42 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
   if (tiles == 0) return hipSuccess;
   dim3 grid((unsigned)(tiles * ksplit));
   ProfileScope ps(tag, stream);
-#define DF2_GEMM_LAUNCH(BMV, BNV, SV, NWV, IV, ONE)                                                  \
-  if (t.bm == BMV && t.bn == BNV && t.stages == SV && t.waves == NWV && t.issue == IV &&               \
-      (P.nseg == 1) == ONE) {                                                                          \
-    constexpr int kLds = SV * (BMV + BNV) * BK * 2;                                                    \
-    static bool done = false;                                                                          \
-    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, BNV, SV, NWV, IV, ONE>, kLds, done);    \
-    if (e != hipSuccess) return e;                                                                     \
-    return launch(gemm_dma_kernel<BMV, BNV, SV, NWV, IV, ONE>, grid, dim3(NWV * 64), kLds, stream, ps, P); \
+  // one dense problem whose sizes fit the compact arguments: the kernel
+  // whose arguments are all preloaded
+  const GemmSeg& s0 = P.s[0];
+  const bool dense = P.nseg == 1 && !s0.gather && s0.grp_rows == 0 && s0.gate == 0 && s0.n0 >= s0.N &&
+                     s0.x_rows == s0.M && s0.ldx <= INT32_MAX && s0.ldo <= INT32_MAX &&
+                     (P.ksplit == 1 || s0.out_kstride == (int64_t)s0.M * s0.ldo);
+  DenseProblem D{};
+  if (dense) {
+    D.x = s0.x;
+    D.w = s0.w0;
+    D.out = s0.out;
+    D.M = s0.M;
+    D.N = s0.N;
+    D.K = P.K;
+    D.ksplit = P.ksplit;
+    D.ldx = (int)s0.ldx;
+    D.ldo = (int)s0.ldo;
   }
-  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1, true)    // the conv's taps from 1,024 rows
-  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1, false)
-  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1, false)   // projection, per-token tables
-  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1, true)
-  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1, true)     // the conv's taps, H
-  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1, false)    // projection at small batches
+#define DF2_GEMM_LAUNCH(BMV, BNV, SV, NWV, IV)                                                          \
+  if (t.bm == BMV && t.bn == BNV && t.stages == SV && t.waves == NWV && t.issue == IV) {               \
+    constexpr int kLds = SV * (BMV + BNV) * BK * 2;                                                    \
+    if (dense) {                                                                                       \
+      static bool done_d = false;                                                                      \
+      hipError_t e = allow_lds((const void*)gemm_dense_kernel<BMV, BNV, SV, NWV, IV>, kLds, done_d);   \
+      if (e != hipSuccess) return e;                                                                   \
+      return launch(gemm_dense_kernel<BMV, BNV, SV, NWV, IV>, grid, dim3(NWV * 64), kLds, stream, ps, D.x, D.w, \
+                    D.out, D.M, D.N, D.K, D.ksplit, D.ldx, D.ldo);                                              \
+    }                                                                                                  \
+    static bool done = false;                                                                          \
+    hipError_t e = allow_lds((const void*)gemm_dma_kernel<BMV, BNV, SV, NWV, IV>, kLds, done);         \
+    if (e != hipSuccess) return e;                                                                     \
+    return launch(gemm_dma_kernel<BMV, BNV, SV, NWV, IV>, grid, dim3(NWV * 64), kLds, stream, ps, P);  \
+  }
+  DF2_GEMM_LAUNCH(128, 128, 3, 4, 1)   // the conv's taps from 1,024 rows
+  DF2_GEMM_LAUNCH(128, 128, 3, 8, 1)   // projection, per-token tables
+  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // the conv's taps, H, projection at small batches
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
 }

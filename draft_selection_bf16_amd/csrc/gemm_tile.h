@@ -77,11 +77,13 @@ using mfma::vmcnt_imm;
 // cycles in the issue; 55.7 -> 47.5 us alone).  Measured on one box, the
 // batch-32 / block-16 step was 0.5220 ms with 0 everywhere, 0.5239 with 2
 // and 0.5206 with 1 (the cycle without the conv 132.5 / 128.6 / 129.0 us).
-// ONE_SEG: the problem has a single segment (segment 0): its fields are
-// fetched in the same round of scalar loads as the header (a round trip of
-// the prologue less; the conv's tap GEMM and H take this form).
-template <int BM, int BN, int S, int NW, int ISSUE, bool ONE_SEG>
-__device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
+// The tile itself: product rows m0 .. m0 + BM - 1 and columns n0 .. n0 + BN
+// - 1 of one segment, K slice ks of ksplit (every argument a scalar).
+template <int BM, int BN, int S, int NW, int ISSUE>
+__device__ __forceinline__ void tile_core(const uint16_t* sx, const int32_t* sgather, int x_rows, int ldx, int M,
+                                          int N, int sn0, const uint16_t* w0, const uint16_t* w1, float* sout,
+                                          int64_t ldo, int64_t out_kstride, int gate, int grows, int gstride, int K,
+                                          int m0, int n0, int ks, int ksplit) {
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
   static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
   constexpr int kThreads = NW * 64;
@@ -91,42 +93,8 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
   constexpr int ALD = BM / (8 * NW), BLD = BN / (8 * NW);   // load instructions per wave per stage
   constexpr int LPW = ALD + BLD;
   constexpr int STAGE = (BM + BN) * BK * 2;     // bytes
-
-  // Every kernel-argument scalar is read up front and every choice below is
-  // a select, not a branch: the scalar loads then go out together instead
-  // of one dependent round trip each.
-  const int ksplit = Pb.ksplit, K = Pb.K;
-  const int full = nb / kXcds * kXcds;
-  const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
-  int si = 0;
-  if constexpr (!ONE_SEG) {
-    const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
-    asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
-    const int tile_ = ksplit == 1 ? bx : bid / ksplit;
-    // tile_begin[i] for i >= nseg is the tile total
-    si = (tile_ >= tb1 ? 1 : 0) + (tile_ >= tb2 ? 1 : 0) + (tile_ >= tb3 ? 1 : 0);
-  }
-  static_assert(kMaxSeg == 4, "segment index select");
-  const GemmSeg& S_ = Pb.s[si];
-  const uint16_t* sx = S_.x;
-  const int32_t* sgather = S_.gather;
-  const int x_rows = S_.x_rows, ldx = S_.ldx, M = S_.M, N = S_.N, sn0 = S_.n0;
-  const uint16_t *w0 = S_.w0, *w1 = S_.w1;
-  const int tiles_n = S_.tiles_n;
-  float* const sout = S_.out;
-  const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
-  const int gate = S_.gate;
-  const int grows = S_.grp_rows, gstride = S_.grp_stride;
-  const int tbegin = ONE_SEG ? 0 : Pb.tile_begin[si];
-  asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
-               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate), "s"(grows),
-               "s"(gstride), "s"(tbegin), "s"(ksplit), "s"(K));   // one round trip
-  const int tile = ksplit == 1 ? bx : bid / ksplit;
-  const int ks = ksplit == 1 ? 0 : bid % ksplit;
   // product row -> row of the gather list / x and of out
   auto phys = [&](int m) { return grows > 0 ? (m / grows) * gstride + m % grows : m; };
-  const int local = tile - tbegin;
-  const int m0 = (local / tiles_n) * BM, n0 = (local % tiles_n) * BN;
   const int nkt = K / BK;
   const int kt0 = ks * nkt / ksplit, kt1 = (ks + 1) * nkt / ksplit;
   const int k_begin = kt0 * BK;
@@ -269,6 +237,73 @@ __device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
       *(f32x4*)(out + (int64_t)phys(m) * ldo + n) = v;
     }
   }
+}
+
+// The tile of work-group `bid` of a grid of `nb` over the segments of Pb.
+template <int BM, int BN, int S, int NW, int ISSUE>
+__device__ __forceinline__ void run_tile(const Problem& Pb, int bid, int nb) {
+
+  // Every kernel-argument scalar is read up front and every choice below is
+  // a select, not a branch: the scalar loads then go out together instead
+  // of one dependent round trip each.
+  const int ksplit = Pb.ksplit, K = Pb.K;
+  const int full = nb / kXcds * kXcds;
+  const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
+  const int tb1 = Pb.tile_begin[1], tb2 = Pb.tile_begin[2], tb3 = Pb.tile_begin[3];
+  asm volatile("" ::"s"(ksplit), "s"(K), "s"(tb1), "s"(tb2), "s"(tb3), "s"(nb));   // one round trip
+  const int tile_ = ksplit == 1 ? bx : bid / ksplit;
+  // tile_begin[i] for i >= nseg is the tile total
+  const int si = (tile_ >= tb1 ? 1 : 0) + (tile_ >= tb2 ? 1 : 0) + (tile_ >= tb3 ? 1 : 0);
+  static_assert(kMaxSeg == 4, "segment index select");
+  const GemmSeg& S_ = Pb.s[si];
+  const uint16_t* sx = S_.x;
+  const int32_t* sgather = S_.gather;
+  const int x_rows = S_.x_rows, ldx = S_.ldx, M = S_.M, N = S_.N, sn0 = S_.n0;
+  const uint16_t *w0 = S_.w0, *w1 = S_.w1;
+  const int tiles_n = S_.tiles_n;
+  float* const sout = S_.out;
+  const int64_t ldo = S_.ldo, out_kstride = S_.out_kstride;
+  const int gate = S_.gate;
+  const int grows = S_.grp_rows, gstride = S_.grp_stride;
+  const int tbegin = Pb.tile_begin[si];
+  asm volatile("" ::"s"(sx), "s"(sgather), "s"(x_rows), "s"(ldx), "s"(M), "s"(N), "s"(sn0), "s"(w0),
+               "s"(w1), "s"(tiles_n), "s"(sout), "s"(ldo), "s"(out_kstride), "s"(gate), "s"(grows),
+               "s"(gstride), "s"(tbegin), "s"(ksplit), "s"(K));   // one round trip
+  const int tile = ksplit == 1 ? bx : bid / ksplit;
+  const int ks = ksplit == 1 ? 0 : bid % ksplit;
+  const int local = tile - tbegin;
+  const int m0 = (local / tiles_n) * BM, n0 = (local % tiles_n) * BN;
+  tile_core<BM, BN, S, NW, ISSUE>(sx, sgather, x_rows, ldx, M, N, sn0, w0, w1, sout, ldo, out_kstride, gate, grows,
+                                  gstride, K, m0, n0, ks, ksplit);
+}
+
+// One dense problem (no gather, no row map, no gate, one weight matrix, x
+// holding exactly the M rows, K slices of [M, ldo] one after another):
+// 48 bytes of arguments, which the command processor preloads into SGPRs
+// when the kernel takes them as separate scalars (it preloads 56 bytes), so
+// the work-group starts without a scalar load -- the conv's tap GEMM and H;
+// with the 464-byte Problem, which is loaded from memory, the conv GEMM's
+// prologue spent about 2,000 cycles on its arguments.
+struct DenseProblem {
+  const uint16_t* x;    // [M, K] rows, ldx elements apart
+  const uint16_t* w;    // [N, K]
+  float* out;           // out[m * ldo + n] (+ slice * M * ldo)
+  int M, N, K, ksplit;
+  int ldx, ldo;
+};
+
+template <int BM, int BN, int S, int NW, int ISSUE>
+__device__ __forceinline__ void run_tile_dense(const DenseProblem& D, int bid) {
+  const int ksplit = D.ksplit;
+  const int tiles_n = (D.N + BN - 1) / BN;
+  const int nb = ((D.M + BM - 1) / BM) * tiles_n * ksplit;   // the grid
+  const int full = nb / kXcds * kXcds;
+  const int bx = bid < full ? (bid % kXcds) * (full / kXcds) + bid / kXcds : bid;
+  const int tile = ksplit == 1 ? bx : bid / ksplit;
+  const int ks = ksplit == 1 ? 0 : bid % ksplit;
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  tile_core<BM, BN, S, NW, ISSUE>(D.x, nullptr, D.M, D.ldx, D.M, D.N, D.N, D.w, D.w, D.out, D.ldo,
+                                  (int64_t)D.M * D.ldo, 0, 0, 1, D.K, m0, n0, ks, ksplit);
 }
 
 // Fill P for up to kMaxSeg problems (hipErrorInvalidValue for shapes the
