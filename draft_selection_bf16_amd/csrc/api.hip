@@ -238,10 +238,12 @@ int dflash2_verify_reject_head(const void* h, const void* emb, int emb_dt, int64
 // ------------------------------------------------------------------ pair scores
 namespace {
 // projection tiling: 128-row tiles, one work-group per CU, 8 waves (two per
-// SIMD) over 3 LDS stages.  In the batch-32 / block-16 cycle (replayed
-// graph, top-K + pair scores + path + verify): 142.1 us against 144.7 us
-// with 4 waves over 4 stages and 143.9-145.2 us with 64-row tiles.
-constexpr GemmTiling kProjTiling{128, 128, 3, 8, 1};
+// SIMD) in two alternating groups over 4 LDS stages.  In the batch-32 /
+// block-16 cycle (replayed graph, top-K + pair scores + path + verify):
+// 142.1 us with both groups in step over 3 stages against 144.7 us with 4
+// waves over 4 stages and 143.9-145.2 us with 64-row tiles; the alternating
+// groups then took the projection alone (warm caches) from 49.3 to 47.6 us.
+constexpr GemmTiling kProjTiling{128, 128, 4, 8, 3};
 // The projection's K split: with few tiles (small batches) the reduction
 // over d is split so that up to about one work-group per CU takes part
 // (slices of >= 4 K-tiles, at most kMaxProjSplit).  The slices are summed

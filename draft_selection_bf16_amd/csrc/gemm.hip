@@ -113,6 +113,7 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
   DF2_GEMM_LAUNCH(128, 128, 3, 4, 1)   // the conv's taps from 1,024 rows
   DF2_GEMM_LAUNCH(128, 128, 3, 8, 1)   // projection, per-token tables
   DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // the conv's taps, H, projection at small batches
+  DF2_GEMM_LAUNCH(128, 128, 4, 8, 3)   // two alternating wave groups
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
 }

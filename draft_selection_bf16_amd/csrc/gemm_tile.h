@@ -67,7 +67,8 @@ using mfma::vmcnt_imm;
 
 // The tile of work-group `bid` of a grid of `nb` (the body of the GEMM
 // kernel; NW waves per work-group: 2 x 2 (NW = 4) or 2 x 4 (NW = 8)).
-// ISSUE: where in a K step the copies of tile t + S - 1 are issued (into
+// ISSUE 3: the ping-pong loop of mfma_tile.h (NW = 8, waves in two
+// alternating groups).  ISSUE 0-2: where in a K step the copies of tile t + S - 1 are issued (into
 // the stage read in step t - 1, which every wave left before this step's
 // barrier): 0 right after the barrier (the longest lead: best for the
 // conv's few-K-tile, feed-bound tiles), 1 between the two halves of the
@@ -85,6 +86,7 @@ __device__ __forceinline__ void tile_core(const uint16_t* sx, const int32_t* sga
                                           int64_t ldo, int64_t out_kstride, int gate, int grows, int gstride, int K,
                                           int m0, int n0, int ks, int ksplit) {
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "whole load instructions per wave");
+  static_assert(ISSUE != 3 || NW == 8, "two alternating groups of four waves");
   static_assert((BM / 2) % 16 == 0 && (BN / (NW / 2)) % 16 == 0, "whole 16 x 16 blocks per wave");
   constexpr int kThreads = NW * 64;
   constexpr int WCOL = NW / 2;                  // waves along N
@@ -184,6 +186,9 @@ __device__ __forceinline__ void tile_core(const uint16_t* sx, const int32_t* sga
 
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) issue(t);
+  if constexpr (ISSUE == 3) {
+    mfma::pingpong_loop<S, FM, FN, LPW, STAGE>(dyn_lds, issue, ao, bo, acc, nk, wm);
+  } else
   for (int t = 0; t < nk; ++t) {
     // this wave's copies of tile t are done; the barrier makes everyone's
     // visible and frees the stage read in step t - 1 for tile t + S - 1
