@@ -154,7 +154,8 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
 
 // ---- drafter LM head fused with the top-K ----------------------------------
 struct LmHeadPlan {
-  int mblocks;      // 128-row blocks of h
+  int bm;           // rows of h per tile: 128 or 256
+  int mblocks;      // bm-row blocks of h
   int nblocks;      // 128-token blocks of the vocabulary
   int nranges;      // token ranges (work-groups per row block)
   int xcd_groups;   // nranges % 8 == 0: a range's row blocks run on one XCD

@@ -11,15 +11,17 @@
 // then the K best per row by (value desc, index asc).
 //
 // Two launches:
-//  1. lmhead_topk_kernel: the product on the matrix cores, 128 x 128 tiles
-//     (rows of h x tokens), K-tiles of 64 staged through 4 LDS stages by
-//     direct buffer-to-LDS loads (mfma_tile.h), 8 waves.  A work-group owns
-//     one 128-row block and a contiguous range of 128-token blocks; after
-//     each token block the fp32 tile goes through LDS, and thread (row, q)
-//     folds columns q, q + 4, ... of its row into a running best-16 list
+//  1. lmhead_topk_kernel: the product on the matrix cores, 256 x 128 or
+//     128 x 128 tiles (rows of h x tokens; 256 rows wherever they add no
+//     padding), K-tiles of 64 staged through 3 or 4 LDS stages by direct
+//     buffer-to-LDS loads (mfma_tile.h), 8 waves.  A work-group owns one
+//     row block and a contiguous range of 128-token blocks; after each token
+//     block the fp32 tile goes through LDS, and thread (row, q) of the row's
+//     Q = 2 or 4 threads folds columns q, q + Q, ... of its row into a
+//     running best-16 list
 //     held in registers (a sorted insertion, taken only by the few values
 //     at or above the row's current threshold, found with one fp32 compare
-//     each).  At the end the four lists of a row are ranked against
+//     each).  At the end the Q lists of a row are ranked against
 //     each other and the row's 16 best keys of the range are written out.
 //     The work-groups that share a token range (one per row block) run on
 //     one XCD, one after the other in dispatch order, so that the token
@@ -45,22 +47,34 @@ using mfma::load_lds16;
 using mfma::swz;
 using mfma::vmcnt_imm;
 
-constexpr int kBM = 128, kBN = 128, kS = 4, kNW = 8;   // tile, LDS stages, waves
+// Work-group tile: BM rows of h x 128 tokens, 8 waves, K-tiles of 64 through
+// LDS stages.  BM = 128: waves 2 x 4 (64 x 32 each), 4 stages (128 KB), four
+// threads per row in the epilogues; BM = 256: waves 4 x 2 (64 x 64 each: half
+// the fragment bytes per MFMA, and a token block's rows are fetched by half
+// as many work-groups), 3 stages (144 KB), two threads per row.
+constexpr int kBN = 128, kNW = 8;
 constexpr int kThreads = kNW * 64;
-constexpr int kWcol = kNW / 2;                          // waves along the tokens
-constexpr int kWM = kBM / 2, kWN = kBN / kWcol;         // 64 x 32 per wave
-constexpr int kFM = kWM / 16, kFN = kWN / 16;           // 4 x 2 blocks of 16 x 16
-constexpr int kALD = kBM / (8 * kNW), kBLD = kBN / (8 * kNW);   // loads per wave per stage
-constexpr int kLPW = kALD + kBLD;
-constexpr int kStage = (kBM + kBN) * BK * 2;             // bytes
-constexpr int kLds = kS * kStage;                        // 128 KB
-constexpr int kOld = kBN + 4;                            // padded row of the fp32 tile
-constexpr int kQ = kThreads / kBM;                       // threads per row (4)
+constexpr int kOld = kBN + 4;   // padded row of the fp32 tile
 constexpr int kMaxRanges = 256;
-static_assert(kBM * kOld * 4 <= kLds, "fp32 tile fits the stages");
-static_assert(kBM * kQ * 16 * 8 <= kLds, "the rows' lists fit the stages");
-static_assert(kQ == 4 && kBN % kQ == 0, "four threads per row");
 static_assert(kBN == kHeadBlock, "statistics are kept per token block");
+template <int BM>
+struct HeadTile {
+  static constexpr int kBM = BM;
+  static constexpr int kWcol = BM == 128 ? 4 : 2;   // waves along the tokens
+  static constexpr int kWM = kBM / (kNW / kWcol), kWN = kBN / kWcol;
+  static constexpr int kFM = kWM / 16, kFN = kWN / 16;
+  static constexpr int kALD = kBM / (8 * kNW), kBLD = kBN / (8 * kNW);   // loads per wave per stage
+  static constexpr int kLPW = kALD + kBLD;
+  static constexpr int kStage = (kBM + kBN) * BK * 2;   // bytes
+  static constexpr int kS = BM == 128 ? 4 : 3;
+  static constexpr int kLds = kS * kStage;
+  static constexpr int kQ = kThreads / kBM;   // threads per row
+  static constexpr int kCpt = 16 / kQ;        // candidates (statistics) and output keys per thread
+  static_assert(BM == 128 || BM == 256, "row tile");
+  static_assert(kBM * kOld * 4 <= kLds, "fp32 tile fits the stages");
+  static_assert(kBM * kQ * 16 * 8 + kBM * 16 * 8 <= kLds, "the rows' lists and results fit the stages");
+  static_assert(kQ == 2 || kQ == 4, "threads per row");
+};
 
 // Insert key x into the list l[0] > l[1] > ... > l[15] (0 = empty) when it
 // is larger than l[15]: every entry moves down one place past x.
@@ -79,10 +93,16 @@ __device__ __forceinline__ void insert16(uint64_t (&l)[16], uint64_t x) {
 // KEEP = 0 (statistics for rejection verification): per row and 128-token
 // block the online-softmax partial hs.stats, and the logits of the row's
 // candidates (hs.zc) and drafted token (hs.zx) as their blocks go by.
-template <int KEEP>
+template <int KEEP, int BM>
 __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     const uint16_t* __restrict__ h, int M, const uint16_t* __restrict__ emb, int64_t vocab, int K,
     int mblocks, int nranges, int nblocks, int xcd_groups, uint64_t* __restrict__ part, HeadStats hs) {
+  using TT = HeadTile<BM>;
+  constexpr int kBM = TT::kBM, kWcol = TT::kWcol, kWM = TT::kWM, kWN = TT::kWN, kFM = TT::kFM, kFN = TT::kFN;
+  constexpr int kALD = TT::kALD, kBLD = TT::kBLD, kLPW = TT::kLPW, kStage = TT::kStage, kS = TT::kS;
+  constexpr int kQ = TT::kQ, kCpt = TT::kCpt;
+  // one bit per column of a thread's share of a token block
+  using Mask = typename std::conditional<(kBN / kQ > 32), uint64_t, uint32_t>::type;
   const int bid = blockIdx.x;
   int mb, nr;
   if (xcd_groups) {   // nranges % 8 == 0: the row blocks of a token range share an XCD
@@ -135,14 +155,16 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
   float* tile = (float*)dyn_lds;
   // statistics mode: this thread's four candidates of its row (ranks
   // 4 q .. 4 q + 3) and, for q = 0, the drafted token
-  int32_t cid[4] = {-1, -1, -1, -1};
+  int32_t cid[kCpt];
+#pragma unroll
+  for (int i = 0; i < kCpt; ++i) cid[i] = -1;
   int32_t xt = -1;
   if constexpr (KEEP == 0) {
     const int r = m0 + my_row, b = r / (hs.T + 1), t = r % (hs.T + 1);
     if (r < M && t < hs.T) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = my_q * 4 + i;
+      for (int i = 0; i < kCpt; ++i) {
+        const int k = my_q * kCpt + i;
         if (k < hs.K) cid[i] = hs.cand[((int64_t)b * hs.T + t) * hs.K + k];
       }
       if (my_q == 0) xt = hs.xtok[(int64_t)b * hs.T + t];
@@ -211,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
         for (int e = 0; e < 4; ++e)
           tile[(wm * kWM + i * 16 + fq * 4 + e) * kOld + wn * kWN + j * 16 + fr] = acc[i][j][e];
     __syncthreads();
-    // The row's threshold: the largest of its four threads' 16th keys (the
+    // The row's threshold: the largest of its threads' 16th keys (the
     // row has 16 keys at least that large, so no key at or below it can be
     // among its 16 best).  One fp32 compare per value against the
     // threshold's value marks the few that may pass; only those are made
@@ -223,8 +245,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     const int ncols = m0 + my_row < M ? wrows : 0;
     if constexpr (KEEP == 0) {
       // the block's online-softmax partial of this row: each thread over its
-      // columns, then the row's four threads combined (symmetrically: all
-      // four hold the same result)
+      // columns, then the row's threads combined (symmetrically: all of
+      // them hold the same result)
       float v[kBN / kQ];
 #pragma unroll
       for (int j = 0; j < kBN / kQ; ++j) v[j] = trow[my_q + kQ * j];
@@ -243,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
           if (my_q + kQ * j < ncols && v[j] == v[j]) sum += v[j] == m ? 1.f : exp2f((v[j] - m) * hs.c);
       }
 #pragma unroll
-      for (int msk = 1; msk <= 2; msk <<= 1) {
+      for (int msk = 1; msk < kQ; msk <<= 1) {
         const uint64_t k2 = shfl_xor_u64(mk, msk);
         const float s2 = __shfl_xor(sum, msk);
         uint64_t ka = mk < k2 ? mk : k2, kb = mk < k2 ? k2 : mk;
@@ -261,30 +283,29 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
         hs.stats[(int64_t)r * nblocks + nb] = bs;
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (cid[i] >= n0 && cid[i] < n0 + ncols) hs.zc[(int64_t)r * hs.K + my_q * 4 + i] = trow[cid[i] - n0];
+      for (int i = 0; i < kCpt; ++i)
+        if (cid[i] >= n0 && cid[i] < n0 + ncols) hs.zc[(int64_t)r * hs.K + my_q * kCpt + i] = trow[cid[i] - n0];
       if (xt >= n0 && xt < n0 + ncols) hs.zx[r] = trow[xt - n0];
       __syncthreads();   // the tile is read before the next block's stages overwrite it
       continue;
     }
     uint64_t thr = best[KEEP > 0 ? KEEP - 1 : 0];
-    {
-      const uint64_t o1 = shfl_xor_u64(thr, 1);
-      thr = o1 > thr ? o1 : thr;
-      const uint64_t o2 = shfl_xor_u64(thr, 2);
-      thr = o2 > thr ? o2 : thr;
+#pragma unroll
+    for (int msk = 1; msk < kQ; msk <<= 1) {
+      const uint64_t o = shfl_xor_u64(thr, msk);
+      thr = o > thr ? o : thr;
     }
     const float tv = thr ? key_value(thr) : -INFINITY;
     float v[kBN / kQ];
 #pragma unroll
     for (int j = 0; j < kBN / kQ; ++j) v[j] = trow[my_q + kQ * j];
-    uint32_t mask = 0u;
+    Mask mask = 0;
 #pragma unroll
     for (int j = 0; j < kBN / kQ; ++j)
-      mask |= (my_q + kQ * j < ncols && v[j] >= tv) ? (1u << j) : 0u;   // NaN never passes
+      mask |= (my_q + kQ * j < ncols && v[j] >= tv) ? ((Mask)1 << j) : (Mask)0;   // NaN never passes
     while (mask) {
-      const int j = __builtin_ctz(mask);
-      mask &= mask - 1u;
+      const int j = sizeof(Mask) == 8 ? __builtin_ctzll((uint64_t)mask) : __builtin_ctz((uint32_t)mask);
+      mask &= mask - 1;
       const int c = my_q + kQ * j;
       const uint64_t key = make_key(trow[c], (uint32_t)(n0 + c));
       if constexpr (KEEP == 16) {
@@ -298,22 +319,22 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
 
   if constexpr (KEEP == 0) return;
   if constexpr (KEEP == 1) {
-    // the row's argmax key of the range: the largest of its four threads'
+    // the row's argmax key of the range: the largest of its threads'
     uint64_t m = best[0];
-    const uint64_t o1 = shfl_xor_u64(m, 1);
-    m = o1 > m ? o1 : m;
-    const uint64_t o2 = shfl_xor_u64(m, 2);
-    m = o2 > m ? o2 : m;
+#pragma unroll
+    for (int msk = 1; msk < kQ; msk <<= 1) {
+      const uint64_t o = shfl_xor_u64(m, msk);
+      m = o > m ? o : m;
+    }
     if (my_q == 0 && m0 + my_row < M) part[(int64_t)(m0 + my_row) * nranges + nr] = m;
     return;
   }
-  // the four lists of each row, ranked against each other
+  // the Q lists of each row, ranked against each other
   uint64_t* lists = (uint64_t*)dyn_lds;   // [kBM][kQ * 16]
 #pragma unroll
   for (int i = 0; i < KEEP; ++i) lists[my_row * (kQ * 16) + my_q * 16 + i] = best[i];
   __syncthreads();
   uint64_t* out16 = lists + kBM * kQ * 16;   // [kBM][16], after the lists
-  static_assert(kBM * kQ * 16 * 8 + kBM * 16 * 8 <= kLds, "lists and results fit");
   if (my_q == 0)
 #pragma unroll
     for (int i = 0; i < 16; ++i) out16[my_row * 16 + i] = 0ull;
@@ -328,11 +349,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
     if (rank < 16) out16[my_row * 16 + rank] = key;
   }
   __syncthreads();
-  // rows of the block that exist: 16 keys each, 4 threads per row
+  // rows of the block that exist: 16 keys each, kQ threads per row
   if (m0 + my_row < M) {
     uint64_t* dst = part + ((int64_t)(m0 + my_row) * nranges + nr) * 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[my_q * 4 + i] = out16[my_row * 16 + my_q * 4 + i];
+    for (int i = 0; i < kCpt; ++i) dst[my_q * kCpt + i] = out16[my_row * 16 + my_q * kCpt + i];
   }
 }
 
@@ -438,18 +459,44 @@ __global__ __launch_bounds__(kFinalThreads) void greedy_head_final_kernel(const 
   if (lane <= T) out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? x : (lane == n ? y : -1);
 }
 
-bool g_lds_set = false;
-bool g_lds_set1 = false;
-bool g_lds_set0 = false;
+// Launch lmhead_topk_kernel<KEEP, BM> over the plan's grid (its dynamic-LDS
+// limit raised on first use).
+template <int KEEP, int BM>
+hipError_t launch_head_tiles(const void* h, int M, const void* emb, int64_t vocab, int d, const LmHeadPlan& plan,
+                             uint64_t* part, const HeadStats& hs, const char* tag, hipStream_t stream) {
+  constexpr int kLds = HeadTile<BM>::kLds;
+  static bool lds_set = false;
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<KEEP, BM>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
+    if (e != hipSuccess) return e;
+    lds_set = true;
+  }
+  ProfileScope ps(tag, stream);
+  return launch(lmhead_topk_kernel<KEEP, BM>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
+                stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks, plan.nranges,
+                plan.nblocks, plan.xcd_groups, part, hs);
+}
+
+template <int KEEP>
+hipError_t launch_head(const void* h, int M, const void* emb, int64_t vocab, int d, const LmHeadPlan& plan,
+                       uint64_t* part, const HeadStats& hs, const char* tag, hipStream_t stream) {
+  return plan.bm == 256 ? launch_head_tiles<KEEP, 256>(h, M, emb, vocab, d, plan, part, hs, tag, stream)
+                        : launch_head_tiles<KEEP, 128>(h, M, emb, vocab, d, plan, part, hs, tag, stream);
+}
 
 }  // namespace
 
 LmHeadPlan lmhead_plan(int M, int64_t vocab, int d, int keep) {
   (void)d;
   LmHeadPlan p;
-  p.mblocks = (M + kBM - 1) / kBM;
+  // 256-row tiles where they add no padding rows over 128-row ones (and from
+  // 1,024 rows on, where the extra padding is at most 1/8), else 128
+  const int64_t pad128 = ((int64_t)M + 127) / 128 * 128, pad256 = ((int64_t)M + 255) / 256 * 256;
+  p.bm = (M > 128 && pad256 == pad128) || M >= 1024 ? 256 : 128;
+  p.mblocks = (M + p.bm - 1) / p.bm;
   p.nblocks = (int)((vocab + kBN - 1) / kBN);
-  // about one work-group per CU (each holds 96 KB of LDS and 8 waves)
+  // about one work-group per CU (each holds 128 or 144 KB of LDS and 8 waves)
   int nr = 256 / (p.mblocks > 0 ? p.mblocks : 1);
   if (nr < 1) nr = 1;
   if (nr > p.nblocks) nr = p.nblocks;
@@ -466,18 +513,7 @@ hipError_t launch_lmhead_topk(const void* h, const void* emb, int64_t vocab, int
                               hipStream_t stream) {
   if (M == 0) return hipSuccess;
   uint64_t* part = (uint64_t*)ws;
-  if (!g_lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    g_lds_set = true;
-  }
-  {
-    ProfileScope ps("lmhead_topk", stream);
-    DF2_TRY(launch(lmhead_topk_kernel<16>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
-                   stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
-                   plan.nranges, plan.nblocks, plan.xcd_groups, part, HeadStats{}));
-  }
+  DF2_TRY(launch_head<16>(h, M, emb, vocab, d, plan, part, HeadStats{}, "lmhead_topk", stream));
   ProfileScope ps("lmhead_merge", stream);
   DF2_TRY(launch(lmhead_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), 0, stream, ps, part,
                  plan.nranges, k, out_idx, out_val));
@@ -490,18 +526,7 @@ hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t voc
   if (B == 0) return hipSuccess;
   const int M = B * (T + 1);
   uint64_t* part = (uint64_t*)ws;
-  if (!g_lds_set1) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<1>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    g_lds_set1 = true;
-  }
-  {
-    ProfileScope ps("head_argmax", stream);
-    DF2_TRY(launch(lmhead_topk_kernel<1>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
-                   stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks,
-                   plan.nranges, plan.nblocks, plan.xcd_groups, part, HeadStats{}));
-  }
+  DF2_TRY(launch_head<1>(h, M, emb, vocab, d, plan, part, HeadStats{}, "head_argmax", stream));
   ProfileScope ps("greedy_head_final", stream);
   DF2_TRY(launch(greedy_head_final_kernel, dim3((unsigned)B), dim3(kFinalThreads), 0, stream, ps, part, plan.nranges,
                  path_tok, T, accept_len, out_tok));
@@ -511,16 +536,7 @@ hipError_t launch_verify_greedy_head(const void* h, const void* emb, int64_t voc
 hipError_t launch_head_stats(const void* h, const void* emb, int64_t vocab, int M, int d, const HeadStats& hs,
                              const LmHeadPlan& plan, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (!g_lds_set0) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_topk_kernel<0>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-    if (e != hipSuccess) return e;
-    g_lds_set0 = true;
-  }
-  ProfileScope ps("head_stats", stream);
-  DF2_TRY(launch(lmhead_topk_kernel<0>, dim3((unsigned)(plan.mblocks * plan.nranges)), dim3(kThreads), kLds,
-                 stream, ps, (const uint16_t*)h, M, (const uint16_t*)emb, vocab, d, plan.mblocks, plan.nranges,
-                 plan.nblocks, plan.xcd_groups, (uint64_t*)nullptr, hs));
+  DF2_TRY(launch_head<0>(h, M, emb, vocab, d, plan, (uint64_t*)nullptr, hs, "head_stats", stream));
   return hipGetLastError();
 }
 
