@@ -154,7 +154,7 @@ hipError_t launch_dynconv2(const void* x, const void* x_prev, const void* w, con
 
 // ---- drafter LM head fused with the top-K ----------------------------------
 struct LmHeadPlan {
-  int bm;           // rows of h per tile: 128 or 256
+  int bm;           // rows of h per tile: 64, 128 or 256
   int mblocks;      // bm-row blocks of h
   int nblocks;      // 128-token blocks of the vocabulary
   int nranges;      // token ranges (work-groups per row block)

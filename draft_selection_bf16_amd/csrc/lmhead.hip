@@ -51,7 +51,10 @@ using mfma::vmcnt_imm;
 // LDS stages.  BM = 128: waves 2 x 4 (64 x 32 each), 4 stages (128 KB), four
 // threads per row in the epilogues; BM = 256: waves 4 x 2 (64 x 64 each: half
 // the fragment bytes per MFMA, and a token block's rows are fetched by half
-// as many work-groups), 3 stages (144 KB), two threads per row.
+// as many work-groups), 3 stages (144 KB), two threads per row; BM = 64 (a
+// few rows: the head is streamed from memory, and the padding rows' MFMAs
+// halve): waves 2 x 4 (32 x 32 each), 6 stages (144 KB: five K-tiles of
+// copies in flight), eight threads per row.
 constexpr int kBN = 128, kNW = 8;
 constexpr int kThreads = kNW * 64;
 constexpr int kOld = kBN + 4;   // padded row of the fp32 tile
@@ -60,20 +63,20 @@ static_assert(kBN == kHeadBlock, "statistics are kept per token block");
 template <int BM>
 struct HeadTile {
   static constexpr int kBM = BM;
-  static constexpr int kWcol = BM == 128 ? 4 : 2;   // waves along the tokens
+  static constexpr int kWcol = BM == 256 ? 2 : 4;   // waves along the tokens
   static constexpr int kWM = kBM / (kNW / kWcol), kWN = kBN / kWcol;
   static constexpr int kFM = kWM / 16, kFN = kWN / 16;
   static constexpr int kALD = kBM / (8 * kNW), kBLD = kBN / (8 * kNW);   // loads per wave per stage
   static constexpr int kLPW = kALD + kBLD;
   static constexpr int kStage = (kBM + kBN) * BK * 2;   // bytes
-  static constexpr int kS = BM == 128 ? 4 : 3;
+  static constexpr int kS = BM == 64 ? 6 : (BM == 128 ? 4 : 3);
   static constexpr int kLds = kS * kStage;
   static constexpr int kQ = kThreads / kBM;   // threads per row
   static constexpr int kCpt = 16 / kQ;        // candidates (statistics) and output keys per thread
-  static_assert(BM == 128 || BM == 256, "row tile");
+  static_assert(BM == 64 || BM == 128 || BM == 256, "row tile");
   static_assert(kBM * kOld * 4 <= kLds, "fp32 tile fits the stages");
   static_assert(kBM * kQ * 16 * 8 + kBM * 16 * 8 <= kLds, "the rows' lists and results fit the stages");
-  static_assert(kQ == 2 || kQ == 4, "threads per row");
+  static_assert(kQ == 2 || kQ == 4 || kQ == 8, "threads per row");
 };
 
 // Insert key x into the list l[0] > l[1] > ... > l[15] (0 = empty) when it
@@ -153,8 +156,8 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
 #pragma unroll
   for (int i = 0; i < (KEEP > 0 ? KEEP : 1); ++i) best[i] = 0ull;
   float* tile = (float*)dyn_lds;
-  // statistics mode: this thread's four candidates of its row (ranks
-  // 4 q .. 4 q + 3) and, for q = 0, the drafted token
+  // statistics mode: this thread's 16 / Q candidates of its row (ranks
+  // q 16 / Q onwards) and, for q = 0, the drafted token
   int32_t cid[kCpt];
 #pragma unroll
   for (int i = 0; i < kCpt; ++i) cid[i] = -1;
@@ -199,6 +202,11 @@ __global__ __launch_bounds__(kThreads) void lmhead_topk_kernel(
       for (int j = 0; j < kFN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kS - 1; ++t) issue(t);
+    // 256-row tiles: the waves in two alternating groups (mfma_tile.h; 2 %
+    // faster here, no gain with 128-row tiles)
+    if constexpr (BM == 256) {
+      mfma::pingpong_loop<kS, kFM, kFN, kLPW, kStage>(dyn_lds, issue, ao, bo, acc, nkt, wave / 4);
+    } else
     for (int t = 0; t < nkt; ++t) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm((kS - 2) * kLPW));
       __builtin_amdgcn_s_barrier();
@@ -481,6 +489,7 @@ hipError_t launch_head_tiles(const void* h, int M, const void* emb, int64_t voca
 template <int KEEP>
 hipError_t launch_head(const void* h, int M, const void* emb, int64_t vocab, int d, const LmHeadPlan& plan,
                        uint64_t* part, const HeadStats& hs, const char* tag, hipStream_t stream) {
+  if (plan.bm == 64) return launch_head_tiles<KEEP, 64>(h, M, emb, vocab, d, plan, part, hs, tag, stream);
   return plan.bm == 256 ? launch_head_tiles<KEEP, 256>(h, M, emb, vocab, d, plan, part, hs, tag, stream)
                         : launch_head_tiles<KEEP, 128>(h, M, emb, vocab, d, plan, part, hs, tag, stream);
 }
@@ -490,10 +499,11 @@ hipError_t launch_head(const void* h, int M, const void* emb, int64_t vocab, int
 LmHeadPlan lmhead_plan(int M, int64_t vocab, int d, int keep) {
   (void)d;
   LmHeadPlan p;
-  // 256-row tiles where they add no padding rows over 128-row ones (and from
-  // 1,024 rows on, where the extra padding is at most 1/8), else 128
+  // 64-row tiles up to 64 rows; 256-row tiles where they add no padding rows
+  // over 128-row ones (and from 1,024 rows on, where the extra padding is at
+  // most 1/8); else 128
   const int64_t pad128 = ((int64_t)M + 127) / 128 * 128, pad256 = ((int64_t)M + 255) / 256 * 256;
-  p.bm = (M > 128 && pad256 == pad128) || M >= 1024 ? 256 : 128;
+  p.bm = M <= 64 ? 64 : ((M > 128 && pad256 == pad128) || M >= 1024 ? 256 : 128);
   p.mblocks = (M + p.bm - 1) / p.bm;
   p.nblocks = (int)((vocab + kBN - 1) / kBN);
   // about one work-group per CU (each holds 128 or 144 KB of LDS and 8 waves)
