@@ -78,11 +78,13 @@ def _inputs(rows, V, d, seed, scale_h=1.0):
 
 
 @pytest.mark.parametrize("rows,V,d,k", [(133, 5003, 640, 16), (1, 131, 64, 16), (7, 20011, 256, 16),
-                                        (300, 2500, 128, 5), (64, 17, 192, 16), (260, 1000, 64, 1)])
+                                        (300, 2500, 128, 5), (64, 17, 192, 16), (260, 1000, 64, 1),
+                                        (1100, 3001, 128, 16)])
 def test_lm_head_topk_small_shapes(rows, V, d, k):
-    """Ragged row blocks (133 = 128 + 5, 260), a ragged last token block,
-    fewer tokens than one block (17, 131), k < 16, d from 64 to 640; every
-    row checked."""
+    """Every row-tile height: 64 rows (1, 7, 64), 128 (260, 300), 256 (133:
+    one ragged block; 1,100: five blocks, the last ragged, 48 token ranges);
+    a ragged last token block, fewer tokens than one block (17, 131), k < 16,
+    d from 64 to 640; every row checked."""
     print(f"[case] lm_head_topk rows={rows} V={V} d={d} k={k}", flush=True)
     h, E = _inputs(rows, V, d, rows + V)
     gi, gv = _gpu(h, E, k)
@@ -175,8 +177,10 @@ def _check_verify_head(h, E, path, ga, go, reqs, label):
     assert near <= max(1, len(reqs) // 8)
 
 
-@pytest.mark.parametrize("B,T,V,d", [(3, 7, 5003, 640), (5, 15, 2049, 128), (2, 1, 300, 64)])
+@pytest.mark.parametrize("B,T,V,d", [(3, 7, 5003, 640), (5, 15, 2049, 128), (2, 1, 300, 64), (25, 7, 3001, 128)])
 def test_verify_greedy_head_small(B, T, V, d):
+    """Rows B (T + 1) = 24 and 4 (64-row tiles), 80 (128), 200 (one ragged
+    256-row block)."""
     g = torch.Generator().manual_seed(B * 100 + T)
     h = torch.randn(B, T + 1, d, generator=g).to(torch.bfloat16)
     E = (0.02 * torch.randn(V, d, generator=g)).to(torch.bfloat16)

@@ -144,8 +144,10 @@ def _hidden(B, T, E, seed):
 
 @pytest.mark.parametrize("B,T,V,d,K,tau", [(4, 7, 5003, 640, 16, 1.0), (5, 15, 2049, 128, 16, 0.7),
                                            (2, 1, 300, 64, 5, 1.3), (3, 3, 129, 64, 16, 1.0),
-                                           (6, 7, 20011, 256, 8, 0.5)])
+                                           (6, 7, 20011, 256, 8, 0.5), (25, 7, 3001, 128, 16, 0.8)])
 def test_verify_reject_head_small(B, T, V, d, K, tau):
+    """Rows B (T + 1) up to 64 (64-row tiles), 80 (128), 200 (one ragged
+    256-row block)."""
     g = torch.Generator().manual_seed(B * 100 + T)
     E = (0.02 * torch.randn(V, d, generator=g)).to(torch.bfloat16)
     h = _hidden(B, T, E, B * 7 + T)
