@@ -11,8 +11,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
   run_tile<BM, BN, S, NW, ISSUE>(Pb, blockIdx.x, gridDim.x);
 }
 
-// (the fields as separate arguments: an aggregate passed by value is not
-// preloaded into SGPRs, scalars and pointers are)
+// One dense problem, its fields passed as separate arguments: an aggregate
+// passed by value is not preloaded into SGPRs, scalars and pointers are
+// (all 48 bytes of these arrive preloaded).
 template <int BM, int BN, int S, int NW, int ISSUE>
 __global__ __launch_bounds__(NW * 64) void gemm_dense_kernel(const uint16_t* x, const uint16_t* w, float* out,
                                                              int M, int N, int K, int ksplit, int ldx, int ldo) {
