@@ -219,6 +219,7 @@ TopkPlan fused_topk_plan(int64_t rows, int64_t vocab, int k) {
     p.chunk = chunk;
     p.ws_bytes = align256((size_t)rows * (size_t)p.splits * 16 * sizeof(uint64_t));
   }
+  p.small = 0;   // the persistent launch runs the streaming chunk body
   return p;
 }
 

@@ -56,6 +56,7 @@ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct TopkPlan {
   int splits;       // work-groups per row
   int64_t chunk;    // elements per split (multiple of 64)
+  int small;        // 1: the short-chunk kernel (chunk <= 8192)
   size_t ws_bytes;  // partial-key buffer
 };
 TopkPlan topk_plan(int64_t rows, int64_t vocab, int k);

@@ -38,6 +38,8 @@ using namespace topkd;
 
 constexpr int kWaves = 8;        // waves per work-group
 constexpr int kThreads = kWaves * kWave;
+constexpr int kSmallEpt = 16;    // entries per thread of the short-chunk path
+constexpr int64_t kSmallChunk = (int64_t)kThreads * kSmallEpt;
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
@@ -45,6 +47,14 @@ __global__ __launch_bounds__(kThreads) void topk_chunk_kernel(
     int32_t* __restrict__ out_idx, float* __restrict__ out_val, uint64_t* __restrict__ part) {
   __shared__ TopkChunkLds<kWaves> L;
   topk_chunk_body<E, kWaves>(logits, vocab, splits, chunk, k, out_idx, out_val, part, blockIdx.x, L);
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void topk_small_kernel(
+    const void* __restrict__ logits, int64_t vocab, int splits, int64_t chunk, int k,
+    int32_t* __restrict__ out_idx, float* __restrict__ out_val, uint64_t* __restrict__ part) {
+  __shared__ TopkSmallLds<kWaves> L;
+  topk_small_body<E, kWaves, kSmallEpt>(logits, vocab, splits, chunk, k, out_idx, out_val, part, blockIdx.x, L);
 }
 
 // one row per wave
@@ -74,7 +84,21 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   // (2 instead of 4), 56 rows 100.3 against 101.1 (4 instead of 8), 15 rows
   // 55.8 against 58.6 (17 instead of 18).  Chunks stay >= 8192 entries and
   // <= 32 per row (the merge holds at most 512 keys per row).
+  // With few rows, chunks of at most kSmallChunk entries on the short-chunk
+  // path instead (one round of loads per work-group).
   constexpr int64_t kCUs = 256;   // MI355X
+  constexpr int64_t kSmallMaxGroups = 512;
+  const int64_t s_small = (vocab + kSmallChunk - 1) / kSmallChunk;
+  if (s_small <= 32 && rows * s_small <= kSmallMaxGroups) {
+    int64_t chunk = (vocab + s_small - 1) / s_small;
+    chunk = (chunk + 63) / 64 * 64;   // <= kSmallChunk (a multiple of 64)
+    TopkPlan p;
+    p.splits = (int)((vocab + chunk - 1) / chunk);
+    p.chunk = chunk;
+    p.small = 1;
+    p.ws_bytes = p.splits > 1 ? align256((size_t)rows * (size_t)p.splits * 16 * sizeof(uint64_t)) : 0;
+    return p;
+  }
   int64_t want = kCUs / (rows > 0 ? rows : 1);
   int64_t max_by_size = vocab / 8192;
   int64_t s = want < max_by_size ? want : max_by_size;
@@ -86,6 +110,7 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   TopkPlan p;
   p.splits = (int)s;
   p.chunk = chunk;
+  p.small = 0;
   p.ws_bytes = s > 1 ? align256((size_t)rows * (size_t)s * 16 * sizeof(uint64_t)) : 0;
   return p;
 }
@@ -96,7 +121,18 @@ hipError_t launch_topk(const void* logits, int dt, int64_t rows, int64_t vocab, 
   if (rows == 0) return hipSuccess;
   uint64_t* part = (uint64_t*)ws;
   dim3 grid((unsigned)(rows * plan.splits)), block(kThreads);
-  {
+  if (plan.small) {
+    ProfileScope ps("topk_chunk", stream);
+    if (dt == 0)
+      DF2_TRY(launch(topk_small_kernel<float>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                           out_idx, out_val, part));
+    else if (dt == 1)
+      DF2_TRY(launch(topk_small_kernel<Bf16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                          out_idx, out_val, part));
+    else
+      DF2_TRY(launch(topk_small_kernel<F16>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,
+                                                         out_idx, out_val, part));
+  } else {
     ProfileScope ps("topk_chunk", stream);
     if (dt == 0)
       DF2_TRY(launch(topk_chunk_kernel<float>, grid, block, 0, stream, ps, logits, vocab, plan.splits, plan.chunk, k,

@@ -355,6 +355,74 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
 }
 
 // LDS of one (row, chunk) work-group of NW waves.
+// Rank the ns <= kThreads pooled keys ssurv[0..ns) (distinct) and put the 16
+// best in sbest[0..16) (slots past ns keep 0); ends with a work-group
+// barrier.  rank = number of larger keys: the list is padded with empty
+// keys to a multiple of 16; P = kThreads / n16 threads share a key, each
+// counting the larger keys in its 1/P of the list (two keys per LDS load,
+// eight loads in flight), the counts meeting in LDS.
+template <int kThreads>
+__device__ __forceinline__ void rank_pool(uint64_t* ssurv, int* srank, int ns, uint64_t* sbest) {
+  const int tid = threadIdx.x;
+  const int n16 = (ns + 15) & ~15;
+  if (tid < n16 - ns) ssurv[ns + tid] = 0ull;
+  srank[tid] = 0;
+  __syncthreads();
+  const int P = n16 > 0 ? kThreads / n16 : 1;   // >= 1
+  const int len = n16 / P > 16 ? ((n16 / P) + 15) & ~15 : 16;   // parts past n16 count nothing
+  const int part = tid / (n16 > 0 ? n16 : 1), i = tid - part * n16;
+  uint64_t key = 0ull;
+  if (part < P && i < ns) {
+    key = ssurv[i];
+    typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+    const int j1 = (part + 1) * len < n16 ? (part + 1) * len : n16;
+    int c = 0;
+    for (int j = part * len; j < j1; j += 16) {
+      u64x2 o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = *(const u64x2*)(ssurv + j + 2 * u);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c += (o[u][0] > key ? 1 : 0) + (o[u][1] > key ? 1 : 0);
+    }
+    if (c > 0) atomicAdd(&srank[i], c);
+  }
+  __syncthreads();
+  key = tid < ns ? ssurv[tid] : 0ull;
+  const int r = tid < ns ? srank[tid] : kThreads;
+  if (key != 0ull && r < 16) sbest[r] = key;
+  __syncthreads();
+}
+
+// Wave 0: the 16 best of the NW waves' lists smerge[w * 16 .. + 16) into
+// sbest (by rank: every key's number of larger keys).
+template <int NW>
+__device__ __forceinline__ void merge_wave_lists(const uint64_t* smerge, uint64_t* sbest, int lane) {
+  static_assert(NW % 4 == 0, "whole lanes of candidates");
+#pragma unroll
+  for (int c = 0; c < NW / 4; ++c) {
+    const uint64_t kc = smerge[c * kWave + lane];
+    const int rc = rank_in_lds<NW * 16>(kc, smerge);
+    if (kc != 0ull && rc < 16) sbest[rc] = kc;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Wave 0: the chunk's result -- the final k (index, value) pairs of the row
+// with one chunk per row, else the chunk's 16 keys for the merge.
+__device__ __forceinline__ void write_chunk_result(const uint64_t* sbest, int splits, int k, int64_t row,
+                                                   int split, int32_t* out_idx, float* out_val, uint64_t* part,
+                                                   int lane) {
+  if (splits == 1) {
+    if (lane < k) {
+      const uint64_t key = sbest[lane];
+      out_idx[row * k + lane] = (int32_t)key_index(key);
+      out_val[row * k + lane] = key_value(key);
+    }
+  } else if (lane < 16) {
+    part[((int64_t)row * splits + split) * 16 + lane] = sbest[lane];
+  }
+}
+
 template <int NW>
 struct TopkChunkLds {
   __attribute__((aligned(16))) uint64_t sbuf[NW][kCap];
@@ -467,38 +535,7 @@ __device__ __forceinline__ void topk_chunk_body(const void* __restrict__ logits,
   __syncthreads();
   const int ns = snsurv;   // the same in every wave
   if (ns <= kThreads) {
-    // rank = number of larger survivors (keys are distinct).  The list is
-    // padded with empty keys to a multiple of 16; P = 512 / n16 threads share
-    // a survivor, each counting the larger keys in its 1/P of the list (two
-    // keys per LDS load, eight loads in flight), the counts meeting in LDS.
-    const int tid = threadIdx.x;
-    const int n16 = (ns + 15) & ~15;
-    if (tid < n16 - ns) ssurv[ns + tid] = 0ull;
-    srank[tid] = 0;
-    __syncthreads();
-    const int P = n16 > 0 ? kThreads / n16 : 1;   // >= 1
-    const int len = n16 / P > 16 ? ((n16 / P) + 15) & ~15 : 16;   // parts past n16 count nothing
-    const int part = tid / (n16 > 0 ? n16 : 1), i = tid - part * n16;
-    uint64_t key = 0ull;
-    if (part < P && i < ns) {
-      key = ssurv[i];
-      typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
-      const int j1 = (part + 1) * len < n16 ? (part + 1) * len : n16;
-      int c = 0;
-      for (int j = part * len; j < j1; j += 16) {
-        u64x2 o[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = *(const u64x2*)(ssurv + j + 2 * u);
-#pragma unroll
-        for (int u = 0; u < 8; ++u) c += (o[u][0] > key ? 1 : 0) + (o[u][1] > key ? 1 : 0);
-      }
-      if (c > 0) atomicAdd(&srank[i], c);
-    }
-    __syncthreads();
-    key = tid < ns ? ssurv[tid] : 0ull;
-    const int r = tid < ns ? srank[tid] : kThreads;
-    if (key != 0ull && r < 16) sbest[r] = key;
-    __syncthreads();
+    rank_pool<kThreads>(ssurv, srank, ns, sbest);
     if (wave != 0) return;
   } else {
     // The 16 best keys of this wave: normally at most 64 keys are left, and
@@ -527,24 +564,117 @@ __device__ __forceinline__ void topk_chunk_body(const void* __restrict__ logits,
     __syncthreads();
     if (wave != 0) return;
     // wave 0: the 16 best of the NW x 16 candidates (NW / 4 per lane), by rank
-    static_assert(NW % 4 == 0, "whole lanes of candidates");
+    merge_wave_lists<NW>(smerge, sbest, lane);
+  }
+  write_chunk_result(sbest, splits, k, row, split, out_idx, out_val, part, lane);
+}
+
+// ---- short chunks (at most kThreads * EPT entries) ----------------------
+// With few rows every row is cut into many short chunks, and the streaming
+// filter above (priming, queues, compaction) costs more than the chunk's
+// one round of loads.  Here every thread loads its EPT entries at once
+// (entry e of thread t is lo + e * kThreads + t, so each load instruction
+// of a wave reads 64 consecutive entries), and
+//  * each wave takes as its bound the 16th largest of its lanes' maxima:
+//    16 lanes hold an entry at least that large, so the wave -- and the
+//    work-group -- has 16 entries at or above it;
+//  * the work-group's bound is the largest of the waves' bounds; the entries
+//    that reach it (a few dozen on these rows) are pooled in LDS and ranked
+//    as in the long path;
+//  * more than kThreads of them (massive ties) falls back to the exact
+//    per-wave 64-bit search and the merge of the NW x 16.
+template <int NW>
+struct TopkSmallLds {
+  __attribute__((aligned(16))) uint64_t ssurv[NW * kWave + 16];
+  int srank[NW * kWave];
+  __attribute__((aligned(16))) uint64_t smerge[NW * 16];
+  uint32_t swb[NW];
+  int snsurv;
+  uint64_t sbest[16];
+};
+
+template <typename E, int NW, int EPT>
+__device__ __forceinline__ void topk_small_body(const void* __restrict__ logits, int64_t vocab, int splits,
+                                                int64_t chunk, int k, int32_t* __restrict__ out_idx,
+                                                float* __restrict__ out_val, uint64_t* __restrict__ part, int bid,
+                                                TopkSmallLds<NW>& L) {
+  constexpr int kThreads = NW * kWave;
+  constexpr int VB = Vec<E>::value_bits;
+  const int wave = wave_id(), lane = lane_id(), tid = threadIdx.x;
+  const int64_t row = bid / splits;
+  const int split = bid % splits;
+  const int64_t lo = (int64_t)split * chunk;
+  const int64_t hi = lo + chunk < vocab ? lo + chunk : vocab;   // lo < hi
+  const int esz = sizeof(u32x4) / Vec<E>::n;
+  const void* rowp = (const char*)logits + row * vocab * esz;
+  // every load unconditional (clamped into the chunk), so all are in flight
+  uint32_t raw[EPT];
 #pragma unroll
-    for (int c = 0; c < NW / 4; ++c) {
-      const uint64_t kc = smerge[c * kWave + lane];
-      const int rc = rank_in_lds<NW * 16>(kc, smerge);
-      if (kc != 0ull && rc < 16) sbest[rc] = kc;
+  for (int e = 0; e < EPT; ++e) {
+    const int64_t i = lo + (int64_t)e * kThreads + tid;
+    raw[e] = Vec<E>::raw(rowp, i < hi ? i : hi - 1);
+  }
+  if (tid == 0) L.snsurv = 0;
+  if (tid < 16) L.sbest[tid] = 0ull;
+  // order values (0: outside the chunk or NaN, never a candidate)
+  uint32_t ord[EPT];
+  uint32_t lmax = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const float f = Vec<E>::get0(u32x4{raw[e], 0u, 0u, 0u});
+    const bool ok = lo + (int64_t)e * kThreads + tid < hi && f == f;
+    ord[e] = ok ? ord_of(f) : 0u;   // a number's order value is never 0
+    lmax = ord[e] > lmax ? ord[e] : lmax;
+  }
+  const uint32_t lm[1] = {lmax};
+  const uint32_t wb = value_cut16<VB, 1>(lm);   // 0: fewer than 16 lanes hold a number
+  if (lane == 0) L.swb[wave] = wb;
+  __syncthreads();
+  uint32_t bound = 0u;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) bound = L.swb[w] > bound ? L.swb[w] : bound;
+  bool keep[EPT];
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    keep[e] = ord[e] != 0u && ord[e] >= bound;
+    n += __popcll(ballot(keep[e]));
+  }
+  int base = 0;
+  if (lane == 0 && n > 0) base = atomicAdd(&L.snsurv, n);
+  base = __builtin_amdgcn_readfirstlane(base);
+  if (base + n <= kThreads) {
+    int off = base;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint64_t m = ballot(keep[e]);
+      if (keep[e]) L.ssurv[off + lanes_below(m)] = ((uint64_t)ord[e] << 32) |
+                                                   (uint64_t)(~(uint32_t)(lo + (int64_t)e * kThreads + tid));
+      off += __popcll(m);
     }
+  }
+  __syncthreads();
+  const int ns = L.snsurv;   // the same in every wave
+  if (ns <= kThreads) {
+    rank_pool<kThreads>(L.ssurv, L.srank, ns, L.sbest);
+    if (wave != 0) return;
+  } else {
+    uint64_t keys[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e)
+      keys[e] = ord[e] != 0u
+                    ? ((uint64_t)ord[e] << 32) | (uint64_t)(~(uint32_t)(lo + (int64_t)e * kThreads + tid))
+                    : 0ull;
+    uint64_t* mine16 = L.smerge + wave * 16;
+    if (lane < 16) mine16[lane] = 0ull;
     __builtin_amdgcn_wave_barrier();
+    const uint64_t t = kth16<EPT>(keys);
+    gather_at_least<EPT>(keys, t, mine16);   // the wave's 16 best (fewer if it holds fewer numbers)
+    __syncthreads();
+    if (wave != 0) return;
+    merge_wave_lists<NW>(L.smerge, L.sbest, lane);
   }
-  if (splits == 1) {
-    if (lane < k) {
-      const uint64_t key = sbest[lane];
-      out_idx[row * k + lane] = (int32_t)key_index(key);
-      out_val[row * k + lane] = key_value(key);
-    }
-  } else if (lane < 16) {
-    part[((int64_t)row * splits + split) * 16 + lane] = sbest[lane];
-  }
+  write_chunk_result(L.sbest, splits, k, row, split, out_idx, out_val, part, lane);
 }
 
 // One wave per row: merge splits * 16 keys (splits <= 32), each split's 16

@@ -201,6 +201,29 @@ def test_topk_one_chunk_per_row(dtype, V):
     assert np.array_equal(gv, ov)
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 151939), (torch.float16, 50001),
+                                     (torch.float32, 50003), (torch.bfloat16, 7000)])
+def test_topk_short_chunks_mixed_rows(dtype, V):
+    """Few rows, so rows are cut into chunks of at most 8,192 entries on the
+    short-chunk kernel (one round of loads per work-group): the same kinds of
+    rows as above -- constant and signed-zero rows take its exact fallback
+    for massive ties -- plus a row that is NaN except for 20 entries, so most
+    chunks hold fewer than 16 numbers; V = 7,000 is one chunk per row (no
+    merge)."""
+    z = _mixed_rows(17, V, seed=V + 1)
+    g = torch.Generator().manual_seed(V)
+    keep = torch.randperm(V, generator=g)[:20]
+    row = torch.full((V,), float("nan"))
+    row[keep] = torch.randn(20, generator=g)
+    z[16] = row
+    z = z.to(dtype)
+    gi, gv = _topk_gpu(dev(z), 16)
+    zo = torch.where(torch.isnan(z), torch.full_like(z, float("-inf")), z)
+    oi, ov = oracle.topk(zo, 16)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv, ov)
+
+
 # ----------------------------------------------------------------- pair scores
 def _pair_gpu(cand_idx, cand_val, last, E, h, wa, wb, wh, gate=0):
     B, T, K = cand_idx.shape
