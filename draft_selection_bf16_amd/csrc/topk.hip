@@ -85,9 +85,13 @@ TopkPlan topk_plan(int64_t rows, int64_t vocab, int k) {
   // 55.8 against 58.6 (17 instead of 18).  Chunks stay >= 8192 entries and
   // <= 32 per row (the merge holds at most 512 keys per row).
   // With few rows, chunks of at most kSmallChunk entries on the short-chunk
-  // path instead (one round of loads per work-group).
+  // path instead (one round of loads per work-group), up to about four
+  // work-groups per CU.  Per cycle against the long path: 7 rows (133
+  // work-groups) 41.5 against 45.6 us, 15 rows 49.6 against 52.4, 56 rows
+  // (1,064) 89.5 against 93.0; 120 rows (2,280) 80.6 against 76.5 and 224
+  // rows (4,256) 107 against 89.5 stay on the long path.
   constexpr int64_t kCUs = 256;   // MI355X
-  constexpr int64_t kSmallMaxGroups = 512;
+  constexpr int64_t kSmallMaxGroups = 1100;
   const int64_t s_small = (vocab + kSmallChunk - 1) / kSmallChunk;
   if (s_small <= 32 && rows * s_small <= kSmallMaxGroups) {
     int64_t chunk = (vocab + s_small - 1) / s_small;

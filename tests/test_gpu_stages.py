@@ -141,8 +141,9 @@ def test_topk_launch_shape_of_the_b32_blk16_workload():
                                   "b32_blk8_v151936"])
 def test_topk_small_batch_launch_shapes(name):
     """The drafter logits of the other batch x block points (15, 56, 120 and
-    224 rows of 151,936: 17, 4, 2 and 1 chunks per row, then the merge where
-    there is more than one), all rows compared."""
+    224 rows of 151,936: 19 short chunks per row for 15 and 56 rows, 2 and 1
+    streamed chunks for 120 and 224, then the merge where there is more than
+    one), all rows compared."""
     w = synth.WORKLOADS[name]
     z, _, _ = synth.drafter_logits(w, device=DEV)
     gi, gv = _topk_gpu(z, 16)
