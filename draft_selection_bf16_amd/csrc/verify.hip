@@ -118,15 +118,20 @@ __global__ __launch_bounds__(kThreads) void sumexp_part_kernel(const void* __res
   }
 }
 
-// one wave per request: row statistics, accept chain, decision record
+// Request b's decision, from one wave (lanes 0 .. 63): row statistics of
+// every position (lane t combines the chunk partials of row t), the accept
+// chain, the decision record.  With `write` it also stores accept_len, the
+// accepted drafts and -1 after the resampled slot (out_tok[n] is left to
+// the draw), and the record in dec[b].
 template <int DT>
-__global__ __launch_bounds__(64) void reject_decide_kernel(
-    const void* __restrict__ z, int64_t vocab, const RowPart* __restrict__ part, int splits, int T,
-    int K, float c, const int32_t* __restrict__ path_tok, const int32_t* __restrict__ path_rank,
-    const float* __restrict__ q, const uint64_t* __restrict__ seed_dev, int b0,
-    int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok, DecRec* __restrict__ dec) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  const uint64_t seed = seed_dev[0];
+__device__ __forceinline__ DecRec decide_request(const void* __restrict__ z, int64_t vocab,
+                                                 const RowPart* __restrict__ part, int splits, int T, int K, float c,
+                                                 const int32_t* __restrict__ path_tok,
+                                                 const int32_t* __restrict__ path_rank, const float* __restrict__ q,
+                                                 uint64_t seed, int b0, int b, bool write,
+                                                 int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok,
+                                                 DecRec* __restrict__ dec) {
+  const int lane = threadIdx.x & 63;
   // this lane's drafted token and its rank, requested with the row partials
   const int lt = lane < T ? lane : 0;
   const int32_t x = path_tok[(int64_t)b * T + lt];
@@ -156,19 +161,22 @@ __global__ __launch_bounds__(64) void reject_decide_kernel(
   uint32_t klo = __shfl((uint32_t)k, n), khi = __shfl((uint32_t)(k >> 32), n);
   float sn = __shfl(s, n);
   uint64_t knn = ((uint64_t)khi << 32) | klo;
-  if (lane == 0) {
-    accept_len[b] = n;
-    DecRec d;
-    d.n = n;
-    d.argmax = knn ? (int)key_index(knn) : 0;
-    d.m = key_value(knn);
-    d.s = sn;
-    d.u2 = cycle_uniform(seed, b0 + b, n, 2);
-    d.pad = 0.f;
-    dec[b] = d;
+  DecRec d;
+  d.n = n;
+  d.argmax = knn ? (int)key_index(knn) : 0;
+  d.m = key_value(knn);
+  d.s = sn;
+  d.u2 = cycle_uniform(seed, b0 + b, n, 2);
+  d.pad = 0.f;
+  if (write) {
+    if (lane == 0) {
+      accept_len[b] = n;
+      dec[b] = d;
+    }
+    if (lane <= T && lane != n)
+      out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? x : -1;
   }
-  if (lane <= T && lane != n)
-    out_tok[(int64_t)b * (T + 1) + lane] = lane < n ? x : -1;
+  return d;
 }
 
 // residual weight of entry v of the resampled row
@@ -237,16 +245,28 @@ __device__ __forceinline__ void residual_fill(Residual& R, const DecRec& d, int 
   }
 }
 
+// Work-group (b, ch): request b's decision (every work-group of the request
+// takes it the same way; chunk 0's stores it and the request's outputs), then
+// the residual mass of vocabulary chunk ch of the resampled row.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void residual_chunk_kernel(
-    const void* __restrict__ z, int64_t vocab, int T, int K, float c, int rchunks, int64_t rchunk,
-    const DecRec* __restrict__ dec, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ q, float* __restrict__ rsum) {
+    const void* __restrict__ z, int64_t vocab, const RowPart* __restrict__ part, int splits, int T, int K, float c,
+    const int32_t* __restrict__ path_tok, const int32_t* __restrict__ path_rank,
+    const int32_t* __restrict__ cand_idx, const float* __restrict__ q, const uint64_t* __restrict__ seed_dev,
+    int b0, int rchunks, int64_t rchunk, int32_t* __restrict__ accept_len, int32_t* __restrict__ out_tok,
+    DecRec* __restrict__ dec, float* __restrict__ rsum) {
   __shared__ Residual R;
+  __shared__ DecRec sd;
   __shared__ float sred[kWaves];
   const int b = blockIdx.x / rchunks, ch = blockIdx.x % rchunks;
+  if (threadIdx.x < kWave) {
+    const DecRec d = decide_request<DT>(z, vocab, part, splits, T, K, c, path_tok, path_rank, q, seed_dev[0], b0, b,
+                                        ch == 0, accept_len, out_tok, dec);
+    if (threadIdx.x == 0) sd = d;
+  }
+  __syncthreads();
+  const DecRec d = sd;
   const int64_t lo = (int64_t)ch * rchunk, hi = lo + rchunk < vocab ? lo + rchunk : vocab;
-  const DecRec d = dec[b];
   const void* row = residual_row<DT>(z, vocab, T, b, d.n);
   residual_fill(R, d, T, K, c, b, cand_idx, q, lo, hi);
   __syncthreads();
@@ -476,15 +496,11 @@ static hipError_t reject_launch(const void* z, int64_t vocab, const int32_t* pat
         z, vocab, plan.splits, plan.chunk, c, part));
   }
   {
-    ProfileScope ps("reject_decide", stream);
-    DF2_TRY(launch(reject_decide_kernel<DT>, dim3(B), dim3(64), 0, stream, ps, z, vocab, part, plan.splits, T, K, c,
-                                                              path_tok, path_rank, q, seed_dev, b0,
-                                                              accept_len, out_tok, dec));
-  }
-  {
+    // the decision (accept chain) is taken inside the residual pass
     ProfileScope ps("residual_chunk", stream);
     DF2_TRY(launch(residual_chunk_kernel<DT>, dim3((unsigned)(B * plan.rchunks)), dim3(kThreads), 0, stream, ps,
-        z, vocab, T, K, c, plan.rchunks, plan.rchunk, dec, cand_idx, q, rsum));
+        z, vocab, part, plan.splits, T, K, c, path_tok, path_rank, cand_idx, q, seed_dev, b0, plan.rchunks,
+        plan.rchunk, accept_len, out_tok, dec, rsum));
   }
   ProfileScope ps("residual_find", stream);
   DF2_TRY(launch(residual_find_kernel<DT>, dim3(B), dim3(kThreads), 0, stream, ps,

@@ -410,9 +410,10 @@ int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t
  * the kernel with tag `kernel` records a start and a stop HIP event in its
  * own dispatch (hipExtLaunchKernel: the kernel's execution interval, without
  * stream-side overhead), for at most max_launches launches.  Tags:
- *   "topk_chunk", "topk_merge", "project_gemm", "pair_epilogue", "path",
- *   "argmax_part", "greedy_final", "sumexp_part", "reject_decide",
- *   "residual_chunk", "residual_find", "conv_gemm", "conv_epilogue", "philox",
+ *   "topk_chunk", "topk_merge", "project_gemm", "proj_reduce", "h_gemm",
+ *   "table_gemm", "pair_epilogue", "path", "argmax_part", "greedy_final",
+ *   "sumexp_part", "residual_chunk", "residual_find", "conv_gemm",
+ *   "conv_epilogue", "philox",
  *   "lmhead_topk", "lmhead_merge", "head_argmax", "greedy_head_final",
  *   "head_stats", "head_row_reduce", "head_decide", "head_block_logits",
  *   "head_draw", "cycle_fused", "fused_clear".
