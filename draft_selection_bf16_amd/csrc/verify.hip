@@ -429,13 +429,20 @@ VerifyPlan verify_plan(int B, int T, int64_t vocab) {
   // about 1024 work-groups (four per CU): 512 rows take 2 chunks (argmax
   // pass 29.3 against 29.9 us with 4), 256 rows 4 (17.5 against 19.6 with 8)
   int64_t want = (1024 + rows - 1) / (rows > 0 ? rows : 1);
-  int64_t max_by_size = vocab / 16384;
+  // a work-group reads 16,384 bf16 entries per pass of its loads (512
+  // threads x 4 x 16 bytes): chunks of at most that many take one round
+  const int64_t one_pass = (vocab + 16383) / 16384;
+  int64_t max_by_size = one_pass;
   // very few rows: smaller chunks (>= 4096 entries) until rows * chunks
   // reaches 256, one work-group per CU (8 rows of 151,936: 32 chunks, 48.8
   // against 51.1 us per cycle with 9; at 64 or more rows 9 chunks stay best)
   const int64_t few = rows > 0 ? 256 / rows : 1;
   if (few > max_by_size) max_by_size = few < vocab / 4096 ? few : vocab / 4096;
   int64_t s = want < max_by_size ? want : max_by_size;
+  // rows whose chunks would take two or more passes go to one-pass chunks
+  // while that stays within about six work-groups per CU (136 rows: 8 -> 10
+  // chunks, 76.5 -> 75.3 us per cycle; 72 rows: 9 -> 10, 88.1 -> 87.6 us)
+  if (s > 1 && s < one_pass && rows * one_pass <= 1536) s = one_pass;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   int64_t chunk = (vocab + s - 1) / s;
