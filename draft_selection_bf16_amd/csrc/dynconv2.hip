@@ -132,10 +132,11 @@ ConvPlan conv_plan(int B, int L, int d, int group) {
   (void)group;
   ConvPlan p;
   // 64 x 128 tiles in 3 LDS stages (72 KB); from 1,024 rows on 128 x 128
-  // tiles (96 KB), which halve the W bytes per work-group (64 requests,
-  // block 16: 926.4 against 949.1 us per cycle with 20 sites)
+  // tiles, which halve the W bytes per work-group (64 requests, block 16:
+  // 926.4 against 949.1 us per cycle with 20 sites), on the projection's
+  // eight waves in two alternating groups (874 -> 861 us against four waves)
   const int M = B * L, N = 2 * (d / 16);
-  p.tiling = M >= 1024 ? GemmTiling{128, 128, 3, 4, 1} : GemmTiling{64, 128, 3, 4, 1};
+  p.tiling = M >= 1024 ? GemmTiling{128, 128, 4, 8, 3} : GemmTiling{64, 128, 3, 4, 1};
   const int bm = p.tiling.bm;
   const int tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int nk = d / 64;
