@@ -42,6 +42,7 @@ namespace {
 
 constexpr int kNW = 4;                   // waves per work-group
 constexpr int kThreads = kNW * kWave;
+constexpr int kTopkEpt = 20;             // entries per thread of the short-chunk top-K
 constexpr int kPBM = 64, kPBN = 128, kPS = 3;   // projection tiles (64 x 128, 3 LDS stages)
 constexpr int kSpinLimit = 1 << 22;      // polls before a wait gives up
 static_assert(verifyd::kThreads == kThreads && selectd::kPathThreads == kThreads, "one work-group size");
@@ -113,9 +114,15 @@ __global__ __launch_bounds__(kThreads) void cycle_fused_kernel(FusedArgs a) {
 
   if (vid < a.base_proj) {
     // ---- top-K of one chunk of one drafter row; the row's last chunk merges
-    auto& L = *reinterpret_cast<topkd::TopkChunkLds<kNW>*>(dyn_lds);
-    topkd::topk_chunk_body<topkd::Bf16, kNW>(a.logits, a.vocab, a.tsplits, a.tchunk, a.K, a.cand_idx, a.cand_val,
-                                             a.tpart, vid, L);
+    if (a.tchunk <= (int64_t)kThreads * kTopkEpt) {   // one round of loads per chunk
+      auto& L = *reinterpret_cast<topkd::TopkSmallLds<kNW>*>(dyn_lds);
+      topkd::topk_small_body<topkd::Bf16, kNW, kTopkEpt>(a.logits, a.vocab, a.tsplits, a.tchunk, a.K, a.cand_idx,
+                                                         a.cand_val, a.tpart, vid, L);
+    } else {
+      auto& L = *reinterpret_cast<topkd::TopkChunkLds<kNW>*>(dyn_lds);
+      topkd::topk_chunk_body<topkd::Bf16, kNW>(a.logits, a.vocab, a.tsplits, a.tchunk, a.K, a.cand_idx, a.cand_val,
+                                               a.tpart, vid, L);
+    }
     if (a.tsplits == 1) {
       signal(ctr + C_MERGED * kCtrStride);
     } else {
@@ -199,6 +206,7 @@ bool g_lds_set = false;
 constexpr size_t lds_bytes() {
   size_t m = (size_t)kPS * (kPBM + kPBN) * mfma::BK * 2;
   m = sizeof(topkd::TopkChunkLds<kNW>) > m ? sizeof(topkd::TopkChunkLds<kNW>) : m;
+  m = sizeof(topkd::TopkSmallLds<kNW>) > m ? sizeof(topkd::TopkSmallLds<kNW>) : m;
   m = sizeof(selectd::PairLds<false>) > m ? sizeof(selectd::PairLds<false>) : m;
   m = sizeof(selectd::PathLds) > m ? sizeof(selectd::PathLds) : m;
   return m;
@@ -219,7 +227,7 @@ TopkPlan fused_topk_plan(int64_t rows, int64_t vocab, int k) {
     p.chunk = chunk;
     p.ws_bytes = align256((size_t)rows * (size_t)p.splits * 16 * sizeof(uint64_t));
   }
-  p.small = 0;   // the persistent launch runs the streaming chunk body
+  p.small = 0;   // (the persistent launch picks its chunk body by the chunk's length)
   return p;
 }
 
