@@ -10,11 +10,11 @@
 // bodies, the same K split and summation orders), so the results equal
 // the multi-launch cycle's bit for bit.
 //
-// Measured at batch 1 / block 8 (V = 151,936, d = 5120): 63.6-65.2 us per
-// replayed cycle against 46.0 us for the eight-kernel graph.  A dependent
+// Measured at batch 1 / block 8 (V = 151,936, d = 5120): 61.2-61.3 us per
+// replayed cycle against 41.7 us for the eight-kernel graph (63.6-65.2
+// against 46.0 us with the streaming top-K body in both).  A dependent
 // launch inside a replayed graph costs only about 1-2 us on this part, while
-// each stage body has 5-15 us of latency of its own (the top-K chunk scan
-// alone 15-22 us here with four waves per work-group, 3.5-6 us for a launch
+// each stage body has 5-15 us of latency of its own (3.5-6 us for a launch
 // whose work-groups do nothing), and every wait on another work-group (its
 // release, the counter round trip, the poll, the acquire) costs about what
 // the launch gap it replaces did.  The multi-launch graph stays the default.
