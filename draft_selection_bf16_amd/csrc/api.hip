@@ -262,16 +262,17 @@ int split_for(const GemmTiling& t, int maxs, int B, int T, int K, int d, int r) 
   if (ks > maxs) ks = maxs;
   return ks < 1 ? 1 : ks;
 }
-// 64 x 128 tiles (4 waves, up to 16 slices) below 1,024 candidate rows, and
-// wherever they need no K split while 128 x 128 tiles would (no reduce
-// pass); 128 x 128 otherwise.  Per cycle: batch 1 / block 8 47.9 -> 45.8 us,
-// batch 8 / block 8 sampled 96.5 -> 93.8, batch 32 / block 8 (3,584 rows,
-// no split instead of two slices) 94.4 -> 91.5; at batch 8 / block 16 both
-// split and the 128 x 128 tiles stay ahead (76.7 against 78.4).
+// 64 x 128 tiles (4 waves, up to 16 slices) below 1,024 candidate rows,
+// 128 x 128 from there on.  Per cycle: batch 1 / block 8 47.9 -> 45.8 us,
+// batch 8 / block 8 sampled 96.5 -> 93.8.  With both waves of a SIMD in
+// step the 64 x 128 tiles also won where they needed no K split while the
+// 128 x 128 ones did (batch 32 / block 8, 3,584 rows: 94.4 -> 91.5); on the
+// two alternating wave groups the 128 x 128 tiles with two slices win there
+// (88.3-88.4 against 89.9-90.2 us).
 bool proj_small(int B, int T, int K, int d, int r) {
-  if (B * T * K < kSmallProjRows) return true;
-  return split_for(kProjTilingSmall, kMaxProjSplitSmall, B, T, K, d, r) == 1 &&
-         split_for(kProjTiling, kMaxProjSplit, B, T, K, d, r) > 1;
+  (void)d;
+  (void)r;
+  return B * T * K < kSmallProjRows;
 }
 const GemmTiling& proj_tiling(int B, int T, int K, int d, int r) {
   return proj_small(B, T, K, d, r) ? kProjTilingSmall : kProjTiling;
