@@ -315,20 +315,21 @@ def test_pair_scores_other_ranks(r, K):
     report("pair_scores other ranks", r=r, K=K, worst_err_over_bound=round(worst, 4))
 
 
-@pytest.mark.parametrize("block", [16, 8])
-def test_pair_scores_full_size_every_request(block):
-    """32 requests, K = 16, V = 151,936, d = 5120, r = 256 through the per-cycle
-    projection (the benchmark's launch at block 16: 7,680 gathered rows on
-    128 x 128 tiles, no K split; at block 8 3,584 rows and two slices summed
-    by the reduce pass): every score of every request against the oracle.
-    Candidate ids uniform over the vocabulary, the first and last token
-    planted."""
-    w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], block=block)
+@pytest.mark.parametrize("B,block,V", [(32, 16, 151936), (32, 8, 151936), (64, 16, 262144)])
+def test_pair_scores_full_size_every_request(B, block, V):
+    """K = 16, d = 5120, r = 256 through the per-cycle projection: the
+    benchmark's launch (32 requests, block 16: 7,680 gathered rows on
+    128 x 128 tiles, no K split), block 8 (3,584 rows, two slices summed by
+    the reduce pass) and the stress shape (64 requests, V = 262,144: a
+    2.7 GB embedding table, whose byte offsets exceed 31 bits); every score
+    of every request against the oracle.  Candidate ids uniform over the
+    vocabulary, the first and last token planted."""
+    w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=block, V=V)
     print(f"[case] pair_scores full size B={w.B} T={w.T} K={w.K} V={w.V} d={w.d}", flush=True)
     E = synth.embeddings(w, device=DEV)
     wa, wb, wh = synth.selector_weights(w, device=DEV)
     h, last = synth.context_hidden(w, device=DEV), synth.last_tokens(w, device=DEV)
-    g = torch.Generator().manual_seed(79 + block)
+    g = torch.Generator().manual_seed(79 + block + B)
     cand = torch.randint(0, w.V, (w.B, w.T, w.K), generator=g, dtype=torch.int32)
     cand[0, 0, 0], cand[-1, -1, -1] = 0, w.V - 1
     U = 3 * torch.randn(w.B, w.T, w.K, generator=g)
