@@ -14,9 +14,10 @@
 // loads, several work-groups per row, per-row partials merged by a small
 // kernel) plus O(B) follow-up work:
 //   greedy : row argmax partials -> per-request prefix check;
-//   reject : row (argmax, sum of exp) partials -> per-request accept chain
-//            -> residual mass per vocabulary chunk of the one row that is
-//            resampled -> chunk search and in-chunk scan.
+//   reject : row (argmax, sum of exp) partials -> per (request, vocabulary
+//            chunk): the request's accept chain, then the residual mass of
+//            that chunk of the one row that is resampled -> chunk search and
+//            in-chunk scan.
 // Probabilities are fp32, p(v) = 2^((z_v - m) * log2(e) / tau) / s.
 #include "verify_body.h"
 
