@@ -225,6 +225,37 @@ def test_topk_short_chunks_mixed_rows(dtype, V):
     assert np.array_equal(gv, ov)
 
 
+def test_topk_random_shapes():
+    """Seeded random shapes around the plan's boundaries (one chunk per row,
+    short chunks, streamed chunks; vocabularies from 17 to ~200k, ragged and
+    unaligned; k from 1 to 16; all three dtypes; NaN densities up to a
+    half; some constant rows): every row against the oracle (NaN as -inf;
+    rows keep >= 16 numbers)."""
+    rng = np.random.default_rng(2026)
+    dts = [torch.float32, torch.bfloat16, torch.float16]
+    for case in range(24):
+        rows = int(rng.integers(1, 41))
+        V = int(rng.choice([17, 31, 64, 1000, 4096, 8191, 8192, 8193, 16384, 50021, 151936, 151939, 200003]))
+        k = int(rng.integers(1, min(16, V) + 1))
+        dt = dts[case % 3]
+        nan_frac = float(rng.choice([0.0, 0.0, 0.01, 0.5]))
+        g = torch.Generator().manual_seed(1000 + case)
+        z = 3 * torch.randn(rows, V, generator=g)
+        if rows > 2:
+            z[1] = 0.5                                   # constant row: ties everywhere
+        if nan_frac > 0 and V >= 64:
+            m = torch.rand(rows, V, generator=g) < nan_frac
+            z[m] = float("nan")
+            z[torch.isnan(z).sum(1) > V - 16] = 1.0      # keep >= 16 numbers per row
+        z = z.to(dt)
+        print(f"[case] topk random {case}: rows={rows} V={V} k={k} dt={dt} nan={nan_frac}", flush=True)
+        gi, gv = _topk_gpu(dev(z), k)
+        zo = torch.where(torch.isnan(z), torch.full_like(z, float("-inf")), z)
+        oi, ov = oracle.topk(zo, k)
+        assert np.array_equal(gi, oi), case
+        assert np.array_equal(gv, ov), case
+
+
 # ----------------------------------------------------------------- pair scores
 def _pair_gpu(cand_idx, cand_val, last, E, h, wa, wb, wh, gate=0):
     B, T, K = cand_idx.shape
