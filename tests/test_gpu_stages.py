@@ -412,6 +412,28 @@ def test_path_deterministic_modes_bit_exact(B, T, K, ties, mode):
         assert np.array_equal(g[key], o[key]), key
 
 
+def test_path_random_shapes():
+    """Seeded random lattices (batch up to 300, block positions 1 to 63,
+    1 to 16 candidates, scores on a quarter grid in half the cases so that
+    equal sums occur): both deterministic modes bit-exact against the
+    oracle."""
+    rng = np.random.default_rng(7171)
+    for case in range(16):
+        B = int(rng.integers(1, 301))
+        T = int(rng.integers(1, 64))
+        K = int(rng.integers(1, 17))
+        ties = bool(case % 2)
+        S = synth.pair_score_lattice(B, T, K, seed=9000 + case, ties=ties)
+        cand = torch.randint(0, 151936, (B, T, K), dtype=torch.int32,
+                             generator=torch.Generator().manual_seed(case))
+        for mode in (0, 1):
+            print(f"[case] path random {case}: B={B} T={T} K={K} ties={ties} mode={mode}", flush=True)
+            g = _path_gpu(S, cand, mode)
+            o = oracle.path(S.numpy(), cand.numpy(), mode)
+            for key in ("rank", "tok", "q", "score"):
+                assert np.array_equal(g[key], o[key]), (case, mode, key)
+
+
 @pytest.mark.parametrize("B,T,K,tau", [(64, 15, 16, 1.0), (8, 7, 16, 0.5), (200, 3, 4, 2.0)])
 def test_path_sampled(B, T, K, tau):
     S = synth.pair_score_lattice(B, T, K, seed=7 + T, spread=1.0)
@@ -490,6 +512,36 @@ def test_verify_greedy_exact(name, B, T, V, dtype):
     report(f"verify greedy {name}", mean_accept=float(ga.mean()))
 
 
+def test_verify_greedy_random_shapes():
+    """Seeded random shapes around the verification plan's boundaries (one
+    chunk per row; one-pass chunks of at most 16,384 entries; the smaller
+    chunks of very few rows; ragged vocabularies), all three dtypes, rows
+    rounded to integers in some cases so that the argmax ties: acceptance
+    lengths and emitted tokens bit-exact against the oracle."""
+    rng = np.random.default_rng(4242)
+    dts = [torch.bfloat16, torch.float16, torch.float32]
+    for case in range(20):
+        B = int(rng.integers(1, 49))
+        T = int(rng.integers(1, 24))
+        V = int(rng.choice([16, 100, 4096, 16383, 16384, 16385, 40000, 151936, 151939, 200003]))
+        while B > 1 and B * (T + 1) * V > 24_000_000:
+            B //= 2
+        dt = dts[case % 3]
+        g = torch.Generator().manual_seed(3000 + case)
+        Z = 3 * torch.randn(B, T + 1, V, generator=g)
+        if case % 4 == 1:
+            Z = torch.round(Z)                           # ties at the argmax
+        Z = Z.to(dt)
+        am = Z.float().argmax(-1).to(torch.int32)
+        flip = torch.rand(B, T, generator=g) < 0.2
+        path = torch.where(flip, (am[:, :T] + 1) % V, am[:, :T]).to(torch.int32).contiguous()
+        print(f"[case] verify greedy random {case}: B={B} T={T} V={V} dt={dt}", flush=True)
+        ga, go = _verify_greedy_gpu(Z, path)
+        o = oracle.verify_greedy(Z, path)
+        assert np.array_equal(ga, o["accept_len"]), case
+        assert np.array_equal(go, o["out_tok"]), case
+
+
 def test_verify_greedy_ties_take_lowest_index():
     Z = torch.zeros((2, 3, 40000), dtype=torch.bfloat16)
     Z[:, :, 777] = 5.0
@@ -548,6 +600,39 @@ def test_verify_reject_matches_oracle(B, T, V, tau, sampled):
     report("verify reject", B=B, T=T, V=V, near_tie_mismatches=near,
            mean_accept=float(np.mean(o["accept_len"])), fallbacks=o["fallbacks"])
     assert bad == 0
+
+
+def test_verify_reject_random_shapes():
+    """Seeded random shapes for rejection verification (batch, block,
+    vocabulary across the chunk and residual-chunk boundaries, temperature,
+    sampled or Viterbi drafts, all three dtypes): every request against the
+    oracle, mismatches only at counted near-ties."""
+    rng = np.random.default_rng(5151)
+    dts = [torch.bfloat16, torch.float16, torch.float32]
+    near = 0
+    for case in range(12):
+        B = int(rng.integers(1, 33))
+        T = int(rng.integers(1, 16))
+        V = int(rng.choice([64, 1000, 4096, 4097, 8193, 20000, 65536, 151936]))
+        while B > 1 and B * (T + 1) * V > 12_000_000:
+            B //= 2
+        tau = float(rng.choice([0.5, 1.0, 1.7]))
+        sampled = bool(case % 2 == 0)
+        seed = 100 + case
+        print(f"[case] verify reject random {case}: B={B} T={T} V={V} tau={tau} sampled={sampled}",
+              flush=True)
+        Z, pth, idx = _reject_case(B, T, V, tau, seed, sampled, dtype=dts[case % 3])
+        ga, go = _verify_reject_gpu(Z, torch.from_numpy(pth["tok"]), torch.from_numpy(pth["rank"]),
+                                    torch.from_numpy(idx), torch.from_numpy(pth["q"]), tau, seed)
+        o = oracle.verify_reject(Z.cpu(), pth["tok"], pth["rank"], idx, pth["q"], tau, seed)
+        for b in range(B):
+            if ga[b] == o["accept_len"][b] and np.array_equal(go[b], o["out_tok"][b]):
+                continue
+            ma = o["margin_accept"][b]
+            assert np.nanmin(ma[: o["accept_len"][b] + 1]) < NEAR_TIE or o["margin_sample"][b] < NEAR_TIE, \
+                (case, b)
+            near += 1
+    report("verify reject random", near_tie_mismatches=near)
 
 
 def test_verify_reject_sub_ranges_draw_the_batch_counters():
@@ -629,6 +714,39 @@ def test_dynconv2_matches_oracle(B, L, d, base, prev):
     bf16_ulp_close(y16, yo, bound)
     report("dynconv2", B=B, L=L, d=d, worst_err_over_1e3_terms=round(worst, 4),
            worst_err_over_sum_bound=round(worst_b, 4), bf16_steps=round(ulp, 3))
+
+
+def test_dynconv2_random_shapes():
+    """Seeded random shapes for the conv: batch and block lengths whose
+    B L rows cross the GEMM's tile-height switch at 1,024 rows and its K
+    split sizes; hidden sizes of any multiple of 64 up to 16,384; base and
+    previous token present or not; fp32 and bf16 outputs against the oracle
+    under the same rules as above."""
+    rng = np.random.default_rng(6161)
+    for case in range(12):
+        d = 64 * int(rng.integers(1, 1 + (4, 16, 64, 256)[case % 4]))
+        B = int(rng.integers(1, 81))
+        L = int(rng.integers(1, 21))
+        if case % 3 == 2:                                # 1,024 rows or more
+            B, L, d = int(rng.integers(64, 81)), 16, 64 * int(rng.integers(1, 33))
+        while B > 1 and B * L * d * d > 8_000_000_000:  # keeps the fp64 oracle at seconds
+            B //= 2
+        base, prev = bool(rng.integers(2)), bool(rng.integers(2))
+        print(f"[case] dynconv2 random {case}: B={B} L={L} d={d} base={base} prev={prev}", flush=True)
+        w = synth.scaled(synth.WORKLOADS["b32_blk16_v151936_conv"], B=B, block=L, d=d, conv_base=base,
+                         seed=70 + case)
+        x, xp, wt, bs = synth.conv_site(w, case)
+        if not prev:
+            xp = None
+        yo = oracle.dynconv2(x, xp, wt, bs)
+        scale = conv_term_scale(x, xp, wt, bs)
+        bound = conv_error_bound(x, xp, wt, bs)
+        y32 = _conv_gpu(x, xp, wt, bs, torch.float32).cpu().numpy()
+        conv_rel_close(y32, yo, scale)
+        conv_close(y32, yo, bound)
+        y16 = _conv_gpu(x, xp, wt, bs, torch.bfloat16)
+        conv_rel_close_bf16(y16, yo, scale)
+        bf16_ulp_close(y16, yo, bound)
 
 
 def test_dynconv2_identity_and_shift_exact():
