@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void cycle_fused_kernel(FusedArgs a) {
     // ---- one projection tile (one K slice); candidate rows wait for the merges
     const int bid = vid - a.base_proj;
     if (proj_tile(bid, a.nproj, a.P.ksplit) >= a.free_tiles) wait_for(ctr + C_MERGED * kCtrStride, a.rows, err);
-    gemm::run_tile<kPBM, kPBN, kPS, kNW, 1>(a.P, bid, a.nproj);
+    gemm::run_tile<kPBM, kPBN, kPS, kNW, 1, false>(a.P, bid, a.nproj);   // read in this launch: cached stores
     signal(ctr + C_PROJ * kCtrStride);
   } else if (vid < a.base_pair) {
     // ---- slices summed into slice 0, one float4 per thread

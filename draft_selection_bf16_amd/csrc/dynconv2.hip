@@ -15,7 +15,9 @@
 //  2. a streaming epilogue, one work-group per (b, t) row: sums the slice
 //     partials of its 2G taps in a fixed order into LDS and combines them
 //     with x_t and x_{t-1} (16-byte loads, issued together with the partial
-//     loads) into y (bf16 round-to-nearest-even, or fp32).
+//     loads) into y (bf16 round-to-nearest-even, or fp32), written with
+//     streaming stores (y is read by a later launch; measured: the batch-32
+//     / block-16 step 0.4865 -> 0.4752 ms with these alone).
 #include "df2_device.h"
 #include "df2_internal.h"
 
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
 #pragma unroll
       for (int h = 0; h < 4; ++h)
         o[h] = (uint32_t)f32_to_bf16_rne(out[2 * h]) | ((uint32_t)f32_to_bf16_rne(out[2 * h + 1]) << 16);
-      *(u32x4*)((uint16_t*)y + (int64_t)row * d + ch0) = o;
+      __builtin_nontemporal_store(o, (u32x4*)((uint16_t*)y + (int64_t)row * d + ch0));
     } else {
       float* yo = (float*)y + (int64_t)row * d + ch0;
-      *(f32x4*)yo = f32x4{out[0], out[1], out[2], out[3]};
-      *(f32x4*)(yo + 4) = f32x4{out[4], out[5], out[6], out[7]};
+      __builtin_nontemporal_store(f32x4{out[0], out[1], out[2], out[3]}, (f32x4*)yo);
+      __builtin_nontemporal_store(f32x4{out[4], out[5], out[6], out[7]}, (f32x4*)(yo + 4));
     }
   }
 }

@@ -1,5 +1,6 @@
 // gemm.hip -- launcher of the bf16 MFMA GEMM (the tile itself is in
-// gemm_tile.h): one work-group per tile and K slice.
+// gemm_tile.h): one work-group per tile and K slice; the output tiles leave
+// with streaming stores (read by the next launch, not by this one).
 #include "gemm_tile.h"
 
 namespace df2 {
@@ -8,7 +9,7 @@ namespace {
 
 template <int BM, int BN, int S, int NW, int ISSUE>
 __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(Problem Pb) {
-  run_tile<BM, BN, S, NW, ISSUE>(Pb, blockIdx.x, gridDim.x);
+  run_tile<BM, BN, S, NW, ISSUE, true>(Pb, blockIdx.x, gridDim.x);
 }
 
 // One dense problem, its fields passed as separate arguments: an aggregate
@@ -27,7 +28,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_dense_kernel(const uint16_t* x, 
   D.ksplit = ksplit;
   D.ldx = ldx;
   D.ldo = ldo;
-  run_tile_dense<BM, BN, S, NW, ISSUE>(D, blockIdx.x);
+  run_tile_dense<BM, BN, S, NW, ISSUE, true>(D, blockIdx.x);
 }
 
 }  // namespace
