@@ -17,7 +17,11 @@
 //     with x_t and x_{t-1} (16-byte loads, issued together with the partial
 //     loads) into y (bf16 round-to-nearest-even, or fp32), written with
 //     streaming stores (y is read by a later launch; measured: the batch-32
-//     / block-16 step 0.4865 -> 0.4752 ms with these alone).
+//     / block-16 step 0.4865 -> 0.4752 ms with these alone).  Its loads are
+//     streaming loads too: cached ones fill the caches with lines that are
+//     read at most twice (x_t, as the next row's x_{t-1}, is still found),
+//     and the reads of the stages after the conv slow down (step 0.4565 ->
+//     0.4464 ms; the projection 60.1 -> 57.3 us).
 #include "df2_device.h"
 #include "df2_internal.h"
 
@@ -60,8 +64,8 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
   for (int i = 0; i < kChunks; ++i) {
     const int c8 = tid + kThreads * i;
     const int cc = c8 < nch ? c8 : nch - 1;   // clamped: loaded, not used
-    vx[i] = *(const u32x4*)(xt + cc * 8);
-    vp[i] = xp ? *(const u32x4*)(xp + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+    vx[i] = __builtin_nontemporal_load((const u32x4*)(xt + cc * 8));
+    vp[i] = xp ? __builtin_nontemporal_load((const u32x4*)(xp + cc * 8)) : u32x4{0u, 0u, 0u, 0u};
   }
   for (int n4 = tid; n4 < NT / 4; n4 += kThreads) {
     const float* p = part + (int64_t)row * NT + n4 * 4;
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
       f32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        v[u] = *(const f32x4*)(p + (int64_t)(s0 + u < ksplit ? s0 + u : 0) * kstride);
+        v[u] = __builtin_nontemporal_load((const f32x4*)(p + (int64_t)(s0 + u < ksplit ? s0 + u : 0) * kstride));
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (s0 + u < ksplit) acc += v[u];
@@ -91,8 +95,8 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
         ap = vp[q];
       }
     if (i >= kChunks) {
-      ax = *(const u32x4*)(xt + c8 * 8);
-      ap = xp ? *(const u32x4*)(xp + c8 * 8) : u32x4{0u, 0u, 0u, 0u};
+      ax = __builtin_nontemporal_load((const u32x4*)(xt + c8 * 8));
+      ap = xp ? __builtin_nontemporal_load((const u32x4*)(xp + c8 * 8)) : u32x4{0u, 0u, 0u, 0u};
     }
     const int ch0 = c8 * 8, g = ch0 / 16;
     const float c0 = sc[g], c1 = sc[G + g];

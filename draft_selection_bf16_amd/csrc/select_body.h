@@ -131,14 +131,15 @@ __device__ __forceinline__ void pair_epilogue_body(const float* __restrict__ ab,
       if (okc) gb[u] = vb;
     }
   } else {
+    // the projection's results, each read once: streaming loads
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       if (gi[u] < npred) {
         const float* src = t == 0 ? a_last + (int64_t)b * r
                                   : ab + ((int64_t)(bt - 1) * K + gi[u]) * (2 * r);
-        ga[u] = *(const f32x4*)(src + 4 * gq[u]);
+        ga[u] = __builtin_nontemporal_load((const f32x4*)(src + 4 * gq[u]));
       }
-      if (gi[u] < K) gb[u] = *(const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]);
+      if (gi[u] < K) gb[u] = __builtin_nontemporal_load((const f32x4*)(ab + ((int64_t)bt * K + gi[u]) * (2 * r) + r + 4 * gq[u]));
     }
   }
   if (TAB) {
