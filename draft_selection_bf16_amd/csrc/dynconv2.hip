@@ -137,12 +137,15 @@ __global__ __launch_bounds__(kThreads) void conv_epilogue_kernel(
 ConvPlan conv_plan(int B, int L, int d, int group) {
   (void)group;
   ConvPlan p;
-  // 64 x 128 tiles in 3 LDS stages (72 KB); from 1,024 rows on 128 x 128
+  // 64 x 128 tiles in 4 LDS stages (96 KB) on eight waves in two
+  // alternating groups (batch 32 / block 16 step 0.4455-0.4470 -> 0.4419-
+  // 0.4422 ms against four waves over 3 stages; 3, 5 or 6 stages with the
+  // eight waves 0.4606, 0.4498, 0.4555); from 1,024 rows on 128 x 128
   // tiles, which halve the W bytes per work-group (64 requests, block 16:
-  // 926.4 against 949.1 us per cycle with 20 sites), on the projection's
-  // eight waves in two alternating groups (874 -> 861 us against four waves)
+  // 926.4 against 949.1 us per cycle with 20 sites), on the same loop
+  // (874 -> 861 us against four waves)
   const int M = B * L, N = 2 * (d / 16);
-  p.tiling = M >= 1024 ? GemmTiling{128, 128, 4, 8, 3} : GemmTiling{64, 128, 3, 4, 1};
+  p.tiling = M >= 1024 ? GemmTiling{128, 128, 4, 8, 3} : GemmTiling{64, 128, 4, 8, 3};
   const int bm = p.tiling.bm;
   const int tiles = ((M + bm - 1) / bm) * ((N + 127) / 128);
   const int nk = d / 64;

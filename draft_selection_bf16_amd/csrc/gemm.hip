@@ -112,7 +112,8 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
     if (e != hipSuccess) return e;                                                                     \
     return launch(gemm_dma_kernel<BMV, BNV, SV, NWV, IV>, grid, dim3(NWV * 64), kLds, stream, ps, P);  \
   }
-  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // the conv's taps, H, projection at small batches
+  DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // H, projection at small batches
+  DF2_GEMM_LAUNCH(64, 128, 4, 8, 3)    // the conv's taps below 1,024 rows
   DF2_GEMM_LAUNCH(128, 128, 4, 8, 3)   // projection, per-token tables, the conv's taps from 1,024 rows
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
