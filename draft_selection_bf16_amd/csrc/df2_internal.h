@@ -127,6 +127,7 @@ struct VerifyPlan {
   int64_t chunk;     // elements per split
   int rchunks;       // chunks of the residual scan per request
   int64_t rchunk;    // elements per residual chunk
+  int fused;         // rejection: residual draw in one work-group per request over the chunks above
   size_t off_part;   // partial results [rows, splits] (8 bytes each)
   size_t off_dec;    // per-request decision record
   size_t off_rsum;   // residual chunk sums [B, rchunks]
