@@ -126,6 +126,10 @@ __global__ __launch_bounds__(kThreads) void head_decide_kernel(
       k = r.key;
       s = r.s;
     }
+    // one Philox block per position: the acceptance uniform (word 1) and
+    // the draw's uniform should the chain stop there (word 2)
+    const u64x4 ph = philox4x64_10(seed, 0, (uint64_t)(lane <= T ? lane : 0), (uint64_t)(b0 + b), 0, 0);
+    const float u2l = uniform_of_word(ph.w[2]);
     bool reject = false;
     int32_t x = -1;
     if (lane < T) {
@@ -134,19 +138,19 @@ __global__ __launch_bounds__(kThreads) void head_decide_kernel(
       const float qx = (rk >= 0 && rk < K) ? q[((int64_t)b * T + lane) * K + rk] : 0.f;
       float px = 0.f;
       if (x >= 0 && x < vocab && k) px = exp2f((zx[row0 + lane] - key_value(k)) * c) / s;
-      const float u1 = cycle_uniform(seed, b0 + b, lane, 1);
-      reject = !(qx <= 0.f || u1 < px / qx);
+      reject = !(qx <= 0.f || uniform_of_word(ph.w[1]) < px / qx);
     }
     const uint64_t rm = ballot(reject);
     const int n = rm ? __ffsll((unsigned long long)rm) - 1 : T;
     const uint64_t kn = shfl_u64(k, n);
     const float sn = __shfl(s, n), mn = key_value(kn);
+    const float u2n = __shfl(u2l, n);
     if (lane == 0) {
       s_n = n;
       s_m = mn;
       s_s = sn;
       s_arg = kn ? (int)key_index(kn) : 0;
-      s_u2 = cycle_uniform(seed, b0 + b, n, 2);
+      s_u2 = u2n;
       accept_len[b] = n;
     }
     if (lane <= T && lane != n) out_tok[row0 + lane] = lane < n ? x : -1;

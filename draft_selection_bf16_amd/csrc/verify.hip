@@ -147,6 +147,11 @@ __device__ __forceinline__ DecRec decide_request(const void* __restrict__ z, int
 #pragma unroll 8
     for (int i = 0; i < splits; ++i) combine_part(k, s, p[i].key, p[i].s, c);
   }
+  // one Philox block per position: its acceptance uniform (word 1) and the
+  // draw's uniform should the chain stop there (word 2; the chain then
+  // picks lane n's), both off the critical path
+  const u64x4 ph = philox4x64_10(seed, 0, (uint64_t)(lane <= T ? lane : 0), (uint64_t)(b0 + b), 0, 0);
+  const float u1l = uniform_of_word(ph.w[1]), u2l = uniform_of_word(ph.w[2]);
   bool reject = false;
   if (lane < T) {
     const float qx = (rk >= 0 && rk < K) ? q[((int64_t)b * T + lane) * K + rk] : 0.f;
@@ -156,8 +161,7 @@ __device__ __forceinline__ DecRec decide_request(const void* __restrict__ z, int
       float zx = Elt<DT>::one(rowp, x);
       px = exp2f((zx - key_value(k)) * c) / s;
     }
-    const float u1 = cycle_uniform(seed, b0 + b, lane, 1);
-    const bool accept = qx <= 0.f || u1 < px / qx;
+    const bool accept = qx <= 0.f || u1l < px / qx;
     reject = !accept;
   }
   uint64_t rm = ballot(reject);
@@ -170,7 +174,7 @@ __device__ __forceinline__ DecRec decide_request(const void* __restrict__ z, int
   d.argmax = knn ? (int)key_index(knn) : 0;
   d.m = key_value(knn);
   d.s = sn;
-  d.u2 = cycle_uniform(seed, b0 + b, n, 2);
+  d.u2 = __shfl(u2l, n);
   d.pad = 0.f;
   if (write) {
     if (lane == 0) {
