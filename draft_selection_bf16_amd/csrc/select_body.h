@@ -399,6 +399,9 @@ __device__ __forceinline__ void path_body(const float* __restrict__ scores, cons
     __syncthreads();
   } else {
     const uint64_t seed = (mode == 2) ? seed_dev[0] : 0ull;
+    // SAMPLE: position t's uniform depends on (seed, request, t) alone, so
+    // lane t draws it before the walk (T <= 63) and each step reads it
+    const float ul = (mode == 2 && lane < T) ? cycle_uniform(seed, b0 + b, lane, 0) : 0.f;
     int prev = 0;
     for (int t = 0; t < T; ++t) {
       float v = (lane < K) ? S[((int64_t)t * K + prev) * K + lane] : -INFINITY;
@@ -425,7 +428,7 @@ __device__ __forceinline__ void path_body(const float* __restrict__ scores, cons
         float p = e / z;
         // inclusive prefix sum in rank order
         float c = row16_prefix(p);
-        float u = cycle_uniform(seed, b0 + b, t, 0);
+        const float u = __shfl(ul, t);
         uint64_t over = ballot(lane < K && c > u);
         if (over) {
           pick = __ffsll((unsigned long long)over) - 1;
