@@ -619,6 +619,9 @@ def main():
                    "conv_sites": w.conv_sites, "path": w.path_mode, "verify": w.verify,
                    "step": "20 x dynconv2 + topk + pair_scores + path + verify, one HIP graph"},
         "tokens_scored_per_s": round(w.B * w.T * w.K / (ms / 1e3), 1),
+        # scored (predecessor, candidate) pairs: K at the first position (from
+        # the last verified token), K x K at each later one
+        "pair_scores_per_s": round(w.B * (w.K + (w.T - 1) * w.K * w.K) / (ms / 1e3), 1),
         "value_without_conv": round(w.B / (ms_nc / 1e3), 1),
         "hbm_frac": hbm_frac(w, True, ms * 1e3),
         "hbm_frac_without_conv": hbm_frac(w, False, ms_nc * 1e3),
