@@ -95,6 +95,7 @@ struct Filter {
   u32x4* q;
   uint32_t* qi;
   float* share;   // read and written with relaxed work-group atomics
+  uint32_t* prime; // the work-group's lane maxima of the first batch
   int cnt;     // keys in buf
   int qn;      // groups in q
   float thr;   // entries with value < thr cannot be in the result
@@ -241,6 +242,8 @@ __device__ __forceinline__ bool bf16_may_pass(const u32x4& v, int thr16) {
   return m >= thr16;
 }
 
+// Filter the entries [lo, hi) of a row into the waves' key buffers.  Every
+// wave of the work-group calls it (it holds one work-group barrier).
 template <typename E, int NW>
 __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t lo, int64_t hi,
                                            int wave) {
@@ -325,16 +328,21 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
   u32x4 va[kUnroll], vb[kUnroll];
   bool oka[kUnroll], okb[kUnroll];
   int g0 = wave * kWave;
+  uint32_t lmax = 0u;
   if (g0 < ng) {
     load(g0, va, oka);
     // prime the threshold from the batch just issued (kUnroll groups per
-    // lane): the 16th largest of the 64 lanes' maxima, which 16 distinct
-    // entries reach (NaN never qualifies); the scan sees these entries again
-    // below.  With kUnroll x VN = 32 bf16 entries per lane this sits near
-    // the 99th percentile of a row's values, against the 97th for the 16th
+    // lane): each lane's maximum; below, the 16th largest of the work-
+    // group's lane maxima, which 16 distinct entries reach (NaN never
+    // qualifies); the scan sees these entries again below.  With kUnroll x
+    // VN = 32 bf16 entries per lane, one wave's 16th largest of 64 sits near
+    // the 99th percentile of a row's values (against the 97th for the 16th
     // best of one group per lane: at 480 rows of 151,936 a wave then queued
-    // 138 groups and flushed 1.14 times in its scan (6,500 cycles a flush).
-    uint32_t lmax = 0u;
+    // 138 groups and flushed 1.14 times in its scan, 6,500 cycles a flush;
+    // with it 80 groups and 0.99 flushes), the work-group's 16th largest of
+    // 512 near the 99.9th: top-k 31.9 -> 31.55 us at 480 rows, batch 8 /
+    // block 16 72.4 -> 71.1 us and batch 32 / block 8 85.4 -> 84.2 us per
+    // cycle (the stress cycle 812.5 -> 814.8).
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
@@ -343,8 +351,14 @@ __device__ __forceinline__ void scan_range(Filter& F, const void* rowp, int64_t 
         const uint32_t o = oka[u] && f == f ? ord_of(f) : 0u;
         lmax = o > lmax ? o : lmax;
       }
-    const uint32_t lm1[1] = {lmax};
-    const uint32_t t = value_cut16<VB, 1>(lm1);
+  }
+  F.prime[wave * kWave + lane] = lmax;
+  __syncthreads();
+  {
+    uint32_t lm[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) lm[w] = F.prime[w * kWave + lane];
+    const uint32_t t = value_cut16<VB, NW>(lm);
     if (t != 0u) {
       F.thr = fmaxf(F.thr, value_of_ord(t));
       if (lane == 0) publish(F, wave);
@@ -437,6 +451,7 @@ struct TopkChunkLds {
   uint32_t sqidx[NW][kQueue];
   __attribute__((aligned(16))) uint64_t smerge[NW * 16];
   float sthr[NW];
+  uint32_t sprime[NW * kWave];
   __attribute__((aligned(16))) uint64_t ssurv[NW * kWave + 16];
   int srank[NW * kWave];
   int snsurv;
@@ -469,7 +484,7 @@ __device__ __forceinline__ void topk_chunk_body(const void* __restrict__ logits,
 
   if (lane == 0) sthr[wave] = -INFINITY;
   __syncthreads();
-  Filter F{sbuf[wave], squeue[wave], sqidx[wave], sthr, 0, 0, -INFINITY};
+  Filter F{sbuf[wave], squeue[wave], sqidx[wave], sthr, L.sprime, 0, 0, -INFINITY};
   scan_range<E, NW>(F, rowp, lo, hi, wave);
   // Keep up to 64 keys per wave (no final cut), then filter every wave's
   // keys by two lower bounds on the chunk's 16th best key: the largest
