@@ -274,12 +274,24 @@ bool proj_small(int B, int T, int K, int d, int r) {
   (void)r;
   return B * T * K < kSmallProjRows;
 }
+// 256 x 128 tiles (three LDS stages, same loop) where the 128 x 128 ones
+// need more than one round of work-groups: a quarter fewer operand bytes
+// per work-group and one round.  64 requests, block 16 (484 tiles of 128 x
+// 128 against 244): 822 -> 803 us per stress cycle; where they would need a
+// K split instead (batch 32 / block 16: 124 tiles, two slices and a 12.5 us
+// slice sum) they lost, 0.442 -> 0.450 ms.
+constexpr GemmTiling kProjTilingBig{256, 128, 3, 8, 3};
+int proj_tiles(const GemmTiling& t, int B, int T, int K, int r) {
+  auto tl = [&](int m, int n) { return ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn); };
+  return tl(B * T * K, r) + tl(B * (T - 1) * K, r) + tl(B, r) + tl(B * T, r);
+}
 const GemmTiling& proj_tiling(int B, int T, int K, int d, int r) {
-  return proj_small(B, T, K, d, r) ? kProjTilingSmall : kProjTiling;
+  if (proj_small(B, T, K, d, r)) return kProjTilingSmall;
+  return proj_tiles(kProjTiling, B, T, K, r) > 256 ? kProjTilingBig : kProjTiling;
 }
 int proj_split(int B, int T, int K, int d, int r) {
-  return proj_small(B, T, K, d, r) ? split_for(kProjTilingSmall, kMaxProjSplitSmall, B, T, K, d, r)
-                                   : split_for(kProjTiling, kMaxProjSplit, B, T, K, d, r);
+  const GemmTiling& t = proj_tiling(B, T, K, d, r);
+  return split_for(t, &t == &kProjTilingSmall ? kMaxProjSplitSmall : kMaxProjSplit, B, T, K, d, r);
 }
 struct PairWs {
   int split;

@@ -93,7 +93,7 @@ struct GemmTiling {
 };
 // out = gate(X W^T) for up to 4 segments in one launch; K = d (multiple of 64).
 // Each segment needs n0 % bn == 0 or n0 >= N, and x_rows * ldx * 2 < 2^32.
-// (bm, bn, stages, waves, issue) in {(64,128,3,4,1), (64,128,4,8,3), (128,128,4,8,3)};
+// (bm, bn, stages, waves, issue) in {(64,128,3,4,1), (64,128,4,8,3), (128,128,4,8,3), (256,128,3,8,3)};
 // K % 64 == 0 and
 // 1 <= ksplit <= K / 64 (slices of K / 64 / ksplit K-tiles, rounded).
 hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const GemmTiling& t,

@@ -115,6 +115,7 @@ hipError_t launch_gemm(const GemmSeg* segs, int nseg, int K, int ksplit, const G
   DF2_GEMM_LAUNCH(64, 128, 3, 4, 1)    // H, projection at small batches
   DF2_GEMM_LAUNCH(64, 128, 4, 8, 3)    // the conv's taps below 1,024 rows
   DF2_GEMM_LAUNCH(128, 128, 4, 8, 3)   // projection, per-token tables, the conv's taps from 1,024 rows
+  DF2_GEMM_LAUNCH(256, 128, 3, 8, 3)   // projection with more than one round of 128 x 128 tiles
 #undef DF2_GEMM_LAUNCH
   return hipErrorInvalidValue;
 }
