@@ -279,7 +279,8 @@ bool proj_small(int B, int T, int K, int d, int r) {
 // per work-group and one round.  64 requests, block 16 (484 tiles of 128 x
 // 128 against 244): 822 -> 803 us per stress cycle; where they would need a
 // K split instead (batch 32 / block 16: 124 tiles, two slices and a 12.5 us
-// slice sum) they lost, 0.442 -> 0.450 ms.
+// slice sum) they lost, 0.442 -> 0.450 ms.  The per-token table build
+// (4,748 tiles of 128 x 128 at V = 151,936) takes them too: 1.05 -> 0.877 ms.
 constexpr GemmTiling kProjTilingBig{256, 128, 3, 8, 3};
 int proj_tiles(const GemmTiling& t, int B, int T, int K, int r) {
   auto tl = [&](int m, int n) { return ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn); };
@@ -574,7 +575,7 @@ int dflash2_selector_tables(const void* emb, int emb_dt, int64_t vocab, int d, c
     s[1].out = tab + r;
     nseg = 2;
   }
-  return hip_status(launch_gemm(s, nseg, d, 1, kProjTiling, "table_gemm", stream), "dflash2_selector_tables");
+  return hip_status(launch_gemm(s, nseg, d, 1, kProjTilingBig, "table_gemm", stream), "dflash2_selector_tables");
 }
 
 namespace {
