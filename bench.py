@@ -38,7 +38,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 STRESS = "b64_blk16_v262144_stress"
 KERNEL_TAGS = ["conv_gemm", "conv_epilogue", "topk_chunk", "topk_merge", "project_gemm", "h_gemm",
                "proj_reduce", "pair_epilogue", "path", "argmax_part", "greedy_final",
-               "sumexp_part", "residual_chunk", "residual_find"]
+               "sumexp_part", "residual_fused", "residual_chunk", "residual_find"]
 EVICT_BYTES = 1 << 30          # written between cold replays: 4x the 256 MB Infinity Cache
 
 

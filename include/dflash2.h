@@ -408,11 +408,11 @@ int dflash2_philox4x64(const uint64_t* seed_dev, const int32_t* b, const int32_t
 /* ------------------------------------------------------------------------
  * Kernel timing hook (host).  Arms this thread so that every later launch of
  * the kernel with tag `kernel` records a start and a stop HIP event in its
- * own dispatch (hipExtLaunchKernel: the kernel's execution interval, without
- * stream-side overhead), for at most max_launches launches.  Tags:
+ * own dispatch (hipExtLaunchKernel: the interval of the kernel's dispatch,
+ * without stream-side overhead), for at most max_launches launches.  Tags:
  *   "topk_chunk", "topk_merge", "project_gemm", "proj_reduce", "h_gemm",
  *   "table_gemm", "pair_epilogue", "path", "argmax_part", "greedy_final",
- *   "sumexp_part", "residual_chunk", "residual_find", "conv_gemm",
+ *   "sumexp_part", "residual_fused", "residual_chunk", "residual_find", "conv_gemm",
  *   "conv_epilogue", "philox",
  *   "lmhead_topk", "lmhead_merge", "head_argmax", "greedy_head_final",
  *   "head_stats", "head_row_reduce", "head_decide", "head_block_logits",
