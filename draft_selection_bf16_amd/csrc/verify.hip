@@ -693,8 +693,11 @@ VerifyPlan verify_plan(int B, int T, int64_t vocab) {
   // about 1024 work-groups (four per CU): 512 rows take 2 chunks (argmax
   // pass 29.3 against 29.9 us with 4), 256 rows 4 (17.5 against 19.6 with 8)
   int64_t want = (1024 + rows - 1) / (rows > 0 ? rows : 1);
-  // a work-group reads 16,384 bf16 entries per pass of its loads (512
-  // threads x 4 x 16 bytes): chunks of at most that many take one round
+  // a work-group reads 8,192 bf16 entries per pass of its loads (256
+  // threads x 4 x 16 bytes); chunks of at most 16,384 entries take two.
+  // (Capping them at one pass instead: batch 1 / block 16 48.5 -> 47.7 us
+  // per cycle, batch 8 / block 8 sampled 74.8 -> 77.0 with 1,216
+  // work-groups instead of 640.)
   const int64_t one_pass = (vocab + 16383) / 16384;
   int64_t max_by_size = one_pass;
   // very few rows: smaller chunks (>= 4096 entries) until rows * chunks
@@ -703,7 +706,7 @@ VerifyPlan verify_plan(int B, int T, int64_t vocab) {
   const int64_t few = rows > 0 ? 256 / rows : 1;
   if (few > max_by_size) max_by_size = few < vocab / 4096 ? few : vocab / 4096;
   int64_t s = want < max_by_size ? want : max_by_size;
-  // rows whose chunks would take two or more passes go to one-pass chunks
+  // rows whose chunks would take three or more passes go to two-pass chunks
   // while that stays within about six work-groups per CU (136 rows: 8 -> 10
   // chunks, 76.5 -> 75.3 us per cycle; 72 rows: 9 -> 10, 88.1 -> 87.6 us)
   if (s > 1 && s < one_pass && rows * one_pass <= 1536) s = one_pass;
