@@ -694,11 +694,9 @@ VerifyPlan verify_plan(int B, int T, int64_t vocab) {
   // pass 29.3 against 29.9 us with 4), 256 rows 4 (17.5 against 19.6 with 8)
   int64_t want = (1024 + rows - 1) / (rows > 0 ? rows : 1);
   // a work-group reads 8,192 bf16 entries per pass of its loads (256
-  // threads x 4 x 16 bytes); chunks of at most 16,384 entries take two.
-  // (Capping them at one pass instead: batch 1 / block 16 48.5 -> 47.7 us
-  // per cycle, batch 8 / block 8 sampled 74.8 -> 77.0 with 1,216
-  // work-groups instead of 640.)
+  // threads x 4 x 16 bytes); chunks of at most 16,384 entries take two
   const int64_t one_pass = (vocab + 16383) / 16384;
+  const int64_t single = (vocab + 8191) / 8192;
   int64_t max_by_size = one_pass;
   // very few rows: smaller chunks (>= 4096 entries) until rows * chunks
   // reaches 256, one work-group per CU (8 rows of 151,936: 32 chunks, 48.8
@@ -710,6 +708,11 @@ VerifyPlan verify_plan(int B, int T, int64_t vocab) {
   // while that stays within about six work-groups per CU (136 rows: 8 -> 10
   // chunks, 76.5 -> 75.3 us per cycle; 72 rows: 9 -> 10, 88.1 -> 87.6 us)
   if (s > 1 && s < one_pass && rows * one_pass <= 1536) s = one_pass;
+  // and into one-pass chunks while that stays within two work-groups per CU
+  // (batch 1 / block 16, 16 rows: 16 -> 19 chunks, 48.5 -> 47.7 us per
+  // cycle; for every row count up to 6 per CU, batch 8 / block 8 sampled
+  // took 74.8 -> 77.0 us with 1,216 work-groups instead of 640)
+  if (s < single && rows * single <= 512) s = single;
   if (s < 1) s = 1;
   if (s > 64) s = 64;
   int64_t chunk = (vocab + s - 1) / s;
