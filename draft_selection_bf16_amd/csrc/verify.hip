@@ -562,9 +562,6 @@ __global__ __launch_bounds__(kFuseThreads) void residual_fused_kernel(
       R.cq[lanes_below(im)] = qc;
     }
     if (lane == 0) {
-      R.m = d.m;
-      R.s = d.s;
-      R.c = c;
       R.ncand = __popcll(im);
       s_chunk = ch;
       s_target = target - before;
