@@ -582,12 +582,13 @@ def _reject_case(B, T, V, tau, seed, sampled=True, dtype=torch.bfloat16):
 @pytest.mark.parametrize("B,T,V,tau,sampled", [(8, 7, 151936, 1.0, True), (16, 15, 20000, 0.7, True),
                                                (16, 15, 20000, 1.0, False), (4, 3, 1000, 1.5, True),
                                                (1, 7, 151936, 1.0, True), (2, 63, 3001, 1.0, True),
-                                               (3, 5, 20011, 0.8, True), (32, 15, 151936, 1.0, True)])
+                                               (3, 5, 20011, 0.8, True), (8, 7, 163840, 1.0, True),
+                                               (32, 15, 151936, 1.0, True)])
 def test_verify_reject_matches_oracle(B, T, V, tau, sampled):
     """Residual draws in one work-group per request (streaming chunks of at
     most 16,384 entries: every case but the last, which takes the two-pass
-    search), 63 drafted positions, an odd vocabulary (rows not 16-byte
-    aligned)."""
+    search; V = 163,840 at 8 requests gives chunks of exactly 16,384), 63
+    drafted positions, an odd vocabulary (rows not 16-byte aligned)."""
     seed = 2
     Z, pth, idx = _reject_case(B, T, V, tau, seed, sampled)
     ga, go = _verify_reject_gpu(Z, torch.from_numpy(pth["tok"]), torch.from_numpy(pth["rank"]),
