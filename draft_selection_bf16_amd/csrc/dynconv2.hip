@@ -28,12 +28,19 @@
 namespace df2 {
 namespace {
 
-constexpr int kThreads = 256;
+// Epilogue work-groups of 640 threads, one 16-byte chunk of x_t and of
+// x_{t-1} each in flight (the whole row at d = 5120; a larger d loads its
+// further chunks in the output loop).  Batch 32 / block 16 step (ms) and the
+// stress cycle (us): 256 threads with three chunks each 0.4418 / 801; 320
+// threads 0.4306 / 790; 512 0.4331 / 802; 640 with three chunk slots
+// 0.4383 / 826 (their registers cost residency at 1,024 rows); 640 with one
+// 0.4215 / 784.6.
+constexpr int kThreads = 640;
 constexpr int kMaxTaps = 2048;   // 2G <= 2048  <=>  d <= 16384
 constexpr int kMaxSplit = 16;    // K slices of the tap GEMM
 constexpr int kCUs = 256;        // MI355X
 
-constexpr int kChunks = 3;       // 16-byte x chunks per thread kept in flight (d <= 6144)
+constexpr int kChunks = 1;       // 16-byte x chunks per thread requested before the first wait
 
 // One work-group per (b, t) row.  Everything the row needs is requested
 // before the first wait: the thread's x_t / x_{t-1} chunks, and, for
