@@ -57,17 +57,13 @@ __global__ __launch_bounds__(kThreads) void topk_small_kernel(
   topk_small_body<E, kWaves, kSmallEpt>(logits, vocab, splits, chunk, k, out_idx, out_val, part, blockIdx.x, L);
 }
 
-// one row per wave
-__global__ __launch_bounds__(kThreads) void topk_merge_kernel(const uint64_t* __restrict__ part,
-                                                              int64_t rows, int splits, int k,
-                                                              int32_t* __restrict__ out_idx,
-                                                              float* __restrict__ out_val) {
-  __shared__ uint64_t sel[kWaves][16];
-  __shared__ __attribute__((aligned(16))) uint64_t ssv[kWaves][kWave];
-  const int wave = threadIdx.x / kWave;
-  const int64_t row = (int64_t)blockIdx.x * kWaves + wave;
-  if (row >= rows) return;   // the same in the whole wave; no work-group barrier below
-  topk_merge_row(part, row, splits, k, out_idx, out_val, sel[wave], ssv[wave]);
+// one row per work-group of one wave (grid = rows)
+__global__ __launch_bounds__(kWave) void topk_merge_kernel(const uint64_t* __restrict__ part, int splits, int k,
+                                                           int32_t* __restrict__ out_idx,
+                                                           float* __restrict__ out_val) {
+  __shared__ uint64_t sel[16];
+  __shared__ __attribute__((aligned(16))) uint64_t ssv[kWave];
+  topk_merge_row(part, (int64_t)blockIdx.x, splits, k, out_idx, out_val, sel, ssv);
 }
 
 }  // namespace
@@ -149,9 +145,12 @@ hipError_t launch_topk(const void* logits, int dt, int64_t rows, int64_t vocab, 
                                                          out_idx, out_val, part));
   }
   if (plan.splits > 1) {
+    // one wave per row, each in a work-group of its own (rows on as many
+    // CUs: batch 1 / block 8 41.35 -> 40.8 us per cycle against eight rows
+    // per work-group)
     ProfileScope ps("topk_merge", stream);
-    dim3 g2((unsigned)((rows + kWaves - 1) / kWaves));
-    DF2_TRY(launch(topk_merge_kernel, g2, block, 0, stream, ps, part, rows, plan.splits, k, out_idx, out_val));
+    DF2_TRY(launch(topk_merge_kernel, dim3((unsigned)rows), dim3(kWave), 0, stream, ps, part, plan.splits, k, out_idx,
+                   out_val));
   }
   return hipGetLastError();
 }
